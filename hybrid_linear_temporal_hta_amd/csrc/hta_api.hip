@@ -1,0 +1,437 @@
+// hta_api.hip -- the C ABI of libhta (declared in include/hta.h): argument
+// validation, workspace layout and the order of kernel launches.
+//
+// The branches and their sum follow page "Kairos：面向物理 AI 的原生世界模型栈"
+// (yingwang.github.io), section 二、方法, second pillar: SWA, DSWA and GLA
+// paragraphs and the three-branch figure. Every check runs before the first
+// launch, so a failing call enqueues nothing and touches no output.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/hta.h"
+#include "hta_internal.h"
+
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr long long kMaxElems = (1LL << 62);
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dtype) { return dtype == HTA_BF16 ? 2 : 4; }
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return HTA_ERR_HIP;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, size_t bytes) {
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Shape checks shared by every entry point. L = T*P.
+int check_shape(const hta_shape* s) {
+    if (!s) return HTA_ERR_NULL;
+    if (s->dtype != HTA_F32 && s->dtype != HTA_BF16) return HTA_ERR_DTYPE;
+    if (s->out_dtype != HTA_F32 && s->out_dtype != HTA_BF16) return HTA_ERR_DTYPE;
+    if (s->dtype == HTA_F32 && s->out_dtype != HTA_F32) return HTA_ERR_DTYPE;
+    if (s->B < 1 || s->H < 1 || s->T < 1 || s->P < 1 || s->dk < 1 || s->dv < 1) return HTA_ERR_SHAPE;
+    if (s->dk != s->dv) return HTA_ERR_UNSUPPORTED;
+    if (s->dk != 64 && s->dk != 128) return HTA_ERR_UNSUPPORTED;
+    if (s->dtype == HTA_BF16 && s->dk != 128) return HTA_ERR_UNSUPPORTED;
+    const long long L = (long long)s->T * s->P;
+    const long long bh = (long long)s->B * s->H;
+    if (bh > (1LL << 30) || L > (1LL << 40)) return HTA_ERR_SHAPE;
+    if ((double)bh * (double)L * (double)s->dk >= (double)kMaxElems) return HTA_ERR_SHAPE;
+    if (bh * (long long)((s->P + 63) / 64) * s->T > 0x7fffffffLL) return HTA_ERR_SHAPE;
+    return HTA_OK;
+}
+
+int check_scale(float scale) {
+    if (!(scale >= 0.f) || !isfinite(scale)) return HTA_ERR_UNSUPPORTED;
+    return HTA_OK;
+}
+
+int check_window(int window) { return (window >= 1 && window <= hta::kMaxTaps) ? HTA_OK : HTA_ERR_WINDOW; }
+
+int check_dilated(int taps, int dil) {
+    if (taps < 1 || taps > hta::kMaxTaps || dil < 1) return HTA_ERR_WINDOW;
+    if ((long long)(taps - 1) * dil + 1 > 4096) return HTA_ERR_WINDOW;
+    return HTA_OK;
+}
+
+int check_chunk(int dtype, int chunk) {
+    if (dtype == HTA_BF16) return chunk == 64 ? HTA_OK : HTA_ERR_UNSUPPORTED;
+    return (chunk == 16 || chunk == 32 || chunk == 64) ? HTA_OK : HTA_ERR_UNSUPPORTED;
+}
+
+int check_params(const hta_shape* s, const hta_params* p) {
+    if (!p) return HTA_ERR_NULL;
+    int st;
+    if ((st = check_window(p->swa_window)) != HTA_OK) return st;
+    if ((st = check_dilated(p->dswa_taps, p->dswa_dilation)) != HTA_OK) return st;
+    if ((st = check_chunk(s->dtype, p->gla_chunk)) != HTA_OK) return st;
+    if ((st = check_scale(p->attn_scale)) != HTA_OK) return st;
+    if (!isfinite(p->gla_scale)) return HTA_ERR_UNSUPPORTED;
+    return HTA_OK;
+}
+
+float attn_scale_of(float scale, int dk) { return scale > 0.f ? scale : 1.0f / sqrtf((float)dk); }
+float gla_scale_of(float scale) { return scale != 0.f ? scale : 1.0f; }
+
+size_t seq_bytes(const hta_shape* s, int d) {
+    return (size_t)s->B * s->H * (size_t)s->T * s->P * d * elem_bytes(s->dtype);
+}
+size_t out_bytes(const hta_shape* s) {
+    return (size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * elem_bytes(s->out_dtype);
+}
+size_t gate_bytes(const hta_shape* s) { return (size_t)s->B * s->H * (size_t)s->T * s->P * 4; }
+size_t state_bytes(const hta_shape* s) { return (size_t)s->B * s->H * s->dk * s->dv * 4; }
+
+// Workspace: [GLA scratch][fp32 partial of the GLA branch (bf16 hybrid only)].
+size_t gla_ws(const hta_shape* s, int chunk) {
+    if (s->dtype == HTA_F32) return kAlign;
+    const long long L = (long long)s->T * s->P;
+    return align_up(hta::gla_bf16_workspace_bytes(s->B * s->H, L, chunk));
+}
+// fp32 output: the GLA branch is written straight into o and the attention
+// epilogue adds to it in place; bf16 output keeps the fp32 GLA partial here.
+size_t partial_ws(const hta_shape* s) {
+    if (s->out_dtype == HTA_F32) return 0;
+    return align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 4);
+}
+
+hta::WinLaunch win_base(const hta_shape* s, const void* q, const void* k, const void* v, void* o,
+                        float scale) {
+    hta::WinLaunch w;
+    memset(&w, 0, sizeof(w));
+    const long long L = (long long)s->T * s->P;
+    w.q = q; w.k = k; w.v = v; w.o = o; w.add = nullptr;
+    w.q_bh = L * s->dk;
+    w.kv_bh = L * s->dk;
+    w.kv_frame = (long long)s->P * s->dk;
+    w.BH = s->B * s->H;
+    w.P = s->P;
+    w.Tq = s->T;
+    w.frame0 = 0;
+    w.R = 0;
+    w.scale = attn_scale_of(scale, s->dk);
+    w.d = s->dk;
+    w.dtype = s->dtype;
+    w.out_f32 = s->out_dtype == HTA_F32 ? 1 : 0;
+    return w;
+}
+
+void taps_swa(hta::WinTaps& t, int window) {
+    t.nA = window;
+    for (int j = 0; j < window; ++j) t.offA[j] = j;
+    t.nB = 0;
+}
+
+void taps_dswa(hta::WinTaps& t, int taps, int dil) {
+    t.nA = taps;
+    for (int j = 0; j < taps; ++j) t.offA[j] = j * dil;
+    t.nB = 0;
+}
+
+// SWA as branch A (own frame first), DSWA taps 1.. as branch B.
+void taps_hybrid(hta::WinTaps& t, int window, int taps, int dil) {
+    t.nA = window;
+    for (int j = 0; j < window; ++j) t.offA[j] = j;
+    t.nB = taps - 1;
+    for (int j = 1; j < taps; ++j) t.offB[j - 1] = j * dil;
+}
+
+hta::GlaLaunch gla_base(const hta_shape* s, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, float* state, void* o,
+                        int chunk, float scale, void* ws, size_t ws_bytes) {
+    hta::GlaLaunch g;
+    memset(&g, 0, sizeof(g));
+    g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta; g.state = state; g.o = o;
+    g.out_f32 = s->out_dtype == HTA_F32 ? 1 : 0;
+    g.L = (long long)s->T * s->P;
+    g.BH = s->B * s->H;
+    g.d = s->dk;
+    g.chunk = chunk;
+    g.scale = gla_scale_of(scale);
+    g.dtype = s->dtype;
+    g.ws = ws;
+    g.ws_bytes = ws_bytes;
+    return g;
+}
+
+hipError_t run_gla(const hta::GlaLaunch& g, hipStream_t st) {
+    return g.dtype == HTA_F32 ? hta::launch_gla_f32(g, st) : hta::launch_gla_bf16(g, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hta_status_string(int status) {
+    switch (status) {
+        case HTA_OK: return "HTA_OK";
+        case HTA_ERR_NULL: return "HTA_ERR_NULL: a required pointer is NULL";
+        case HTA_ERR_SHAPE: return "HTA_ERR_SHAPE: invalid or too large shape";
+        case HTA_ERR_WINDOW: return "HTA_ERR_WINDOW: window, taps or dilation out of range";
+        case HTA_ERR_DTYPE: return "HTA_ERR_DTYPE: dtype must be HTA_F32 or HTA_BF16";
+        case HTA_ERR_UNSUPPORTED: return "HTA_ERR_UNSUPPORTED: head dim, chunk or scale not supported";
+        case HTA_ERR_WORKSPACE: return "HTA_ERR_WORKSPACE: workspace missing or too small";
+        case HTA_ERR_RING: return "HTA_ERR_RING: ring buffer shorter than the attention windows";
+        case HTA_ERR_HIP: return "HTA_ERR_HIP: a HIP runtime call failed";
+        case HTA_ERR_ALIAS: return "HTA_ERR_ALIAS: an output overlaps an input";
+        default: return "unknown hta status";
+    }
+}
+
+int hta_last_hip_error(void) { return g_last_hip_error; }
+
+const char* hta_version(void) { return "hta 0.1.0 gfx950"; }
+
+size_t hta_workspace_bytes(int op, const hta_shape* shape, const hta_params* params) {
+    if (check_shape(shape) != HTA_OK) return 0;
+    if (op == HTA_OP_GLA) {
+        if (!params || check_chunk(shape->dtype, params->gla_chunk) != HTA_OK) return 0;
+        return gla_ws(shape, params->gla_chunk);
+    }
+    if (op == HTA_OP_HYBRID || op == HTA_OP_STREAM_STEP) {
+        if (check_params(shape, params) != HTA_OK) return 0;
+        if (op == HTA_OP_STREAM_STEP && shape->T != 1) return 0;
+        return gla_ws(shape, params->gla_chunk) + partial_ws(shape);
+    }
+    return 0;
+}
+
+static int window_fwd(int kind, const hta_shape* s, const void* q, const void* k, const void* v,
+                      void* o, int a, int b, float scale, void* stream) {
+    int st;
+    if ((st = check_shape(s)) != HTA_OK) return st;
+    if (!q || !k || !v || !o) return HTA_ERR_NULL;
+    if ((st = (kind == 0 ? check_window(a) : check_dilated(a, b))) != HTA_OK) return st;
+    if ((st = check_scale(scale)) != HTA_OK) return st;
+    const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
+    const Range ro = range_of(o, out_bytes(s));
+    if (overlap(ro, range_of(q, nq)) || overlap(ro, range_of(k, nq)) || overlap(ro, range_of(v, nv)))
+        return HTA_ERR_ALIAS;
+    hta::WinLaunch w = win_base(s, q, k, v, o, scale);
+    w.nbr = 1;
+    if (kind == 0) taps_swa(w.taps, a);
+    else taps_dswa(w.taps, a, b);
+    hipError_t e = hta::launch_win_attn(w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+int hta_swa_fwd(const hta_shape* shape, const void* q, const void* k, const void* v, void* o,
+                int window_frames, float scale, void* stream) {
+    return window_fwd(0, shape, q, k, v, o, window_frames, 0, scale, stream);
+}
+
+int hta_dswa_fwd(const hta_shape* shape, const void* q, const void* k, const void* v, void* o,
+                 int taps, int dilation_frames, float scale, void* stream) {
+    return window_fwd(1, shape, q, k, v, o, taps, dilation_frames, scale, stream);
+}
+
+static int check_gla_buffers(const hta_shape* s, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* state,
+                             const void* o, const void* ws, size_t ws_bytes, size_t ws_need) {
+    if (!q || !k || !v || !alpha || !beta || !state || !o) return HTA_ERR_NULL;
+    if (!ws || ws_bytes < ws_need) return HTA_ERR_WORKSPACE;
+    const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
+    const Range in[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                         range_of(alpha, gate_bytes(s)), range_of(beta, gate_bytes(s))};
+    const Range outs[3] = {range_of(o, out_bytes(s)), range_of(state, state_bytes(s)),
+                           range_of(ws, ws_need)};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlap(outs[i], in[j])) return HTA_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return HTA_ERR_ALIAS;
+    }
+    return HTA_OK;
+}
+
+int hta_gla_fwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                const float* alpha, const float* beta, float* state, void* o, int chunk,
+                float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_shape(shape)) != HTA_OK) return st;
+    if ((st = check_chunk(shape->dtype, chunk)) != HTA_OK) return st;
+    if (!isfinite(scale)) return HTA_ERR_UNSUPPORTED;
+    const size_t need = gla_ws(shape, chunk);
+    if ((st = check_gla_buffers(shape, q, k, v, alpha, beta, state, o, workspace, workspace_bytes,
+                                need)) != HTA_OK)
+        return st;
+    hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, o, chunk, scale, workspace, need);
+    hipError_t e = run_gla(g, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void* q, const void* k,
+                   const void* v, const float* alpha, const float* beta, float* state, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_shape(shape)) != HTA_OK) return st;
+    if ((st = check_params(shape, params)) != HTA_OK) return st;
+    const size_t need_gla = gla_ws(shape, params->gla_chunk);
+    const size_t need = need_gla + partial_ws(shape);
+    if ((st = check_gla_buffers(shape, q, k, v, alpha, beta, state, o, workspace, workspace_bytes,
+                                need)) != HTA_OK)
+        return st;
+    hipStream_t sm = static_cast<hipStream_t>(stream);
+    // 1. GLA branch -> fp32 partial (bf16 output) or straight into o (fp32 output).
+    float* partial = shape->out_dtype == HTA_BF16
+                         ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need_gla)
+                         : static_cast<float*>(o);
+    hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, partial, params->gla_chunk,
+                                params->gla_scale, workspace, need_gla);
+    g.out_f32 = 1;
+    hipError_t e = run_gla(g, sm);
+    if (e != hipSuccess) return hip_fail(e);
+    // 2. SWA + DSWA in one pass; the epilogue adds the GLA partial and rounds once.
+    hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
+    w.nbr = 2;
+    w.add = partial;
+    taps_hybrid(w.taps, params->swa_window, params->dswa_taps, params->dswa_dilation);
+    e = hta::launch_win_attn(w, sm);
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+static int check_ctx(const hta_stream_ctx* c) {
+    if (!c) return HTA_ERR_NULL;
+    hta_shape s1 = c->s;
+    s1.T = 1;
+    int st;
+    if ((st = check_shape(&s1)) != HTA_OK) return st;
+    if ((st = check_params(&s1, &c->p)) != HTA_OK) return st;
+    if (!c->ring_k || !c->ring_v || !c->state) return HTA_ERR_NULL;
+    const long long need = (long long)(c->p.dswa_taps - 1) * c->p.dswa_dilation + 1;
+    if (c->R < 1 || c->R < c->p.swa_window || c->R < need) return HTA_ERR_RING;
+    if (c->n_frames < 0) return HTA_ERR_SHAPE;
+    return HTA_OK;
+}
+
+static size_t ring_bytes(const hta_stream_ctx* c, int d) {
+    return (size_t)c->s.B * c->s.H * (size_t)c->R * c->s.P * d * elem_bytes(c->s.dtype);
+}
+
+int hta_stream_init(hta_stream_ctx* ctx, const void* k_prefix, const void* v_prefix, int T_prefix,
+                    const float* state_prefix, void* stream) {
+    int st;
+    if ((st = check_ctx(ctx)) != HTA_OK) return st;
+    if (T_prefix < 0) return HTA_ERR_SHAPE;
+    if (T_prefix > 0 && (!k_prefix || !v_prefix)) return HTA_ERR_NULL;
+    const hta_shape& s = ctx->s;
+    const int BH = s.B * s.H;
+    const Range rk = range_of(ctx->ring_k, ring_bytes(ctx, s.dk));
+    const Range rv = range_of(ctx->ring_v, ring_bytes(ctx, s.dv));
+    const Range rs = range_of(ctx->state, (size_t)BH * s.dk * s.dv * 4);
+    if (overlap(rk, rv) || overlap(rk, rs) || overlap(rv, rs)) return HTA_ERR_ALIAS;
+    if (T_prefix > 0) {
+        const size_t pb = (size_t)BH * T_prefix * (size_t)s.P * s.dk * elem_bytes(s.dtype);
+        const Range pk = range_of(k_prefix, pb), pv = range_of(v_prefix, pb);
+        if (overlap(pk, rk) || overlap(pk, rv) || overlap(pk, rs) || overlap(pv, rk) ||
+            overlap(pv, rv) || overlap(pv, rs))
+            return HTA_ERR_ALIAS;
+    }
+    if (state_prefix) {
+        const Range sp = range_of(state_prefix, (size_t)BH * s.dk * s.dv * 4);
+        if (overlap(sp, rk) || overlap(sp, rv) || (overlap(sp, rs) && state_prefix != ctx->state))
+            return HTA_ERR_ALIAS;
+    }
+    hipStream_t sm = static_cast<hipStream_t>(stream);
+    const long long fe = (long long)s.P * s.dk;  // elements per frame
+    const int nfill = T_prefix < ctx->R ? T_prefix : ctx->R;
+    for (int i = 0; i < nfill; ++i) {
+        const long long f = (long long)T_prefix - nfill + i;
+        const long long slot = f % ctx->R;
+        hipError_t e = hta::launch_copy_frames(k_prefix, ctx->ring_k, BH, (long long)T_prefix * fe,
+                                               (long long)ctx->R * fe, f * fe, slot * fe, fe,
+                                               elem_bytes(s.dtype), sm);
+        if (e == hipSuccess)
+            e = hta::launch_copy_frames(v_prefix, ctx->ring_v, BH, (long long)T_prefix * fe,
+                                        (long long)ctx->R * fe, f * fe, slot * fe, fe,
+                                        elem_bytes(s.dtype), sm);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (state_prefix != ctx->state) {
+        hipError_t e = hta::launch_fill_f32(ctx->state, state_prefix, (long long)BH * s.dk * s.dv, sm);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    ctx->n_frames = T_prefix;
+    return HTA_OK;
+}
+
+int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, void* o, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_ctx(ctx)) != HTA_OK) return st;
+    hta_shape s = ctx->s;
+    s.T = 1;
+    if (!q || !k || !v || !alpha || !beta) return HTA_ERR_NULL;
+    const size_t need_gla = gla_ws(&s, ctx->p.gla_chunk);
+    const size_t need = need_gla + (o ? partial_ws(&s) : 0);
+    if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    const int BH = s.B * s.H;
+    const size_t nq = seq_bytes(&s, s.dk), nv = seq_bytes(&s, s.dv);
+    const Range in[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                         range_of(alpha, gate_bytes(&s)), range_of(beta, gate_bytes(&s))};
+    const Range outs[5] = {range_of(ctx->ring_k, ring_bytes(ctx, s.dk)),
+                           range_of(ctx->ring_v, ring_bytes(ctx, s.dv)),
+                           range_of(ctx->state, state_bytes(&s)), range_of(workspace, need),
+                           o ? range_of(o, out_bytes(&s)) : Range{0, 0}};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlap(outs[i], in[j])) return HTA_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(outs[i], outs[j])) return HTA_ERR_ALIAS;
+    }
+    hipStream_t sm = static_cast<hipStream_t>(stream);
+    const long long n = ctx->n_frames;
+    const long long slot = n % ctx->R;
+    const long long fe = (long long)s.P * s.dk;
+    // 1. K/V of the new frame into ring slot n mod R.
+    hipError_t e = hta::launch_copy_frames(k, ctx->ring_k, BH, fe, (long long)ctx->R * fe, 0,
+                                           slot * fe, fe, elem_bytes(s.dtype), sm);
+    if (e == hipSuccess)
+        e = hta::launch_copy_frames(v, ctx->ring_v, BH, fe, (long long)ctx->R * fe, 0, slot * fe,
+                                    fe, elem_bytes(s.dtype), sm);
+    if (e != hipSuccess) return hip_fail(e);
+    // 2. GLA over the frame's P tokens from the carried state (chunks start at the frame).
+    float* partial = nullptr;
+    if (o) partial = s.out_dtype == HTA_BF16
+                         ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need_gla)
+                         : static_cast<float*>(o);
+    hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, partial, ctx->p.gla_chunk,
+                                ctx->p.gla_scale, workspace, need_gla);
+    g.out_f32 = 1;
+    e = run_gla(g, sm);
+    if (e != hipSuccess) return hip_fail(e);
+    // 3. Attention of the frame's queries over the ring, plus the GLA partial.
+    if (o) {
+        hta::WinLaunch w = win_base(&s, q, ctx->ring_k, ctx->ring_v, o, ctx->p.attn_scale);
+        w.kv_bh = (long long)ctx->R * s.P * s.dk;
+        w.frame0 = n;
+        w.R = ctx->R;
+        w.nbr = 2;
+        w.add = partial;
+        taps_hybrid(w.taps, ctx->p.swa_window, ctx->p.dswa_taps, ctx->p.dswa_dilation);
+        e = hta::launch_win_attn(w, sm);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    ctx->n_frames = n + 1;
+    return HTA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// hta_internal.h -- launcher interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace hta {
+
+constexpr int kMaxTaps = 16;
+
+// Frame offsets of one windowed-attention launch. Branch A's offsets are
+// processed first; with two branches, offset 0 (the query's own frame) is
+// listed once, first in A, and its partial softmax state seeds branch B too.
+struct WinTaps {
+    int nA, nB;
+    int offA[kMaxTaps];
+    int offB[kMaxTaps];
+};
+
+// One windowed-attention launch (SWA, DSWA, or both summed).
+//   query frame fq (0..Tq-1) has absolute frame index frame0 + fq;
+//   key frame for offset j is abs - j, skipped if < 0;
+//   key frame storage index is abs - j (linear) or (abs - j) mod R (ring).
+struct WinLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    const float* add;       // optional fp32 partial [BH][Tq*P][dv] added to o (may equal o for fp32)
+    long long q_bh;         // elements between (b,h) slices of q / o / add
+    long long kv_bh;        // elements between (b,h) slices of k / v
+    long long kv_frame;     // elements between consecutive key frames (P*d)
+    int BH, P, Tq;
+    long long frame0;
+    int R;                  // 0 = linear key addressing
+    float scale;            // softmax scale
+    int d;                  // dk == dv
+    int dtype;              // HTA_F32 / HTA_BF16 (inputs)
+    int out_f32;            // 1: o is fp32, 0: o is bf16
+    int nbr;                // 1 or 2 branches
+    WinTaps taps;
+};
+
+hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream);
+
+// Chunked GLA over one segment of tokens per (b,h).
+struct GlaLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    float* state;           // [BH][d][d] in/out
+    void* o;                // output; may be NULL (state only)
+    int out_f32;            // 1: o is fp32, 0: o is bf16
+    long long L;            // tokens per (b,h)
+    int BH, d, chunk;
+    float scale;
+    int dtype;
+    void* ring_k;           // optional: copy k/v of these tokens into a ring slot
+    void* ring_v;
+    long long ring_bh;      // elements between (b,h) slices of the ring
+    long long ring_off;     // element offset of the slot inside a (b,h) slice
+    void* ws;               // workspace
+    size_t ws_bytes;
+};
+
+// Chunked GLA: fp32 (vector ALU) and bf16 (MFMA) paths.
+hipError_t launch_gla_f32(const GlaLaunch& g, hipStream_t stream);
+hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream);
+size_t gla_bf16_workspace_bytes(int BH, long long L, int chunk);
+
+// Per-(b,h) strided copy of `elems` elements (16-byte multiples) from
+// src[bh*src_bh + src_off] to dst[bh*dst_bh + dst_off] (strides/offsets in elements).
+hipError_t launch_copy_frames(const void* src, void* dst, int BH, long long src_bh,
+                              long long dst_bh, long long src_off, long long dst_off,
+                              long long elems, int elem_bytes, hipStream_t stream);
+
+// dst[i] = src ? src[i] : 0 for i < n (a kernel, not hipMemsetAsync).
+hipError_t launch_fill_f32(float* dst, const float* src, long long n, hipStream_t stream);
+
+}  // namespace hta

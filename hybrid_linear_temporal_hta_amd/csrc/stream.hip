@@ -1,0 +1,63 @@
+// stream.hip -- data movement of the streaming step: ring-slot copies of K/V
+// frames and the copy (or zeroing) of the carried GLA state. HBM-bound copies,
+// 16 bytes per lane, one grid-stride loop.
+#include "device_common.h"
+#include "hta_internal.h"
+
+namespace hta {
+
+namespace {
+
+// dst[bh][dst_off + e] = src[bh][src_off + e] for e < n16*16 bytes, all bh.
+__global__ __launch_bounds__(256) void copy_frames_kernel(const char* __restrict__ src,
+                                                          char* __restrict__ dst, int BH,
+                                                          long long src_bh, long long dst_bh,
+                                                          long long n16) {
+    const long long total = (long long)BH * n16;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (long long)gridDim.x * 256) {
+        const long long bh = i / n16, e = i - bh * n16;
+        *reinterpret_cast<u32x4*>(dst + bh * dst_bh + e * 16) =
+            *reinterpret_cast<const u32x4*>(src + bh * src_bh + e * 16);
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ dst,
+                                                       const float* __restrict__ src, long long n) {
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n;
+         i += (long long)gridDim.x * 256)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+unsigned grid_for(long long work) {
+    long long g = (work + 255) / 256;
+    if (g > 8192) g = 8192;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+// Copies `elems` elements per (b,h) slice; byte offsets and strides are elems * elem_bytes.
+hipError_t launch_copy_frames(const void* src, void* dst, int BH, long long src_bh,
+                              long long dst_bh, long long src_off, long long dst_off,
+                              long long elems, int elem_bytes, hipStream_t stream) {
+    const long long bytes = elems * elem_bytes;
+    if (BH == 0 || bytes == 0) return hipSuccess;
+    if ((bytes & 15) || ((src_bh * elem_bytes) & 15) || ((dst_bh * elem_bytes) & 15) ||
+        ((src_off * elem_bytes) & 15) || ((dst_off * elem_bytes) & 15))
+        return hipErrorInvalidValue;
+    const long long n16 = bytes / 16;
+    hipLaunchKernelGGL(copy_frames_kernel, dim3(grid_for((long long)BH * n16)), dim3(256), 0, stream,
+                       static_cast<const char*>(src) + src_off * elem_bytes,
+                       static_cast<char*>(dst) + dst_off * elem_bytes, BH, src_bh * elem_bytes,
+                       dst_bh * elem_bytes, n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* dst, const float* src, long long n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, stream, dst, src, n);
+    return hipGetLastError();
+}
+
+}  // namespace hta

@@ -1,0 +1,421 @@
+// win_attn.hip -- frame-windowed block-causal softmax attention (SWA and DSWA).
+//
+// Method: page "Kairos：面向物理 AI 的原生世界模型栈" (yingwang.github.io), section
+// 二、方法, second pillar: SWA is standard attention inside a window of W frames
+// (L x window_size tokens, L tokens per frame); DSWA keeps the window size but
+// spaces its taps `dilation` frames apart (the page realises it by regrouping
+// (B, F*L, D) -> (B*d, F/d*L, D); here the regrouping is an index map over
+// tap frames and is never materialised). A query attends to every key of each
+// tap frame, its own frame included, and to no later frame.
+//
+// bf16 kernel (d = 128), one workgroup = 4 waves = 128 query rows of one frame:
+//   * each wave keeps its 32 query rows as MFMA B fragments in registers and
+//     computes S^T = K Q^T (keys x queries) with v_mfma_f32_32x32x16_bf16, so a
+//     lane owns one query and 16 of its logits per 32-key block: the softmax
+//     row max / sum is lane-local plus one swap with lane^32;
+//   * O^T += V^T P^T reuses the logits' register layout directly as the B
+//     fragment (key order permuted consistently in both operands), so P never
+//     goes through LDS;
+//   * key/value tiles of 64 keys are staged through LDS, double buffered; V is
+//     transposed in registers on the way in so that A fragments of V^T are two
+//     8-byte LDS reads;
+//   * both branches in one pass: the query's own frame (offset 0, common to
+//     SWA and DSWA) is processed once and its partial softmax state seeds the
+//     second branch, saving one of the seven tap frames of an interior query;
+//   * running max is updated lazily (only when a logit exceeds it by more than
+//     8 in log2 units), so the O rescale is rare; exp2 with the log2(e) scale
+//     folded into one FMA;
+//   * the softmax denominator sums the same bf16-rounded weights that feed the
+//     PV product (v_dot2_f32_bf16 against ones), so the output is an exact
+//     convex combination of those weights;
+//   * the epilogue adds an optional fp32 partial (the GLA branch) and writes
+//     the fp32 sum, or rounds it once to bf16.
+// fp32 kernel (d = 64 or 128): a plain per-row online softmax on the vector
+// ALU (4 lanes per query row); used for fp32 inputs, whose workloads are tiny.
+#include "device_common.h"
+#include "hta_internal.h"
+
+namespace hta {
+
+namespace {
+
+constexpr int kD = 128;          // head dim of the bf16 kernel
+constexpr int kBQ = 128;         // query rows per workgroup
+constexpr int kBK = 64;          // keys per LDS tile
+constexpr int kKPad = kD + 8;    // K tile row stride (bf16 elements)
+constexpr int kVPad = kBK + 4;   // V^T tile row stride (bf16 elements)
+constexpr float kLazyLog2 = 8.0f;
+
+struct Acc {
+    f32x16 o[4];   // O^T fragments: d-block db, element i -> d = 32 db + 8(i/4) + 4 h + i%4
+    float m;       // running max (raw logit units)
+    float l;       // this lane's share of the softmax denominator
+};
+
+__device__ __forceinline__ void acc_init(Acc& a) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a.o[db][i] = 0.f;
+    a.m = -INFINITY;
+    a.l = 0.f;
+}
+
+// Offsets are ascending, so the taps present for absolute query frame fa
+// (those with fa - off >= 0) are a prefix of each list.
+__device__ __forceinline__ int taps_present(const int* off, int n, long long fa) {
+    int c = 0;
+    for (int j = 0; j < n; ++j) c += (off[j] <= fa) ? 1 : 0;
+    return c;
+}
+
+// Storage index of the key frame of segment sg (branch A's present taps first).
+__device__ __forceinline__ long long seg_frame(const WinLaunch& w, long long fa, int sg, int nAv) {
+    const int off = sg < nAv ? w.taps.offA[sg] : w.taps.offB[sg - nAv];
+    const long long f = fa - off;
+    return w.R > 0 ? (f % w.R) : f;
+}
+
+struct TileRegs {
+    u32x4 k[4];
+    u32x4 v[4];
+};
+
+// Global -> registers for one 64-key tile (rows >= nvalid are zero).
+__device__ __forceinline__ void load_tile(TileRegs& r, const bf16* kbase, const bf16* vbase,
+                                          int nvalid, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        const int key = c >> 4;
+        const int col = (c & 15) * 8;
+        if (key < nvalid)
+            r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (long long)key * kD + col);
+        else
+            r.k[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    const int kg = tid & 15, dg = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = 4 * kg + i;
+        if (key < nvalid)
+            r.v[i] = *reinterpret_cast<const u32x4*>(vbase + (long long)key * kD + 8 * dg);
+        else
+            r.v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Registers -> LDS: K row-major (padded), V transposed to V^T[d][key].
+__device__ __forceinline__ void store_tile(const TileRegs& r, bf16* Ks, bf16* Vt, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        const int key = c >> 4;
+        const int col = (c & 15) * 8;
+        *reinterpret_cast<u32x4*>(Ks + key * kKPad + col) = r.k[i];
+    }
+    const int kg = tid & 15, dg = tid >> 4;
+    // r.v[i] holds keys 4kg+i, d = 8dg .. 8dg+7 (two bf16 per dword).
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {            // dword w covers d = 8dg + 2w, 8dg + 2w + 1
+        const uint32_t a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
+        u32x2 lo, hi;                         // lo: d even, hi: d odd; keys 4kg..4kg+3
+        lo[0] = (a0 & 0xffffu) | (a1 << 16);
+        lo[1] = (a2 & 0xffffu) | (a3 << 16);
+        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+        *reinterpret_cast<u32x2*>(Vt + (8 * dg + 2 * w) * kVPad + 4 * kg) = lo;
+        *reinterpret_cast<u32x2*>(Vt + (8 * dg + 2 * w + 1) * kVPad + 4 * kg) = hi;
+    }
+}
+
+// One 64-key tile for one wave: S^T = K Q^T, lazy online softmax, O^T += V^T P^T.
+__device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const bf16* Ks,
+                                            const bf16* Vt, int nvalid, float c, int n, int h) {
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + n) * kKPad + 16 * ks + 8 * h);
+            s[kb] = mfma32(kf, qf[ks], s[kb]);
+        }
+    }
+    if (nvalid < kBK) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                if (key >= nvalid) s[kb][i] = -INFINITY;
+            }
+    }
+    float mt = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+    mt = fmaxf(mt, wave_xor32(mt));
+    const bool grow = (mt - a.m) * c > kLazyLog2;
+    if (__any(grow)) {
+        const float mn = grow ? mt : a.m;
+        const float corr = fast_exp2((a.m - mn) * c);
+        a.m = mn;
+        a.l *= corr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a.o[db][i] *= corr;
+    }
+    const float mc = a.m * c;
+    bf16x8 pf[2][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                pf[kb][gg][j] = f2bf(fast_exp2(__builtin_fmaf(s[kb][8 * gg + j], c, -mc)));
+            // the denominator sums the same rounded weights the PV product uses
+#pragma unroll
+            for (int j = 0; j < 8; j += 2)
+                lsum = add_pair(bf16x2{pf[kb][gg][j], pf[kb][gg][j + 1]}, lsum);
+        }
+    a.l += lsum;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const bf16* vrow = Vt + (db * 32 + n) * kVPad;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + kb * 32 + 16 * gg + 4 * h);
+                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + kb * 32 + 16 * gg + 8 + 4 * h);
+                a.o[db] = mfma32(cat(lo, hi), pf[kb][gg], a.o[db]);
+            }
+    }
+}
+
+template <int NBR>
+__global__ __launch_bounds__(256) void win_attn_bf16_kernel(WinLaunch w) {
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBK * kKPad];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[2][kD * kVPad];
+
+    const int nqt = (w.P + kBQ - 1) / kBQ;
+    const int nwg = w.BH * w.Tq * nqt;
+    const int wid = xcd_remap(blockIdx.x, nwg);
+    const int qt = wid % nqt;
+    const int fq = w.Tq - 1 - (wid / nqt) % w.Tq;   // heavy (late) frames first
+    const int bh = wid / (nqt * w.Tq);
+    const long long fa = w.frame0 + fq;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, h = lane >> 5;
+
+    const bf16* kbh = static_cast<const bf16*>(w.k) + (long long)bh * w.kv_bh;
+    const bf16* vbh = static_cast<const bf16*>(w.v) + (long long)bh * w.kv_bh;
+
+    // Segments: present taps of branch A, then of branch B.
+    const int nSegA = taps_present(w.taps.offA, w.taps.nA, fa);
+    const int nseg = nSegA + (NBR == 2 ? taps_present(w.taps.offB, w.taps.nB, fa) : 0);
+    const int ntk = (w.P + kBK - 1) / kBK;
+    const int nit = nseg * ntk;
+
+    // Query fragments (B operand of S^T = K Q^T).
+    const int qrow = qt * kBQ + wave * 32 + n;
+    const bf16* qp = static_cast<const bf16*>(w.q) + (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
+    bf16x8 qf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        if (qrow < w.P) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks + 8 * h);
+        else
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qf[ks][j] = (bf16)0.f;
+    }
+    const float c = w.scale * kLog2e;
+
+    Acc A, Bacc;
+    acc_init(A);
+    acc_init(Bacc);
+
+    TileRegs tr;
+    {
+        const long long kofs = seg_frame(w, fa, 0, nSegA) * w.kv_frame;
+        load_tile(tr, kbh + kofs, vbh + kofs, min(kBK, w.P), tid);
+        store_tile(tr, Ks[0], Vt[0], tid);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < nit; ++it) {
+        const int cur = it & 1;
+        const int sg = it / ntk, tk = it - sg * ntk;
+        const int nvalid = min(kBK, w.P - tk * kBK);
+        const bool more = it + 1 < nit;
+        if (more) {
+            const int sg1 = (it + 1) / ntk, tk1 = (it + 1) - sg1 * ntk;
+            const long long kofs = seg_frame(w, fa, sg1, nSegA) * w.kv_frame + (long long)tk1 * kBK * kD;
+            load_tile(tr, kbh + kofs, vbh + kofs, min(kBK, w.P - tk1 * kBK), tid);
+        }
+        if (NBR == 1 || sg < nSegA) attend_tile(A, qf, Ks[cur], Vt[cur], nvalid, c, n, h);
+        else attend_tile(Bacc, qf, Ks[cur], Vt[cur], nvalid, c, n, h);
+        if (NBR == 2 && sg == 0 && tk == ntk - 1) Bacc = A;   // own frame seeds branch B
+        if (more) store_tile(tr, Ks[cur ^ 1], Vt[cur ^ 1], tid);
+        __syncthreads();
+    }
+
+    // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add), rounded once.
+    if (qrow >= w.P) return;
+    const float invA = 1.f / (A.l + wave_xor32(A.l));
+    float invB = 0.f;
+    if (NBR == 2) invB = 1.f / (Bacc.l + wave_xor32(Bacc.l));
+    const long long orow = (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
+    const float* ap = w.add ? w.add + orow : nullptr;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = db * 32 + 8 * g + 4 * h;
+            float r[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                r[i] = A.o[db][4 * g + i] * invA;
+                if (NBR == 2) r[i] += Bacc.o[db][4 * g + i] * invB;
+            }
+            if (ap) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(ap + d0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] += x[i];
+            }
+            if (w.out_f32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(w.o) + orow + d0) =
+                    f32x4{r[0], r[1], r[2], r[3]};
+            } else {
+                bf16x4 ov;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = f2bf(r[i]);
+                *reinterpret_cast<bf16x4*>(static_cast<bf16*>(w.o) + orow + d0) = ov;
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------------
+// fp32 path: 64 query rows per workgroup, 4 lanes per row (each owns D/4 dims,
+// interleaved), keys streamed from global memory, exact online softmax.
+
+template <int D>
+__device__ __forceinline__ void f32_branch(const WinLaunch& w, long long fa, int nAv,
+                                           const float* qv, const float* kbh, const float* vbh,
+                                           int s0, int s1, int sub,
+                                           float& m, float& l, float (&acc)[D / 4]) {
+    const int P = w.P;
+    const float scale = w.scale;
+    for (int sg = s0; sg < s1; ++sg) {
+        const long long fr = seg_frame(w, fa, sg, nAv);
+        const float* kf = kbh + fr * w.kv_frame;
+        const float* vf = vbh + fr * w.kv_frame;
+        for (int p = 0; p < P; ++p) {
+            const float* kr = kf + (long long)p * D;
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < D / 4; ++i) s += qv[i] * kr[4 * i + sub];
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            s *= scale;
+            const float mn = fmaxf(m, s);
+            const float corr = expf(m - mn);
+            const float e = expf(s - mn);
+            l = l * corr + e;
+            const float* vr = vf + (long long)p * D;
+#pragma unroll
+            for (int i = 0; i < D / 4; ++i) acc[i] = acc[i] * corr + e * vr[4 * i + sub];
+            m = mn;
+        }
+    }
+}
+
+template <int D, int NBR>
+__global__ __launch_bounds__(256) void win_attn_f32_kernel(WinLaunch w) {
+    const int nqt = (w.P + 63) / 64;
+    const int wid = blockIdx.x;
+    const int qt = wid % nqt;
+    const int fq = (wid / nqt) % w.Tq;
+    const int bh = wid / (nqt * w.Tq);
+    const long long fa = w.frame0 + fq;
+    const int sub = threadIdx.x & 3;
+    const int row = qt * 64 + (threadIdx.x >> 2);
+    const bool valid = row < w.P;
+    const int prow = valid ? row : w.P - 1;   // invalid rows compute a duplicate, never stored
+
+    const int nSegA = taps_present(w.taps.offA, w.taps.nA, fa);
+    const int nseg = nSegA + (NBR == 2 ? taps_present(w.taps.offB, w.taps.nB, fa) : 0);
+
+    const float* kbh = static_cast<const float*>(w.k) + (long long)bh * w.kv_bh;
+    const float* vbh = static_cast<const float*>(w.v) + (long long)bh * w.kv_bh;
+    const long long qoff = (long long)bh * w.q_bh + ((long long)fq * w.P + prow) * D;
+    const float* qp = static_cast<const float*>(w.q) + qoff;
+    float qv[D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) qv[i] = qp[4 * i + sub];
+
+    float accA[D / 4], accB[D / 4];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) { accA[i] = 0.f; accB[i] = 0.f; }
+    float mA = -INFINITY, lA = 0.f, mB = -INFINITY, lB = 0.f;
+    if (NBR == 2) {
+        // Own frame once, then both branches continue from that state.
+        f32_branch<D>(w, fa, nSegA, qv, kbh, vbh, 0, 1, sub, mA, lA, accA);
+        mB = mA; lB = lA;
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) accB[i] = accA[i];
+        f32_branch<D>(w, fa, nSegA, qv, kbh, vbh, 1, nSegA, sub, mA, lA, accA);
+        f32_branch<D>(w, fa, nSegA, qv, kbh, vbh, nSegA, nseg, sub, mB, lB, accB);
+    } else {
+        f32_branch<D>(w, fa, nSegA, qv, kbh, vbh, 0, nseg, sub, mA, lA, accA);
+    }
+    if (!valid) return;
+    float* op = static_cast<float*>(w.o) + qoff;
+    const float* ap = w.add ? w.add + qoff : nullptr;
+    const float iA = 1.f / lA;
+    const float iB = NBR == 2 ? 1.f / lB : 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+        float r = accA[i] * iA;
+        if (NBR == 2) r += accB[i] * iB;
+        if (ap) r += ap[4 * i + sub];
+        op[4 * i + sub] = r;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream) {
+    if (w.BH == 0 || w.Tq == 0 || w.P == 0) return hipSuccess;
+    if (w.dtype == 1) {  // bf16, d == 128
+        const int nqt = (w.P + kBQ - 1) / kBQ;
+        const long long nwg = (long long)w.BH * w.Tq * nqt;
+        if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+        if (w.nbr == 2)
+            hipLaunchKernelGGL(win_attn_bf16_kernel<2>, dim3((unsigned)nwg), dim3(256), 0, stream, w);
+        else
+            hipLaunchKernelGGL(win_attn_bf16_kernel<1>, dim3((unsigned)nwg), dim3(256), 0, stream, w);
+        return hipGetLastError();
+    }
+    const int nqt = (w.P + 63) / 64;
+    const long long nwg = (long long)w.BH * w.Tq * nqt;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 g((unsigned)nwg), b(256);
+    if (w.d == 64) {
+        if (w.nbr == 2) hipLaunchKernelGGL((win_attn_f32_kernel<64, 2>), g, b, 0, stream, w);
+        else hipLaunchKernelGGL((win_attn_f32_kernel<64, 1>), g, b, 0, stream, w);
+    } else {
+        if (w.nbr == 2) hipLaunchKernelGGL((win_attn_f32_kernel<128, 2>), g, b, 0, stream, w);
+        else hipLaunchKernelGGL((win_attn_f32_kernel<128, 1>), g, b, 0, stream, w);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hta

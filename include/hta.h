@@ -1,0 +1,191 @@
+/*
+ * hta.h -- C ABI of libhta: Hybrid Linear Temporal Attention on AMD MI355X (gfx950).
+ *
+ * The method (web pages on the Kairos world model, page "Kairos：面向物理 AI 的
+ * 原生世界模型栈" on yingwang.github.io, section 二、方法, second pillar) mixes
+ * three temporal attention branches over a frame-major token sequence:
+ *   SWA  -- softmax attention restricted to a window of W frames (SWA paragraph);
+ *   DSWA -- the same window counted in taps spaced `dilation` frames apart
+ *           (DSWA paragraph, re-layout (B, F*L, D) -> (B*d, F/d*L, D));
+ *   GLA  -- gated linear attention with the gated delta update of a fixed-size
+ *           state S (GLA paragraph and its update equations);
+ * and sums them into one mixed temporal representation (three-branch figure).
+ *
+ * Conventions shared by every entry point
+ *   - Sequence tensors are contiguous [B][H][L][d], L = T*P, token t in frame t/P.
+ *     q and k have d = dk, v and o have d = dv.
+ *   - dtype HTA_BF16: q, k, v (and ring buffers) are bfloat16; accumulation,
+ *     softmax, gates and the GLA state are fp32. dtype HTA_F32: everything fp32.
+ *   - out_dtype: the dtype of o. HTA_F32 inputs give HTA_F32 outputs; HTA_BF16
+ *     inputs may write o as HTA_F32 (the fp32 sum itself) or HTA_BF16 (that sum
+ *     rounded once to nearest-even).
+ *   - alpha, beta: fp32 [B][H][L], per-token forget gate alpha in (0, 1] and write
+ *     strength beta in [0, 1] (the pages: beta = sigmoid(.), alpha in (0,1)).
+ *   - GLA state: fp32 [B][H][dk][dv] holding S^T (S is dv x dk: v_old = S k).
+ *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *     caller. The library allocates no device memory and keeps no global state.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
+ *     the null stream). Results are valid once the stream has synchronised.
+ *   - All arguments are checked before anything is enqueued. On a non-zero
+ *     status nothing has been enqueued and no output, state or ring is touched.
+ *   - Outputs must not alias inputs. The state is updated in place.
+ *
+ * Readings of the pages that the library implements (where they are silent):
+ *   - the SWA window counts the current frame: frames f-W+1..f; attention is
+ *     full inside a frame and never looks at later frames;
+ *   - DSWA tap j reads frame f - j*dilation; taps before frame 0 are absent;
+ *   - softmax scale 1/sqrt(dk) unless given;
+ *   - GLA uses the GatedDeltaNet form the pages name as its basis:
+ *       S_t = alpha_t * (S_{t-1} - beta_t (S_{t-1} k_t) k_t^T) + beta_t v_t k_t^T,
+ *       o_t = gla_scale * S_t q_t   (post-update state);
+ *   - the hybrid output is the unweighted sum o_swa + o_dswa + o_gla in fp32,
+ *     rounded once to the output dtype.
+ */
+#ifndef HTA_H
+#define HTA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (int return value of every entry point). */
+#define HTA_OK               0
+#define HTA_ERR_NULL        (-1)  /* a required pointer is NULL                        */
+#define HTA_ERR_SHAPE       (-2)  /* B,H,T,P < 1, or sizes overflow the index range    */
+#define HTA_ERR_WINDOW      (-3)  /* window, taps or dilation < 1                      */
+#define HTA_ERR_DTYPE       (-4)  /* dtype/out_dtype not HTA_F32 or HTA_BF16, or bf16 out of fp32 in */
+#define HTA_ERR_UNSUPPORTED (-5)  /* dk/dv/chunk/taps outside the supported set        */
+#define HTA_ERR_WORKSPACE   (-6)  /* workspace NULL or smaller than required           */
+#define HTA_ERR_RING        (-7)  /* ring has fewer frames than the windows reach      */
+#define HTA_ERR_HIP         (-8)  /* a HIP call failed; see hta_last_hip_error()       */
+#define HTA_ERR_ALIAS       (-9)  /* an output overlaps an input                       */
+
+typedef enum { HTA_F32 = 0, HTA_BF16 = 1 } hta_dtype;
+
+/* Supported sets: dk == dv in {64, 128}; HTA_BF16 requires dk == dv == 128.
+ * gla_chunk in {16, 32, 64} for HTA_F32 and 64 for HTA_BF16.
+ * window, taps <= 16; window, (taps-1)*dilation + 1 <= 4096 frames. */
+typedef struct {
+    int B, H;       /* batch, heads                                    */
+    int T, P;       /* frames, tokens per frame (L = T*P)              */
+    int dk, dv;     /* query/key and value head dims                   */
+    int dtype;      /* hta_dtype of q, k, v and of the ring buffers    */
+    int out_dtype;  /* hta_dtype of o (HTA_F32, or HTA_BF16 for bf16 inputs) */
+} hta_shape;
+
+typedef struct {
+    int   swa_window;     /* W: SWA frames, current frame included          */
+    int   dswa_taps;      /* W_d: DSWA taps (tap 0 is the current frame)    */
+    int   dswa_dilation;  /* dilation between DSWA taps, in frames          */
+    int   gla_chunk;      /* C: tokens per chunk of the chunked GLA         */
+    float attn_scale;     /* softmax scale; 0 selects 1/sqrt(dk)            */
+    float gla_scale;      /* GLA output scale; 0 selects 1                  */
+} hta_params;
+
+/* Operations whose workspace size hta_workspace_bytes() reports. */
+#define HTA_OP_GLA          1
+#define HTA_OP_HYBRID       2
+#define HTA_OP_STREAM_STEP  3
+
+/*
+ * hta_workspace_bytes -- device workspace (bytes, 256-byte aligned start
+ * expected) that `op` needs for `shape`/`params`. For HTA_OP_STREAM_STEP pass
+ * the per-frame shape (T = 1). Returns 0 if the arguments are invalid (an op
+ * that needs no workspace also returns 0 with valid arguments: HTA_OP_*
+ * always needs some, so 0 means invalid).
+ */
+size_t hta_workspace_bytes(int op, const hta_shape* shape, const hta_params* params);
+
+/*
+ * hta_swa_fwd -- SWA branch alone (SWA paragraph): o[t] = softmax attention of
+ * q[t] over every key of frames f-window+1 .. f (>= 0), f = t / P.
+ * q, k: [B][H][L][dk]; v, o: [B][H][L][dv]; scale 0 selects 1/sqrt(dk).
+ */
+int hta_swa_fwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                void* o, int window_frames, float scale, void* stream);
+
+/*
+ * hta_dswa_fwd -- DSWA branch alone (DSWA paragraph): o[t] = softmax attention
+ * of q[t] over every key of frames f - j*dilation, 0 <= j < taps, >= 0.
+ */
+int hta_dswa_fwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                 void* o, int taps, int dilation_frames, float scale, void* stream);
+
+/*
+ * hta_gla_fwd -- GLA branch alone (GLA paragraph and update equations), chunked.
+ * state: fp32 [B][H][dk][dv] = S^T; in: initial state (zero it for S_0 = 0),
+ * out: state after the last token. o: [B][H][L][dv] (o_t = scale * S_t q_t).
+ * workspace: >= hta_workspace_bytes(HTA_OP_GLA, shape, params with gla_chunk).
+ */
+int hta_gla_fwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                const float* alpha, const float* beta, float* state, void* o,
+                int chunk, float scale, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/*
+ * hta_hybrid_fwd -- the whole layer (three-branch figure): o = o_swa + o_dswa + o_gla
+ * with shared q, k, v. state as in hta_gla_fwd. workspace: >=
+ * hta_workspace_bytes(HTA_OP_HYBRID, shape, params).
+ */
+int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params,
+                   const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, float* state, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Streaming context: the complete resumable memory of the layer after
+ * n_frames frames -- the last R frames of K and V in a ring (frame n lives in
+ * slot n mod R) and the GLA state. The caller owns every buffer; copying the
+ * three buffers and n_frames checkpoints the stream exactly.
+ */
+typedef struct {
+    hta_shape  s;          /* T is ignored (one frame per step); P = tokens per frame */
+    hta_params p;
+    int        R;          /* ring frames; must be >= max(W, (W_d - 1) * dil + 1)     */
+    void*      ring_k;     /* [B][H][R][P][dk], dtype s.dtype                          */
+    void*      ring_v;     /* [B][H][R][P][dv]                                         */
+    float*     state;      /* [B][H][dk][dv] fp32, S^T                                 */
+    long long  n_frames;   /* frames committed so far                                  */
+} hta_stream_ctx;
+
+/*
+ * hta_stream_init -- start a stream after a prefix of T_prefix frames.
+ * k_prefix, v_prefix: [B][H][T_prefix*P][d] (may be NULL when T_prefix == 0);
+ * the last min(T_prefix, R) frames are copied into their ring slots.
+ * state_prefix: the GLA state after the prefix (e.g. hta_hybrid_fwd's output
+ * state), copied into ctx->state; NULL sets the state to zero.
+ * Sets ctx->n_frames = T_prefix on success.
+ */
+int hta_stream_init(hta_stream_ctx* ctx, const void* k_prefix, const void* v_prefix,
+                    int T_prefix, const float* state_prefix, void* stream);
+
+/*
+ * hta_stream_step -- append one frame n = ctx->n_frames:
+ *   1. its K and V go to ring slot n mod R;
+ *   2. the GLA state advances over its P tokens (chunks start at the frame);
+ *   3. if o != NULL, o = o_swa + o_dswa + o_gla for the frame's P queries, with
+ *      SWA over frames n..n-W+1 and DSWA over n - j*dil, read from the ring.
+ * q, k, v: [B][H][P][d]; alpha, beta: [B][H][P]; o: [B][H][P][dv] or NULL
+ * (commit only). workspace: >= hta_workspace_bytes(HTA_OP_STREAM_STEP,
+ * &ctx->s with T = 1, &ctx->p). ctx->n_frames is incremented after a
+ * successful enqueue. A context must not be used by two threads at once.
+ */
+int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta, void* o,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* hta_status_string(int status);
+
+/* hipError_t of the last HTA_ERR_HIP returned on the calling thread (0 if none). */
+int hta_last_hip_error(void);
+
+/* Library version, e.g. "hta 0.1.0 gfx950". */
+const char* hta_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HTA_H */

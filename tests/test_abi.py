@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/hta.h declares, and rejects bad arguments with the
+documented status before anything is enqueued (fake pointers are never
+dereferenced because validation fails first)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from hybrid_linear_temporal_hta_amd import hta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hta.h")
+
+F = ctypes.c_void_p(0x10000000)   # fake device pointers (never touched)
+G = ctypes.c_void_p(0x20000000)
+Hh = ctypes.c_void_p(0x30000000)
+O = ctypes.c_void_p(0x40000000)
+A = ctypes.c_void_p(0x50000000)
+Bt = ctypes.c_void_p(0x60000000)
+S = ctypes.c_void_p(0x70000000)
+W = ctypes.c_void_p(0x80000000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**(hta_[a-z0-9_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert set(names) == set(hta.EXPORTED), names
+    lib = hta.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", hta.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (hta_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_version_and_status_strings():
+    lib = hta.lib()
+    assert b"gfx950" in lib.hta_version()
+    for code in range(-9, 1):
+        assert lib.hta_status_string(code)
+    assert lib.hta_status_string(hta.HTA_ERR_ALIAS).startswith(b"HTA_ERR_ALIAS")
+
+
+def shape(B=1, H=2, T=4, P=16, d=128, dtype=hta.HTA_BF16, out=None):
+    return hta.Shape(B, H, T, P, d, d, dtype, dtype if out is None else out)
+
+
+def swa(s, window=3, scale=0.0, q=F, k=G, v=Hh, o=O):
+    return hta.lib().hta_swa_fwd(ctypes.byref(s) if s is not None else None, q, k, v, o,
+                                 window, scale, None)
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(B=0), hta.HTA_ERR_SHAPE), (dict(T=0), hta.HTA_ERR_SHAPE), (dict(P=0), hta.HTA_ERR_SHAPE),
+    (dict(dtype=7), hta.HTA_ERR_DTYPE), (dict(d=96), hta.HTA_ERR_UNSUPPORTED),
+    (dict(out=5), hta.HTA_ERR_DTYPE), (dict(dtype=hta.HTA_F32, d=64, out=hta.HTA_BF16), hta.HTA_ERR_DTYPE),
+    (dict(d=64), hta.HTA_ERR_UNSUPPORTED),   # bf16 needs d = 128
+])
+def test_shape_errors(mut, code):
+    assert swa(shape(**mut)) == code
+
+
+def test_null_and_window_errors():
+    assert swa(None) == hta.HTA_ERR_NULL
+    assert swa(shape(), q=None) == hta.HTA_ERR_NULL
+    assert swa(shape(), window=0) == hta.HTA_ERR_WINDOW
+    assert swa(shape(), window=17) == hta.HTA_ERR_WINDOW
+    assert swa(shape(), scale=-1.0) == hta.HTA_ERR_UNSUPPORTED
+    assert swa(shape(), scale=float("nan")) == hta.HTA_ERR_UNSUPPORTED
+    lib = hta.lib()
+    s = shape()
+    assert lib.hta_dswa_fwd(ctypes.byref(s), F, G, Hh, O, 0, 2, 0.0, None) == hta.HTA_ERR_WINDOW
+    assert lib.hta_dswa_fwd(ctypes.byref(s), F, G, Hh, O, 4, 0, 0.0, None) == hta.HTA_ERR_WINDOW
+    assert lib.hta_dswa_fwd(ctypes.byref(s), F, G, Hh, O, 4, 2000, 0.0, None) == hta.HTA_ERR_WINDOW
+
+
+def test_alias_detected():
+    s = shape()
+    assert swa(s, o=F) == hta.HTA_ERR_ALIAS
+    nbytes = 1 * 2 * 4 * 16 * 128 * 2
+    assert swa(s, o=ctypes.c_void_p(F.value + nbytes - 2)) == hta.HTA_ERR_ALIAS
+    # adjacent but not overlapping is accepted up to the launch; not called here
+
+
+def test_gla_argument_errors():
+    lib = hta.lib()
+    s = shape()
+    prm = hta.make_params(chunk=64)
+    need = hta.hta_workspace_bytes(hta.HTA_OP_GLA, s, prm)
+    assert need >= 256
+    call = lambda chunk=64, ws=W, wsb=need, **kw: lib.hta_gla_fwd(
+        ctypes.byref(s), kw.get("q", F), G, Hh, A, Bt, kw.get("st", S), O, chunk, 0.0, ws, wsb,
+        None)
+    assert call(chunk=48) == hta.HTA_ERR_UNSUPPORTED
+    assert call(chunk=32) == hta.HTA_ERR_UNSUPPORTED      # bf16 path runs chunk 64
+    assert call(ws=None) == hta.HTA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == hta.HTA_ERR_WORKSPACE
+    assert call(q=None) == hta.HTA_ERR_NULL
+    assert call(st=F) == hta.HTA_ERR_ALIAS
+
+
+def test_workspace_bytes_rules():
+    s = shape()
+    prm = hta.make_params()
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, s, prm) > \
+        hta.hta_workspace_bytes(hta.HTA_OP_GLA, s, prm)
+    assert hta.hta_workspace_bytes(99, s, prm) == 0
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, s, hta.make_params(window=0)) == 0
+    assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, s, prm) == 0     # T must be 1
+    s1 = shape(T=1)
+    assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, s1, prm) > 0
+    # fp32 output: the GLA partial lives in o, so the hybrid needs no extra buffer
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape(out=hta.HTA_F32), prm) == \
+        hta.hta_workspace_bytes(hta.HTA_OP_GLA, shape(out=hta.HTA_F32), prm)
+    f32 = shape(dtype=hta.HTA_F32, d=64)
+    assert hta.hta_workspace_bytes(hta.HTA_OP_GLA, f32, hta.make_params(chunk=16)) > 0
+
+
+def test_stream_ring_too_small():
+    lib = hta.lib()
+    ctx = hta.StreamCtx(shape(T=1), hta.make_params(3, 4, 4, 64), 12, F.value, G.value, S.value, 0)
+    assert lib.hta_stream_step(ctypes.byref(ctx), F, G, Hh, A, Bt, O, W, 1 << 30, None) == \
+        hta.HTA_ERR_RING
+    assert ctx.n_frames == 0
+    ctx.R = 13
+    assert lib.hta_stream_step(ctypes.byref(ctx), F, G, Hh, A, Bt, O, W, 16, None) == \
+        hta.HTA_ERR_WORKSPACE
+    assert lib.hta_stream_init(ctypes.byref(ctx), None, None, 3, None, None) == hta.HTA_ERR_NULL
+    assert ctx.n_frames == 0

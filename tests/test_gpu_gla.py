@@ -1,0 +1,126 @@
+"""GPU parity of the chunked GLA kernels and of the hybrid layer against the oracle.
+
+Expected values come only from the fp64 CPU oracle (token-by-token recurrence,
+definitions of SWA/DSWA) on the same seeded inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, assert_parity, assert_parity_rounded, f64
+from hybrid_linear_temporal_hta_amd import hta
+from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(B, H, T, P, dtype=torch.bfloat16, seed=0, **kw):
+    base = dict(q_unit=True, k_unit=True, alpha_mu=3.0)
+    base.update(kw)
+    return Workload("case", B, H, T, P, 128, 128, dtype, seed=seed, **base)
+
+
+def _gla(x, P, state0=None, out_dtype=torch.float32, chunk=64):
+    B, H, L, d = x["q"].shape
+    st = torch.zeros(B, H, d, d, device="cuda") if state0 is None else state0.clone()
+    o = torch.empty(B, H, L, d, dtype=out_dtype, device="cuda")
+    hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, P, chunk)
+    torch.cuda.synchronize()
+    return o, st
+
+
+@pytest.mark.parametrize("T,P", [(5, 100), (1, 1), (1, 37), (1, 64), (2, 64), (3, 129)])
+def test_gla_bf16_parity(T, P):
+    print(f"[case] gla bf16 T{T} P{P}", flush=True)
+    w = _w(1, 2, T, P, seed=11 + T * P)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v)
+         for k, v in make_inputs(w, frames=T).items()}
+    s0 = (torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(5)) * 0.2).cuda()
+    o, st = _gla(x, P, s0)
+    ref_o, ref_st = oracle.gla(x["q"], x["k"], x["v"], x["alpha"], x["beta"], s0)
+    assert_parity(o, ref_o, torch.bfloat16, "gla o")
+    assert_parity(st, ref_st, torch.bfloat16, "gla state")
+    ob, _ = _gla(x, P, s0, out_dtype=torch.bfloat16)
+    assert_parity_rounded(ob, ref_o, TOL[torch.bfloat16], "gla o bf16-out")
+
+
+def test_gla_bf16_edge_gates():
+    """alpha = 1 (no forgetting) and alpha = 0 (full reset), beta in {0, 1}."""
+    print("[case] gla bf16 edge gates", flush=True)
+    T, P = 3, 50
+    w = _w(1, 2, T, P, seed=21)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v)
+         for k, v in make_inputs(w, frames=T).items()}
+    L = T * P
+    a = torch.ones(1, 2, L, device="cuda")
+    a[:, :, 40] = 0.0            # full reset of the state at token 40
+    b = torch.ones(1, 2, L, device="cuda")
+    b[:, :, ::3] = 0.0
+    x["alpha"], x["beta"] = a.contiguous(), b.contiguous()
+    o, st = _gla(x, P)
+    ref_o, ref_st = oracle.gla(x["q"], x["k"], x["v"], a, b)
+    assert_parity(o, ref_o, torch.bfloat16, "gla o edge gates")
+    assert_parity(st, ref_st, torch.bfloat16, "gla state edge gates")
+
+
+def test_gla_bf16_full_size():
+    """The GLA workload at full size (B1 H16 L32760 d128, chunk 64, zero initial
+    state): every output and the final state against the full recurrence."""
+    w = WORKLOADS["gla_bf16"]
+    print(f"[case] full-size {w.name}", flush=True)
+    x = make_inputs(w, device="cuda")
+    o, st = _gla(x, w.P)
+    ref_o, ref_st = oracle.gla(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
+    assert_parity(o, ref_o, w.dtype, "gla full-size o")
+    assert_parity(st, ref_st, w.dtype, "gla full-size state")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_hybrid_small_parity(dtype):
+    print(f"[case] hybrid small {dtype}", flush=True)
+    T, P = 9, 150
+    w = _w(1, 2, T, P, dtype=dtype, seed=31, q_unit=False, qv_std=1.0)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v)
+         for k, v in make_inputs(w, frames=T).items()}
+    prm = hta.make_params(3, 4, 2, 64)
+    ref_o, ref_st, _ = oracle.hybrid(x["q"], x["k"], x["v"], x["alpha"], x["beta"], T, P, 3, 4, 2)
+    for out_dtype in ((torch.float32, torch.bfloat16) if dtype == torch.bfloat16 else (torch.float32,)):
+        st = torch.zeros(1, 2, 128, 128, device="cuda")
+        o = torch.empty(1, 2, T * P, 128, dtype=out_dtype, device="cuda")
+        hta.hta_hybrid_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, P, prm)
+        torch.cuda.synchronize()
+        if out_dtype == torch.float32:
+            assert_parity(o, ref_o, dtype, "hybrid o")
+        else:
+            assert_parity_rounded(o, ref_o, TOL[dtype], "hybrid o bf16-out")
+        assert_parity(st, ref_st, dtype, "hybrid state")
+
+
+@pytest.mark.slow
+def test_hybrid_full_size_sampled():
+    """The hybrid forward at the benchmark workload (B2 H16 T21 P1560 d128 bf16):
+    the full GLA recurrence (every output, final state) plus SWA/DSWA on sampled
+    rows, combined at the sampled rows."""
+    w = WORKLOADS["hybrid_stream"]
+    print(f"[case] full-size hybrid {w.name}", flush=True)
+    x = make_inputs(w, device="cuda", frames=w.T)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    st = torch.zeros(w.B, w.H, 128, 128, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, 128, dtype=torch.float32, device="cuda")
+    hta.hta_hybrid_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, w.P, prm)
+    torch.cuda.synchronize()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    ref_g, ref_st = oracle.gla(q, k, v, x["alpha"], x["beta"])
+    assert_parity(st, ref_st, w.dtype, "hybrid full-size state")
+    rng = np.random.default_rng(3)
+    rows = set(rng.integers(0, w.B * w.H * w.L, 2000).tolist())
+    for bh in (0, 31):
+        for f in (0, 3, 12, w.T - 1):
+            for p in (0, 1535, w.P - 1):
+                rows.add(bh * w.L + f * w.P + p)
+    rows = np.array(sorted(rows), dtype=np.int64)
+    ref = oracle.swa_rows(q, k, v, w.T, w.P, w.window, rows) + \
+        oracle.dswa_rows(q, k, v, w.T, w.P, w.taps, w.dilation, rows) + \
+        ref_g.reshape(-1, 128)[rows]
+    assert_parity(f64(o).reshape(-1, 128)[rows], ref, w.dtype, "hybrid full-size sampled o")
