@@ -242,6 +242,33 @@ int hta_dswa_fwd(const hta_shape* shape, const void* q, const void* k, const voi
     return window_fwd(1, shape, q, k, v, o, taps, dilation_frames, scale, stream);
 }
 
+int hta_swa_dswa_fwd(const hta_shape* s, const hta_params* p, const void* q, const void* k,
+                     const void* v, const float* add, void* o, void* stream) {
+    int st;
+    if ((st = check_shape(s)) != HTA_OK) return st;
+    if (!p) return HTA_ERR_NULL;
+    if ((st = check_window(p->swa_window)) != HTA_OK) return st;
+    if ((st = check_dilated(p->dswa_taps, p->dswa_dilation)) != HTA_OK) return st;
+    if ((st = check_scale(p->attn_scale)) != HTA_OK) return st;
+    if (!q || !k || !v || !o) return HTA_ERR_NULL;
+    const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
+    const Range rq = range_of(q, nq), rk = range_of(k, nq), rv = range_of(v, nv);
+    const Range ro = range_of(o, out_bytes(s));
+    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return HTA_ERR_ALIAS;
+    if (add) {
+        const Range ra = range_of(add, (size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 4);
+        if (overlap(ra, rq) || overlap(ra, rk) || overlap(ra, rv)) return HTA_ERR_ALIAS;
+        const bool in_place = static_cast<const void*>(add) == o && s->out_dtype == HTA_F32;
+        if (!in_place && overlap(ra, ro)) return HTA_ERR_ALIAS;
+    }
+    hta::WinLaunch w = win_base(s, q, k, v, o, p->attn_scale);
+    w.nbr = 2;
+    w.add = add;
+    taps_hybrid(w.taps, p->swa_window, p->dswa_taps, p->dswa_dilation);
+    hipError_t e = hta::launch_win_attn(w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
 static int check_gla_buffers(const hta_shape* s, const void* q, const void* k, const void* v,
                              const float* alpha, const float* beta, const float* state,
                              const void* o, const void* ws, size_t ws_bytes, size_t ws_need) {

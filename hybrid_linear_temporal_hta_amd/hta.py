@@ -35,7 +35,8 @@ HTA_OP_HYBRID = 2
 HTA_OP_STREAM_STEP = 3
 
 EXPORTED = (
-    "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_gla_fwd", "hta_hybrid_fwd",
+    "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_swa_dswa_fwd", "hta_gla_fwd",
+    "hta_hybrid_fwd",
     "hta_stream_init", "hta_stream_step", "hta_status_string", "hta_last_hip_error",
     "hta_version",
 )
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.hta_swa_fwd.argtypes = [sp, vp, vp, vp, vp, i, f, vp]
     L.hta_dswa_fwd.restype = i
     L.hta_dswa_fwd.argtypes = [sp, vp, vp, vp, vp, i, i, f, vp]
+    L.hta_swa_dswa_fwd.restype = i
+    L.hta_swa_dswa_fwd.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp]
     L.hta_gla_fwd.restype = i
     L.hta_gla_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i, f, vp, sz, vp]
     L.hta_hybrid_fwd.restype = i
@@ -168,6 +171,13 @@ def hta_dswa_fwd(q, k, v, o, P: int, taps: int, dilation_frames: int, scale: flo
     s = make_shape(q, v, P, o)
     _check(lib().hta_dswa_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(taps),
                               int(dilation_frames), float(scale), _stream(stream)), "hta_dswa_fwd")
+
+
+def hta_swa_dswa_fwd(q, k, v, o, P: int, params: Params, add=None, stream=None):
+    s = make_shape(q, v, P, o)
+    _check(lib().hta_swa_dswa_fwd(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(add), _ptr(o), _stream(stream)),
+           "hta_swa_dswa_fwd")
 
 
 def hta_gla_fwd(q, k, v, alpha, beta, state, o, P: int, chunk: int = 64, scale: float = 0.0,

@@ -114,6 +114,19 @@ int hta_dswa_fwd(const hta_shape* shape, const void* q, const void* k, const voi
                  void* o, int taps, int dilation_frames, float scale, void* stream);
 
 /*
+ * hta_swa_dswa_fwd -- SWA and DSWA summed, in one pass over the key frames
+ * (the query's own frame, common to both windows, is attended once):
+ * o = o_swa + o_dswa (+ add). params: swa_window, dswa_taps, dswa_dilation,
+ * attn_scale (gla_* ignored). add: NULL, or an fp32 [B][H][L][dv] partial
+ * (e.g. the GLA branch) added before the single rounding to out_dtype; add
+ * may equal o when out_dtype is HTA_F32 (in-place accumulation), and must not
+ * overlap q, k or v otherwise.
+ */
+int hta_swa_dswa_fwd(const hta_shape* shape, const hta_params* params,
+                     const void* q, const void* k, const void* v, const float* add,
+                     void* o, void* stream);
+
+/*
  * hta_gla_fwd -- GLA branch alone (GLA paragraph and update equations), chunked.
  * state: fp32 [B][H][dk][dv] = S^T; in: initial state (zero it for S_0 = 0),
  * out: state after the last token. o: [B][H][L][dv] (o_t = scale * S_t q_t).
@@ -127,7 +140,9 @@ int hta_gla_fwd(const hta_shape* shape, const void* q, const void* k, const void
 /*
  * hta_hybrid_fwd -- the whole layer (three-branch figure): o = o_swa + o_dswa + o_gla
  * with shared q, k, v. state as in hta_gla_fwd. workspace: >=
- * hta_workspace_bytes(HTA_OP_HYBRID, shape, params).
+ * hta_workspace_bytes(HTA_OP_HYBRID, shape, params). Enqueues exactly what
+ * hta_gla_fwd (writing its fp32 partial into o, or into the workspace for a
+ * bf16 o) followed by hta_swa_dswa_fwd (add = that partial) would.
  */
 int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params,
                    const void* q, const void* k, const void* v,

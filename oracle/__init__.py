@@ -68,6 +68,8 @@ def _load():
             fn = getattr(lib, name)
             fn.restype = i
             fn.argtypes = [i, i, ll, i, i, _dp, _dp, _dp, _dp, _dp, d, _dp, _dp]
+        lib.oracle_num_threads.restype = i
+        lib.oracle_num_threads.argtypes = []
         _lib = lib
         return lib
 
@@ -95,6 +97,11 @@ def _dims(q, k, v):
     if k.shape != (B, H, L, dk) or v.shape[:3] != (B, H, L):
         raise ValueError("q, k, v shapes disagree")
     return B, H, L, dk, v.shape[3]
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def default_scale(dk: int) -> float:
@@ -129,32 +136,38 @@ def dswa(q, k, v, T: int, P: int, taps: int, dilation: int,
     return o
 
 
-def swa_rows(q, k, v, T: int, P: int, window: int, rows,
-             scale: float | None = None) -> np.ndarray:
-    """SWA for the listed flat query rows (bh*L + t); returns [n_rows, dv]."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H, L, dk, dv = _dims(q, k, v)
+def _rows_call(fn_name, q, k, v, T, P, rows, scale, qrows, *args):
+    k, v = _f64(k), _f64(v)
+    if k.ndim != 4 or v.ndim != 4 or k.shape[:3] != v.shape[:3]:
+        raise ValueError("k, v must be [B, H, L, d]")
+    B, H, L, dk = k.shape
+    dv = v.shape[3]
+    if L != T * P:
+        raise ValueError("L must equal T*P")
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if qrows is None:
+        qrows = _f64(q).reshape(-1, dk)[rows]
+    qrows = np.ascontiguousarray(np.asarray(qrows, dtype=np.float64).reshape(rows.size, dk))
     o = np.empty((rows.size, dv), np.float64)
     s = default_scale(dk) if not scale else float(scale)
-    _check(_load().oracle_swa_rows(B, H, T, P, dk, dv, _ptr(q), _ptr(k), _ptr(v),
-                                   int(window), s, rows.size,
-                                   rows.ctypes.data_as(_llp), _ptr(o)), "oracle_swa_rows")
+    fn = getattr(_load(), fn_name)
+    _check(fn(B, H, T, P, dk, dv, _ptr(qrows), _ptr(k), _ptr(v), *args, s, rows.size,
+              rows.ctypes.data_as(_llp), _ptr(o)), fn_name)
     return o
+
+
+def swa_rows(q, k, v, T: int, P: int, window: int, rows,
+             scale: float | None = None, qrows=None) -> np.ndarray:
+    """SWA for the listed flat query rows (bh*L + t); returns [n_rows, dv].
+    The query vectors are q's rows, or ``qrows`` ([n_rows, dk]) when q is None."""
+    return _rows_call("oracle_swa_rows", q, k, v, T, P, rows, scale, qrows, int(window))
 
 
 def dswa_rows(q, k, v, T: int, P: int, taps: int, dilation: int, rows,
-              scale: float | None = None) -> np.ndarray:
+              scale: float | None = None, qrows=None) -> np.ndarray:
     """DSWA for the listed flat query rows (bh*L + t); returns [n_rows, dv]."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H, L, dk, dv = _dims(q, k, v)
-    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
-    o = np.empty((rows.size, dv), np.float64)
-    s = default_scale(dk) if not scale else float(scale)
-    _check(_load().oracle_dswa_rows(B, H, T, P, dk, dv, _ptr(q), _ptr(k), _ptr(v),
-                                    int(taps), int(dilation), s, rows.size,
-                                    rows.ctypes.data_as(_llp), _ptr(o)), "oracle_dswa_rows")
-    return o
+    return _rows_call("oracle_dswa_rows", q, k, v, T, P, rows, scale, qrows, int(taps),
+                      int(dilation))
 
 
 def _gla(fn_name, q, k, v, alpha, beta, state0, scale):
@@ -215,10 +228,9 @@ def stream_frame(k_hist, v_hist, q_new, P: int, window: int, taps: int, dilation
     T = Lh // P
     if T * P != Lh or q_new.shape != (B, H, P, dk):
         raise ValueError("history must hold whole frames and q_new one frame")
-    qh = np.zeros((B, H, Lh, dk), np.float64)
-    qh[:, :, (T - 1) * P:, :] = q_new
     pos = np.arange(P) if rows is None else np.asarray(rows, dtype=np.int64)
     flat = (np.arange(B * H)[:, None] * Lh + (T - 1) * P + pos[None, :]).reshape(-1)
-    o = swa_rows(qh, k_hist, v_hist, T, P, window, flat, attn_scale) + \
-        dswa_rows(qh, k_hist, v_hist, T, P, taps, dilation, flat, attn_scale)
+    qr = q_new[:, :, pos, :].reshape(-1, dk)
+    o = swa_rows(None, k_hist, v_hist, T, P, window, flat, attn_scale, qrows=qr) + \
+        dswa_rows(None, k_hist, v_hist, T, P, taps, dilation, flat, attn_scale, qrows=qr)
     return o.reshape(B, H, pos.size, dv)

@@ -43,6 +43,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_OK 0
 #define ORC_EARG (-1)
@@ -108,11 +111,12 @@ static int dswa_frames(int f, int taps, int dil, int *frames)
 
 /*
  * Windowed attention for an explicit list of query rows.
- * rows[r] is a flat token index bh*L + t. out is [n_rows][dv].
+ * rows[r] is the flat token index bh*L + t the query sits at (it fixes the key
+ * window); qrows[r] is that query's vector ([n_rows][dk]). out is [n_rows][dv].
  * kind 0 = SWA (a = window), kind 1 = DSWA (a = taps, b = dilation).
  */
 static int window_rows(int kind, int B, int H, int T, int P, int dk, int dv,
-                       const double *q, const double *k, const double *v,
+                       const double *qrows, const double *k, const double *v,
                        int a, int b, double scale, long long n_rows,
                        const long long *rows, double *out)
 {
@@ -131,7 +135,7 @@ static int window_rows(int kind, int B, int H, int T, int P, int dk, int dv,
         int *frames = (int *)malloc(sizeof(int) * (size_t)a);
         if (!frames) { status = ORC_ENOMEM; continue; }
         int nf = (kind == 0) ? swa_frames(f, a, frames) : dswa_frames(f, a, b, frames);
-        int st = attend_frames(q + rows[r] * dk, k + bh * L * dk, v + bh * L * dv,
+        int st = attend_frames(qrows + r * dk, k + bh * L * dk, v + bh * L * dv,
                                P, dk, dv, frames, nf, scale, out + r * dv);
         if (st != ORC_OK) status = st;
         free(frames);
@@ -139,22 +143,22 @@ static int window_rows(int kind, int B, int H, int T, int P, int dk, int dv,
     return status;
 }
 
-/* SWA over the listed query rows ([P1] SWA paragraph). */
+/* SWA for the listed query rows ([P1] SWA paragraph); qrows: [n_rows][dk]. */
 int oracle_swa_rows(int B, int H, int T, int P, int dk, int dv,
-                    const double *q, const double *k, const double *v,
+                    const double *qrows, const double *k, const double *v,
                     int window, double scale, long long n_rows,
                     const long long *rows, double *out)
 {
-    return window_rows(0, B, H, T, P, dk, dv, q, k, v, window, 0, scale, n_rows, rows, out);
+    return window_rows(0, B, H, T, P, dk, dv, qrows, k, v, window, 0, scale, n_rows, rows, out);
 }
 
-/* DSWA over the listed query rows ([P1] DSWA paragraph). */
+/* DSWA for the listed query rows ([P1] DSWA paragraph); qrows: [n_rows][dk]. */
 int oracle_dswa_rows(int B, int H, int T, int P, int dk, int dv,
-                     const double *q, const double *k, const double *v,
+                     const double *qrows, const double *k, const double *v,
                      int taps, int dilation, double scale, long long n_rows,
                      const long long *rows, double *out)
 {
-    return window_rows(1, B, H, T, P, dk, dv, q, k, v, taps, dilation, scale, n_rows, rows, out);
+    return window_rows(1, B, H, T, P, dk, dv, qrows, k, v, taps, dilation, scale, n_rows, rows, out);
 }
 
 static int window_all(int kind, int B, int H, int T, int P, int dk, int dv,
@@ -264,4 +268,14 @@ int oracle_gla_literal(int B, int H, long long L, int dk, int dv,
                        double *state, double *o)
 {
     return gla_run(1, B, H, L, dk, dv, q, k, v, alpha, beta, scale, state, o);
+}
+
+/* Threads the parallel loops above use (the OpenMP team size). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
