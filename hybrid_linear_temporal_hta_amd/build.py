@@ -30,31 +30,34 @@ CXXFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CXXFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, obj_dir: str = OBJ_DIR, defines=()) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *CXXFLAGS, *["-D" + d for d in defines], "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libhta.so; returns the library path."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every HIP source and link libhta.so (or `out`, with extra -D
+    `defines` for tuning variants); returns the library path."""
+    obj_dir = OBJ_DIR if out == LIB else out + ".objs"
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, defines), srcs))
+    LIBP = out
+    tmp = LIBP + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, LIBP)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {LIBP} from {len(srcs)} sources")
+    return LIBP
 
 
 if __name__ == "__main__":

@@ -42,9 +42,17 @@ namespace {
 constexpr int kD = 128;          // head dim of the bf16 kernel
 constexpr int kBQ = 128;         // query rows per workgroup
 constexpr int kBK = 64;          // keys per LDS tile
-constexpr int kKPad = kD + 8;    // K tile row stride (bf16 elements)
-constexpr int kVPad = kBK + 4;   // V^T tile row stride (bf16 elements)
+constexpr int kRowB = kD * 2;    // bytes per K / V row in LDS (unpadded, chunk-swizzled)
+constexpr int kTileB = kBK * kRowB;
 constexpr float kLazyLog2 = 8.0f;
+#ifndef HTA_ATTN_STAGES
+#define HTA_ATTN_STAGES 2
+#endif
+constexpr int kStages = HTA_ATTN_STAGES;   // LDS ring depth of K/V tiles
+
+// 16-byte chunk c of LDS row r lives in slot c ^ swz(r): conflict-free for both
+// the K fragment reads (32 rows x one chunk) and the transposed V reads.
+__device__ __forceinline__ int swz(int r) { return (r & 7) << 1; }
 
 struct Acc {
     f32x16 o[4];   // O^T fragments: d-block db, element i -> d = 32 db + 8(i/4) + 4 h + i%4
@@ -76,70 +84,59 @@ __device__ __forceinline__ long long seg_frame(const WinLaunch& w, long long fa,
     return w.R > 0 ? (f % w.R) : f;
 }
 
-struct TileRegs {
-    u32x4 k[4];
-    u32x4 v[4];
-};
-
-// Global -> registers for one 64-key tile (rows >= nvalid are zero).
-__device__ __forceinline__ void load_tile(TileRegs& r, const bf16* kbase, const bf16* vbase,
-                                          int nvalid, int tid) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        const int key = c >> 4;
-        const int col = (c & 15) * 8;
-        if (key < nvalid)
-            r.k[i] = *reinterpret_cast<const u32x4*>(kbase + (long long)key * kD + col);
-        else
-            r.k[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-    const int kg = tid & 15, dg = tid >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int key = 4 * kg + i;
-        if (key < nvalid)
-            r.v[i] = *reinterpret_cast<const u32x4*>(vbase + (long long)key * kD + 8 * dg);
-        else
-            r.v[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Registers -> LDS: K row-major (padded), V transposed to V^T[d][key].
-__device__ __forceinline__ void store_tile(const TileRegs& r, bf16* Ks, bf16* Vt, int tid) {
+// One global_load_lds_dwordx4: 16 bytes from gptr (per lane) into LDS at
+// lds_base + 16 * lane (lds_base wave-uniform). Written as asm so that the
+// compiler does not serialise it against the LDS reads of other stages (it
+// cannot tell the buffers apart); completion is tracked by wait_vmcnt. It has
+// no register outputs.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+    typedef __attribute__((address_space(3))) const char lds_char;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(gptr)
+                 : "m0");
+}
+
+// Enqueue one 64-key tile of K and V straight into LDS (global_load_lds_dwordx4):
+// wave w, instruction i writes LDS chunks [64 (4w + i), +64) of each tile, lane l
+// chunk 64 (4w + i) + l = row r, slot c ^ swz(r). Rows past the frame's end
+// re-read the last valid row (finite values; their logits are masked).
+__device__ __forceinline__ void issue_tile(char* ks, char* vs, const bf16* kbase,
+                                           const bf16* vbase, int nvalid, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        const int key = c >> 4;
-        const int col = (c & 15) * 8;
-        *reinterpret_cast<u32x4*>(Ks + key * kKPad + col) = r.k[i];
-    }
-    const int kg = tid & 15, dg = tid >> 4;
-    // r.v[i] holds keys 4kg+i, d = 8dg .. 8dg+7 (two bf16 per dword).
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {            // dword w covers d = 8dg + 2w, 8dg + 2w + 1
-        const uint32_t a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
-        u32x2 lo, hi;                         // lo: d even, hi: d odd; keys 4kg..4kg+3
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(Vt + (8 * dg + 2 * w) * kVPad + 4 * kg) = lo;
-        *reinterpret_cast<u32x2*>(Vt + (8 * dg + 2 * w + 1) * kVPad + 4 * kg) = hi;
+        const int p = 64 * (4 * wave + i) + lane;
+        const int r = p >> 4;
+        const int c = (p & 15) ^ swz(r);
+        const long long off = (long long)min(r, nvalid - 1) * kD + c * 8;
+        dma16(kbase + off, ks + 1024 * (4 * wave + i));
+        dma16(vbase + off, vs + 1024 * (4 * wave + i));
     }
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, lazy online softmax, O^T += V^T P^T.
-__device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const bf16* Ks,
-                                            const bf16* Vt, int nvalid, float c, int n, int h) {
+__device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const char* Ks,
+                                            const char* Vs, int nvalid, float c, int lane) {
+    const int n = lane & 31, h = lane >> 5;
+    const bool two = nvalid > 32;   // second 32-key block has valid keys
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[kb][i] = kb == 0 || two ? 0.f : -INFINITY;
+        if (kb == 1 && !two) continue;
+        const int r = kb * 32 + n;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + n) * kKPad + 16 * ks + 8 * h);
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + r * kRowB + 16 * ((2 * ks + h) ^ swz(r)));
             s[kb] = mfma32(kf, qf[ks], s[kb]);
         }
     }
@@ -185,24 +182,38 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
                 lsum = add_pair(bf16x2{pf[kb][gg][j], pf[kb][gg][j + 1]}, lsum);
         }
     a.l += lsum;
+    // V^T fragments by transposed LDS reads: within each 16-lane group g, lane
+    // 4j + a addresses row (key) base + 4(g/2) + j, columns 16(g%2) + 4a .. +3 of
+    // the d-block; the read hands lane 4a + b column b of rows j = 0..3.
+    const int g = lane >> 4, sl = lane & 15, jr = sl >> 2, ac = sl & 3;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const bf16* vrow = Vt + (db * 32 + n) * kVPad;
+        const int col = 32 * db + 16 * (g & 1) + 4 * ac;
+        const int c16 = col >> 3, half = (col >> 2) & 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int gg = 0; gg < 2; ++gg) {
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + kb * 32 + 16 * gg + 4 * h);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + kb * 32 + 16 * gg + 8 + 4 * h);
+                if (kb == 1 && !two) continue;
+                const int r0 = kb * 32 + 16 * gg + 4 * (g >> 1) + jr;
+                const int r1 = r0 + 8;
+                typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(Vs + r0 * kRowB + 16 * (c16 ^ swz(r0)) + 8 * half));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4*)(Vs + r1 * kRowB + 16 * (c16 ^ swz(r1)) + 8 * half));
                 a.o[db] = mfma32(cat(lo, hi), pf[kb][gg], a.o[db]);
             }
     }
 }
 
-template <int NBR>
-__global__ __launch_bounds__(256) void win_attn_bf16_kernel(WinLaunch w) {
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBK * kKPad];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][kD * kVPad];
+// Two waves per SIMD for the single-branch kernel (fits 256 registers without
+// spilling); the fused two-branch kernel keeps two accumulator sets and runs at one.
+template <int NBR, int NST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3 - NBR, 3 - NBR)))
+void win_attn_bf16_kernel(WinLaunch w) {
+    __shared__ __attribute__((aligned(1024))) char Kst[NST][kTileB];
+    __shared__ __attribute__((aligned(1024))) char Vst[NST][kTileB];
 
     const int nqt = (w.P + kBQ - 1) / kBQ;
     const int nwg = w.BH * w.Tq * nqt;
@@ -225,8 +236,26 @@ __global__ __launch_bounds__(256) void win_attn_bf16_kernel(WinLaunch w) {
     const int ntk = (w.P + kBK - 1) / kBK;
     const int nit = nseg * ntk;
 
+    auto tile_src = [&](int it, const bf16*& kb, const bf16*& vb, int& nv) {
+        const int sg = it / ntk, tk = it - sg * ntk;
+        const long long ofs = seg_frame(w, fa, sg, nSegA) * w.kv_frame + (long long)tk * kBK * kD;
+        kb = kbh + ofs;
+        vb = vbh + ofs;
+        nv = min(kBK, w.P - tk * kBK);
+    };
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st) {
+        if (st < nit) {
+            const bf16 *kb, *vb;
+            int nv;
+            tile_src(st, kb, vb, nv);
+            issue_tile(Kst[st], Vst[st], kb, vb, nv, wave, lane);
+        }
+    }
+
     // Query fragments (B operand of S^T = K Q^T).
     const int qrow = qt * kBQ + wave * 32 + n;
+    const bool wave_rows = qt * kBQ + wave * 32 < w.P;
     const bf16* qp = static_cast<const bf16*>(w.q) + (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
     bf16x8 qf[8];
 #pragma unroll
@@ -242,29 +271,25 @@ __global__ __launch_bounds__(256) void win_attn_bf16_kernel(WinLaunch w) {
     acc_init(A);
     acc_init(Bacc);
 
-    TileRegs tr;
-    {
-        const long long kofs = seg_frame(w, fa, 0, nSegA) * w.kv_frame;
-        load_tile(tr, kbh + kofs, vbh + kofs, min(kBK, w.P), tid);
-        store_tile(tr, Ks[0], Vt[0], tid);
-    }
-    __syncthreads();
-
     for (int it = 0; it < nit; ++it) {
-        const int cur = it & 1;
+        // tile `it` landed (its loads were issued NST-1 tiles ago) ...
+        if (NST >= 3 && it + 1 < nit) wait_vmcnt<8 * (NST >= 3 ? NST - 2 : 0)>();
+        else wait_vmcnt<0>();
+        __syncthreads();   // ... for every wave; and the buffer refilled next was read by all
+        if (it + NST - 1 < nit) {
+            const bf16 *kb, *vb;
+            int nv;
+            tile_src(it + NST - 1, kb, vb, nv);
+            issue_tile(Kst[(it + NST - 1) % NST], Vst[(it + NST - 1) % NST], kb, vb, nv, wave, lane);
+        }
         const int sg = it / ntk, tk = it - sg * ntk;
         const int nvalid = min(kBK, w.P - tk * kBK);
-        const bool more = it + 1 < nit;
-        if (more) {
-            const int sg1 = (it + 1) / ntk, tk1 = (it + 1) - sg1 * ntk;
-            const long long kofs = seg_frame(w, fa, sg1, nSegA) * w.kv_frame + (long long)tk1 * kBK * kD;
-            load_tile(tr, kbh + kofs, vbh + kofs, min(kBK, w.P - tk1 * kBK), tid);
+        const int cur = it % NST;
+        if (wave_rows) {   // waves whose 32 query rows all lie past the frame only stage tiles
+            if (NBR == 1 || sg < nSegA) attend_tile(A, qf, Kst[cur], Vst[cur], nvalid, c, lane);
+            else attend_tile(Bacc, qf, Kst[cur], Vst[cur], nvalid, c, lane);
         }
-        if (NBR == 1 || sg < nSegA) attend_tile(A, qf, Ks[cur], Vt[cur], nvalid, c, n, h);
-        else attend_tile(Bacc, qf, Ks[cur], Vt[cur], nvalid, c, n, h);
         if (NBR == 2 && sg == 0 && tk == ntk - 1) Bacc = A;   // own frame seeds branch B
-        if (more) store_tile(tr, Ks[cur ^ 1], Vt[cur ^ 1], tid);
-        __syncthreads();
     }
 
     // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add), rounded once.
@@ -399,9 +424,9 @@ hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream) {
         const long long nwg = (long long)w.BH * w.Tq * nqt;
         if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
         if (w.nbr == 2)
-            hipLaunchKernelGGL(win_attn_bf16_kernel<2>, dim3((unsigned)nwg), dim3(256), 0, stream, w);
+            hipLaunchKernelGGL((win_attn_bf16_kernel<2, kStages>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
         else
-            hipLaunchKernelGGL(win_attn_bf16_kernel<1>, dim3((unsigned)nwg), dim3(256), 0, stream, w);
+            hipLaunchKernelGGL((win_attn_bf16_kernel<1, kStages>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
         return hipGetLastError();
     }
     const int nqt = (w.P + 63) / 64;

@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhta.so")
+# HTA_LIBRARY selects another build of the same library (tuning variants).
+LIB_PATH = os.environ.get("HTA_LIBRARY") or os.path.join(_HERE, "libhta.so")
 
 HTA_OK = 0
 HTA_ERR_NULL = -1

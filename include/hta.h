@@ -114,9 +114,10 @@ int hta_dswa_fwd(const hta_shape* shape, const void* q, const void* k, const voi
                  void* o, int taps, int dilation_frames, float scale, void* stream);
 
 /*
- * hta_swa_dswa_fwd -- SWA and DSWA summed, in one pass over the key frames
- * (the query's own frame, common to both windows, is attended once):
- * o = o_swa + o_dswa (+ add). params: swa_window, dswa_taps, dswa_dilation,
+ * hta_swa_dswa_fwd -- SWA and DSWA summed: o = o_swa + o_dswa (+ add). The
+ * branches run as two passes accumulating in fp32 (in o when out_dtype is
+ * HTA_F32, else in `add`); a bf16 o with add == NULL is computed in one fused
+ * pass instead. params: swa_window, dswa_taps, dswa_dilation,
  * attn_scale (gla_* ignored). add: NULL, or an fp32 [B][H][L][dv] partial
  * (e.g. the GLA branch) added before the single rounding to out_dtype; add
  * may equal o when out_dtype is HTA_F32 (in-place accumulation), and must not
