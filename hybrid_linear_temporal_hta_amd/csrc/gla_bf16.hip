@@ -1,4 +1,4 @@
-// gla_bf16.hip -- chunked gated-delta GLA on bf16 MFMA (gfx950), fp32 state.
+// gla_bf16.hip -- chunked gated-delta GLA on MFMA (gfx950), bf16 in, fp32 state.
 //
 // Method: page "Kairos：面向物理 AI 的原生世界模型栈" (yingwang.github.io), section
 // 二、方法, GLA paragraph and update equations, GatedDeltaNet reading:
@@ -10,27 +10,30 @@
 //   O = diag(e^g) (Q M0) + Pm U,       Pm = tril(Q K^T o e^{g_i - g_j})
 //   M = e^{g_C} M0 + K^T (diag(e^{g_C - g}) U)
 //
-// Precision: the inputs are bf16 and every accumulation is fp32; the operands
-// the kernels build themselves (T, Pm, the state copy fed to K M0 / Q M0, X,
-// U) are rounded to fp16, whose 11-bit significand keeps the chunk algebra
-// about 8x closer to the exact result than bf16 operands would (bf16 inputs
-// convert to fp16 exactly). fp16 bounds their range: |v| and |state| must stay
-// below 65504 (with unit-norm keys, as the contraction of the update needs).
+// Precision: inputs are bf16 and every accumulation is fp32; the operands the
+// kernels build themselves (K and Q re-expressed in fp16 -- exact --, T, Pm,
+// the state copy fed to K M0 / Q M0, X, U) are fp16, whose 11-bit significand
+// keeps the chunk algebra about 8x closer to exact than bf16 operands would.
+// fp16 bounds their range: |v| and |state| must stay below 65504 (with
+// unit-norm keys, as the contraction of the update needs).
 //
 // Two kernels:
 //   prep (one workgroup per chunk, all chunks in parallel): g, A and Pm from
-//     K K^T and Q K^T on v_mfma_f32_32x32x16_bf16, then T by a register-resident
-//     forward substitution in fp32 (4 lanes per column, 16 columns per wave).
-//     Writes T and Pm (fp16) and g (fp32) per chunk to the workspace.
+//     K K^T and Q K^T on v_mfma_f32_32x32x16_bf16, T by a register-resident
+//     forward substitution in fp32, and the chunk's operand block -- K, Q (fp16),
+//     T, Pm (fp16), g, beta (fp32) -- written contiguously in exactly the LDS
+//     layout the scan consumes (bank-conflict-free swizzles included).
 //   scan (one workgroup per (batch, head, 64 value columns), chunks in order):
 //     each wave owns 16 value columns of the fp32 state as eight 16x16 MFMA
 //     accumulator tiles. K M0, Q M0, T X, Pm U and K^T U run on
-//     v_mfma_f32_16x16x32_f16; every product whose B operand is a previous
-//     result (M0, X, U) takes it straight from the accumulator registers, the
-//     token/key order inside a k-step being permuted identically in A and B,
-//     so the state never leaves registers. K, K^T (transposed on the way in),
-//     Q, T, Pm, g and beta of the next chunk are staged through LDS (double
-//     buffered) while the current chunk computes.
+//     v_mfma_f32_16x16x32_f16; the B operands that are previous results (M0,
+//     X, U) come straight from accumulator registers (token order permuted
+//     identically in A and B), and K^T fragments are transposed LDS reads of
+//     row-major K. The next chunk's operand block and value tile stream into
+//     the other half of a two-stage LDS ring with direct global->LDS loads
+//     while the current chunk computes.
+#include <type_traits>
+
 #include "device_common.h"
 #include "hta_internal.h"
 
@@ -41,10 +44,33 @@ namespace {
 constexpr int kC = 64;                 // chunk
 constexpr int kD = 128;                // head dim
 constexpr float kLogFloor = -1.0e4f;   // log(alpha) floor: alpha = 0 decays to exactly 0
-constexpr size_t kChunkBytes = 2 * kC * kC * 2 + kC * 4;   // T, Pm (fp16) + g (fp32)
 
-__device__ __forceinline__ char* chunk_ws(void* ws, long long cid) {
-    return static_cast<char*>(ws) + (size_t)cid * kChunkBytes;
+// Operand block of one chunk (workspace and LDS stage share this layout).
+constexpr int kOffK = 0;               // K fp16 [64][128], 16-byte chunks swizzled by swz64
+constexpr int kOffQ = 16384;           // Q fp16, same layout
+constexpr int kOffT = 32768;           // T fp16 [64][64], chunks swizzled by swz32
+constexpr int kOffP = 40960;           // Pm fp16, same layout
+constexpr int kOffE = 49152;           // e^{g_t} fp32 [64]
+constexpr int kOffD = 49408;           // e^{g_C - g_t} fp32 [64]
+constexpr int kOffB = 49664;           // beta fp32 [64] (0 past the end of the sequence)
+constexpr int kBlockMain = 49152;      // K, Q, T, Pm: 48 KiB = 12 x 4 KiB
+constexpr int kTailChunks = 48;        // eg, ed, beta: 768 bytes = 48 x 16
+constexpr size_t kChunkBytes = 49920;  // + eg, ed, beta
+constexpr int kOffV = 49920;           // LDS only: V tile bf16 [64 tokens][64 columns]
+constexpr int kStageBytes = kOffV + 64 * 64 * 2;   // 58112
+
+// 256-byte rows (K, Q): chunk c of row r in slot c ^ swz64(r).
+__device__ __forceinline__ int swz64(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// 128-byte rows (T, Pm): chunk c of row r in slot c ^ swz32(r).
+__device__ __forceinline__ int swz32(int r) { return (r >> 1) & 7; }
+// 128-byte rows of the V tile.
+__device__ __forceinline__ int swzv(int r) { return 2 * ((r >> 2) & 3); }
+
+__device__ __forceinline__ int offK(int row, int col) {   // byte offset of element (row, col)
+    return row * 256 + 16 * ((col >> 3) ^ swz64(row)) + 2 * (col & 7);
+}
+__device__ __forceinline__ int offT(int row, int col) {
+    return row * 128 + 16 * ((col >> 3) ^ swz32(row)) + 2 * (col & 7);
 }
 
 // ------------------------------------------------------------------ prep
@@ -65,17 +91,19 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bf16* kp = static_cast<const bf16*>(g.k) + ((long long)bh * g.L + t0) * kD;
     const bf16* qp = static_cast<const bf16*>(g.q) + ((long long)bh * g.L + t0) * kD;
-    char* wsc = chunk_ws(g.ws, cid);
-    f16* Tw = reinterpret_cast<f16*>(wsc);
-    f16* Pw = Tw + kC * kC;
-    float* gw = reinterpret_cast<float*>(Pw + kC * kC);
+    char* blk = static_cast<char*>(g.ws) + (size_t)cid * kChunkBytes;
 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int ci = tid + 256 * r, row = ci >> 4, col = (ci & 15) * 8;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (row < n) val = *reinterpret_cast<const u32x4*>(kp + (long long)row * kD + col);
-        *reinterpret_cast<u32x4*>(Ks + row * kKsP + col) = val;
+        const int ci = tid + 256 * r, row = ci >> 4, cc = ci & 15;
+        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+        if (row < n) {
+            kv = *reinterpret_cast<const u32x4*>(kp + (long long)row * kD + 8 * cc);
+            qv = *reinterpret_cast<const u32x4*>(qp + (long long)row * kD + 8 * cc);
+        }
+        *reinterpret_cast<u32x4*>(Ks + row * kKsP + 8 * cc) = kv;
+        *reinterpret_cast<u32x4*>(blk + kOffK + offK(row, 8 * cc)) = bf16x8_to_f16x8(kv);
+        *reinterpret_cast<u32x4*>(blk + kOffQ + offK(row, 8 * cc)) = bf16x8_to_f16x8(qv);
     }
     if (wave == 0) {
         // inclusive prefix sum of log(alpha) over the chunk (alpha = 1 past the end)
@@ -89,9 +117,13 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
             const float y = __shfl_up(la, off, 64);
             if (lane >= off) la += y;
         }
+        const float b = lane < n ? g.beta[(long long)bh * g.L + t0 + lane] : 0.f;
+        const float gC = __shfl(la, 63, 64);
         gs[lane] = la;
-        gw[lane] = la;
-        bs[lane] = lane < n ? g.beta[(long long)bh * g.L + t0 + lane] : 0.f;
+        bs[lane] = b;
+        reinterpret_cast<float*>(blk + kOffE)[lane] = __expf(la);
+        reinterpret_cast<float*>(blk + kOffD)[lane] = __expf(gC - la);
+        reinterpret_cast<float*>(blk + kOffB)[lane] = b;
     }
     __syncthreads();
 
@@ -123,7 +155,7 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
             const int i = mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
             const float dec = (j <= i) ? __expf(gs[i] - gs[j]) : 0.f;
             As[i * kAsP + (j & 3) * 16 + (j >> 2)] = (j < i) ? bs[i] * dec * kk[e] : 0.f;
-            Pw[i * kC + j] = (f16)((j <= i) ? dec * qk[e] : 0.f);
+            *reinterpret_cast<f16*>(blk + kOffP + offT(i, j)) = (f16)((j <= i) ? dec * qk[e] : 0.f);
         }
     }
     __syncthreads();
@@ -150,116 +182,71 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
             if ((i & 3) == sub) x[i >> 2] = xi;
         }
 #pragma unroll
-        for (int m = 0; m < 16; ++m) Tw[(sub + 4 * m) * kC + col] = (f16)x[m];
+        for (int m = 0; m < 16; ++m)
+            *reinterpret_cast<f16*>(blk + kOffT + offT(sub + 4 * m, col)) = (f16)x[m];
     }
 }
 
 // ------------------------------------------------------------------ scan
 
-constexpr int kQP = kD + 8;    // Ks / Qs row stride
-constexpr int kTP = kC + 8;    // Kt / Ts / Ps row stride
+// One global_load_lds_dwordx4 (16 bytes per lane into LDS at base + 16 * lane,
+// base wave-uniform). Written as asm so the compiler does not serialise it
+// against LDS reads of the other stage; completion is tracked by wait_vmcnt0.
+// It has no register outputs.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+    typedef __attribute__((address_space(3))) const char lds_char;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(gptr) : "m0");
+}
 
-struct ScanBuf {                 // fp16 operands of the scan's products
-    f16 Ks[kC * kQP];
-    f16 Qs[kC * kQP];
-    f16 Kt[kD * kTP];
-    f16 Ts[kC * kTP];
-    f16 Ps[kC * kTP];
-    float gs[kC];
-    float egs[kC];
-    float bs[kC];
-};
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
 
-struct StageRegs {
-    u32x4 k[4];
-    u32x4 q[4];
-    u32x4 t[2];
-    u32x4 p[2];
-    f32x4 gb;
-};
-
-__device__ __forceinline__ void stage_load(StageRegs& r, const GlaLaunch& g, int bh, long long c,
-                                           int tid) {
+// Enqueue chunk c's operand block and the 64-column V tile into an LDS stage.
+__device__ __forceinline__ void issue_chunk(char* stage, const GlaLaunch& g, int bh, int tile,
+                                            long long c, long long nch, int wave, int lane) {
+    const char* blk = static_cast<const char*>(g.ws) + (size_t)((long long)bh * nch + c) * kChunkBytes;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+        const int q = 12 * wave + i;
+        dma16(blk + 1024 * q + 16 * lane, stage + 1024 * q);
+    }
+    if (wave == 0 && lane < kTailChunks) dma16(blk + kBlockMain + 16 * lane, stage + kBlockMain);
     const long long t0 = c * kC;
     const int n = (int)min((long long)kC, g.L - t0);
-    const bf16* kp = static_cast<const bf16*>(g.k) + ((long long)bh * g.L + t0) * kD;
-    const bf16* qp = static_cast<const bf16*>(g.q) + ((long long)bh * g.L + t0) * kD;
-    const int kg = tid & 15, dg = tid >> 4;
+    const bf16* vb = static_cast<const bf16*>(g.v) + ((long long)bh * g.L + t0) * kD + tile * 64;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        const int tok = 4 * kg + r4;
-        r.k[r4] = tok < n ? *reinterpret_cast<const u32x4*>(kp + (long long)tok * kD + 8 * dg)
-                          : u32x4{0u, 0u, 0u, 0u};
-        const int ci = tid + 256 * r4, row = ci >> 4, col = (ci & 15) * 8;
-        r.q[r4] = row < n ? *reinterpret_cast<const u32x4*>(qp + (long long)row * kD + col)
-                          : u32x4{0u, 0u, 0u, 0u};
-    }
-    const f16* Tw = reinterpret_cast<const f16*>(chunk_ws(g.ws, (long long)bh * ((g.L + kC - 1) / kC) + c));
-    const f16* Pw = Tw + kC * kC;
-    const float* gw = reinterpret_cast<const float*>(Pw + kC * kC);
-#pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2) {
-        const int ci = tid + 256 * r2;
-        r.t[r2] = *reinterpret_cast<const u32x4*>(Tw + ci * 8);
-        r.p[r2] = *reinterpret_cast<const u32x4*>(Pw + ci * 8);
-    }
-    if (tid < 16) {
-        r.gb = *reinterpret_cast<const f32x4*>(gw + 4 * tid);
-    } else if (tid < 32) {
-        const int b0 = 4 * (tid - 16);
-        const float* bp = g.beta + (long long)bh * g.L + t0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r.gb[u] = (b0 + u < n) ? bp[b0 + u] : 0.f;
+    for (int i = 0; i < 2; ++i) {
+        const int p = 64 * (2 * wave + i) + lane;
+        const int tok = p >> 3;
+        const int cc = (p & 7) ^ swzv(tok);
+        dma16(vb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * wave + i));
     }
 }
 
-__device__ __forceinline__ void stage_store(const StageRegs& r, ScanBuf& b, int tid) {
-    const int kg = tid & 15, dg = tid >> 4;
-    u32x4 kh[4];                             // K as fp16 (exact)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        kh[r4] = bf16x8_to_f16x8(r.k[r4]);
-        *reinterpret_cast<u32x4*>(b.Ks + (4 * kg + r4) * kQP + 8 * dg) = kh[r4];
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {            // transpose 4 tokens x 8 dims into Kt[dim][token]
-        const uint32_t a0 = kh[0][w], a1 = kh[1][w], a2 = kh[2][w], a3 = kh[3][w];
-        u32x2 lo, hi;
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(b.Kt + (8 * dg + 2 * w) * kTP + 4 * kg) = lo;
-        *reinterpret_cast<u32x2*>(b.Kt + (8 * dg + 2 * w + 1) * kTP + 4 * kg) = hi;
-    }
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        const int ci = tid + 256 * r4, row = ci >> 4, col = (ci & 15) * 8;
-        *reinterpret_cast<u32x4*>(b.Qs + row * kQP + col) = bf16x8_to_f16x8(r.q[r4]);
-    }
-#pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2) {
-        const int ci = tid + 256 * r2, row = ci >> 3, col = (ci & 7) * 8;
-        *reinterpret_cast<u32x4*>(b.Ts + row * kTP + col) = r.t[r2];
-        *reinterpret_cast<u32x4*>(b.Ps + row * kTP + col) = r.p[r2];
-    }
-    if (tid < 16) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            b.gs[4 * tid + u] = r.gb[u];
-            b.egs[4 * tid + u] = __expf(r.gb[u]);
-        }
-    } else if (tid < 32) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) b.bs[4 * (tid - 16) + u] = r.gb[u];
-    }
+// A fragment of a 16-row block from a swizzled fp16 tile: row `row`, k-step
+// columns 32*ks + 4G + j (j < 4) and 32*ks + 16 + 4G + (j - 4).
+__device__ __forceinline__ f16x8 afragK(const char* base, int row, int ks, int G) {
+    const int c0 = 32 * ks + 4 * G;
+    return cat(*reinterpret_cast<const f16x4*>(base + offK(row, c0)),
+               *reinterpret_cast<const f16x4*>(base + offK(row, c0 + 16)));
 }
-
-// A fragment of a 16-row block: row `row`, k-step covering columns [32*ks, 32*ks+32),
-// slots j<4 -> column 32ks + 4G + j, slots j>=4 -> 32ks + 16 + 4G + (j-4).
-__device__ __forceinline__ f16x8 afrag(const f16* base, int stride, int row, int ks, int G) {
-    const f16* p = base + row * stride + 32 * ks + 4 * G;
-    return cat(*reinterpret_cast<const f16x4*>(p), *reinterpret_cast<const f16x4*>(p + 16));
+__device__ __forceinline__ f16x8 afragT(const char* base, int row, int ks, int G) {
+    const int c0 = 32 * ks + 4 * G;
+    return cat(*reinterpret_cast<const f16x4*>(base + offT(row, c0)),
+               *reinterpret_cast<const f16x4*>(base + offT(row, c0 + 16)));
+}
+// K^T fragment for d-block kb, k-step kt (tokens 32kt + 4G + j, + 16) by two
+// transposed reads: source lane 4j + a addresses token row 32kt + 4G + j,
+// columns 16kb + 4a .. +3; lane 4a + b receives column b of rows j = 0..3.
+__device__ __forceinline__ f16x8 afragKt(const char* Kbase, int kb, int kt, int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int G = lane >> 4, s = lane & 15, j = s >> 2, a = s & 3;
+    const int t0 = 32 * kt + 4 * G + j;
+    const int col = 16 * kb + 4 * a;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Kbase + offK(t0, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Kbase + offK(t0 + 16, col)));
+    return cat(__builtin_bit_cast(f16x4, lo), __builtin_bit_cast(f16x4, hi));
 }
 
 // B fragment from two 16x16 accumulator tiles (rows 32ks..+15 and 32ks+16..+31).
@@ -273,18 +260,20 @@ __device__ __forceinline__ f16x8 bfrag(const f32x4& lo, const f32x4& hi) {
     return b;
 }
 
+template <bool OUT_F32>
 __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    ScanBuf* buf = reinterpret_cast<ScanBuf*>(smem);
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int BH = g.BH;
     const int b = blockIdx.x;
     int bh, tile;
     if ((BH & 7) == 0) { bh = (b & 7) + 8 * (b >> 4); tile = (b >> 3) & 1; }   // both tiles of a head on one XCD
     else { bh = b >> 1; tile = b & 1; }
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 15, G = lane >> 4;
-    const int col = tile * 64 + wave * 16 + m;
+    const int colw = wave * 16 + m;             // column inside the workgroup's 64-column tile
+    const int col = tile * 64 + colw;
     const long long nch = (g.L + kC - 1) / kC;
 
     float* st = g.state + (long long)bh * kD * kD;
@@ -294,46 +283,63 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) Mr[kb][i] = st[(16 * kb + 4 * G + i) * kD + col];
 
-    const bf16* vbh = static_cast<const bf16*>(g.v) + (long long)bh * g.L * kD;
-    auto load_v = [&](long long c, bf16 (&vv)[16]) {
-        const long long t0 = c * kC;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const long long t = t0 + 16 * rb + 4 * G + i;
-                vv[4 * rb + i] = t < g.L ? vbh[t * kD + col] : (bf16)0.f;
-            }
-    };
-
-    StageRegs sr;
-    bf16 vc[16], vn[16];
-    stage_load(sr, g, bh, 0, tid);
-    stage_store(sr, buf[0], tid);
-    load_v(0, vc);
-    __syncthreads();
+    issue_chunk(smem, g, bh, tile, 0, nch, wave, lane);
 
     const float scale = g.scale;
     for (long long c = 0; c < nch; ++c) {
-        const ScanBuf& B = buf[c & 1];
-        const bool more = c + 1 < nch;
-        if (more) {
-            stage_load(sr, g, bh, c + 1, tid);
-            load_v(c + 1, vn);
-        }
-        // K M0 and Q M0
+        wait_vmcnt0();
+        __syncthreads();   // chunk c landed for every wave; the other stage is free
+        if (c + 1 < nch) issue_chunk(smem + ((c + 1) & 1) * kStageBytes, g, bh, tile, c + 1, nch, wave, lane);
+        const char* S = smem + (c & 1) * kStageBytes;
+        const float* esm = reinterpret_cast<const float*>(S + kOffE);
+        const float* dsm = reinterpret_cast<const float*>(S + kOffD);
+        const float* bsm = reinterpret_cast<const float*>(S + kOffB);
+
+        // K M0 and Q M0 (fragments of the critical path read ahead of their use)
+        f16x8 kf[4][4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kf[rb][ks] = afragK(S + kOffK, 16 * rb + m, ks, G);
         f16x8 bM[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) bM[ks] = bfrag(Mr[2 * ks], Mr[2 * ks + 1]);
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
         f32x4 KM[4], QM[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
+            KM[rb] = zero4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { KM[rb][i] = 0.f; QM[rb][i] = 0.f; }
+            for (int ks = 0; ks < 4; ++ks) KM[rb] = mfma16h(kf[rb][ks], bM[ks], KM[rb]);
+        }
+        f16x8 tf[4][2];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                KM[rb] = mfma16h(afrag(B.Ks, kQP, 16 * rb + m, ks, G), bM[ks], KM[rb]);
-                QM[rb] = mfma16h(afrag(B.Qs, kQP, 16 * rb + m, ks, G), bM[ks], QM[rb]);
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                if (kt == 0 || rb >= 2) tf[rb][kt] = afragT(S + kOffT, 16 * rb + m, kt, G);
+        // Per-token factors of this lane's rows 16rb + 4G + i, four at a time.
+        f32x4 e4[4], d4[4], b4[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            e4[rb] = *reinterpret_cast<const f32x4*>(esm + 16 * rb + 4 * G);
+            d4[rb] = *reinterpret_cast<const f32x4*>(dsm + 16 * rb + 4 * G);
+            b4[rb] = *reinterpret_cast<const f32x4*>(bsm + 16 * rb + 4 * G);
+        }
+        // V[16rb + 4G + i][colw], i = 0..3, by one transposed read per row block:
+        // source lane 4j + a addresses token 16rb + 4G + j, columns 16w + 4a .. +3.
+        bf16x4 v4[4];
+        {
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            const int j = m >> 2, a = m & 3;
+            const int vc = 16 * wave + 4 * a;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                const int t = 16 * rb + 4 * G + j;
+                const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(
+                    S + kOffV + t * 128 + 16 * ((vc >> 3) ^ swzv(t)) + 2 * (vc & 7)));
+                v4[rb] = __builtin_bit_cast(bf16x4, r);
             }
         }
         // X = diag(beta) (V - diag(e^g) K M0)
@@ -341,68 +347,65 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * rb + 4 * G + i;
-                X[rb][i] = B.bs[t] * (bf2f(vc[4 * rb + i]) - B.egs[t] * KM[rb][i]);
-            }
-        f16x8 xb[2] = {bfrag(X[0], X[1]), bfrag(X[2], X[3])};
+            for (int i = 0; i < 4; ++i)
+                X[rb][i] = b4[rb][i] * (bf2f(v4[rb][i]) - e4[rb][i] * KM[rb][i]);
+        const f16x8 xb[2] = {bfrag(X[0], X[1]), bfrag(X[2], X[3])};
         // U = T X (T lower triangular: row blocks 0,1 only see k-step 0)
         f32x4 U[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) U[rb][i] = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                if (kt == 0 || rb >= 2) U[rb] = mfma16h(afrag(B.Ts, kTP, 16 * rb + m, kt, G), xb[kt], U[rb]);
+            U[rb] = mfma16h(tf[rb][0], xb[0], zero4);
+            if (rb >= 2) U[rb] = mfma16h(tf[rb][1], xb[1], U[rb]);
         }
-        const float gC = B.gs[kC - 1];
         f32x4 Us[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Us[rb][i] = U[rb][i] * __expf(gC - B.gs[16 * rb + 4 * G + i]);
-        f16x8 ub[2] = {bfrag(U[0], U[1]), bfrag(U[2], U[3])};
-        f16x8 usb[2] = {bfrag(Us[0], Us[1]), bfrag(Us[2], Us[3])};
-        // O = diag(e^g) Q M0 + Pm U
-        const long long t0 = c * kC;
+            for (int i = 0; i < 4; ++i) Us[rb][i] = U[rb][i] * d4[rb][i];
+        const f16x8 usb[2] = {bfrag(Us[0], Us[1]), bfrag(Us[2], Us[3])};
+        // M = e^{g_C} M0 + K^T diag(e^{g_C - g}) U
+        const float egC = esm[kC - 1];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            f32x4 PU;
+        for (int kb = 0; kb < 8; ++kb) {
+            const f16x8 k0 = afragKt(S + kOffK, kb, 0, lane);
+            const f16x8 k1 = afragKt(S + kOffK, kb, 1, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) PU[i] = 0.f;
+            for (int i = 0; i < 4; ++i) Mr[kb][i] *= egC;
+            Mr[kb] = mfma16h(k0, usb[0], Mr[kb]);
+            Mr[kb] = mfma16h(k1, usb[1], Mr[kb]);
+        }
+        // O = diag(e^g) Q M0 + Pm U (off the state's dependency chain)
+        if (g.o) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                if (kt == 0 || rb >= 2) PU = mfma16h(afrag(B.Ps, kTP, 16 * rb + m, kt, G), ub[kt], PU);
-            if (g.o) {
+            for (int rb = 0; rb < 4; ++rb) {
+                QM[rb] = zero4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * rb + 4 * G + i;
-                    if (t0 + t < g.L) {
-                        const float ov = scale * (B.egs[t] * QM[rb][i] + PU[i]);
-                        const long long oi = ((long long)bh * g.L + t0 + t) * kD + col;
-                        if (g.out_f32) static_cast<float*>(g.o)[oi] = ov;
-                        else static_cast<bf16*>(g.o)[oi] = f2bf(ov);
-                    }
+                for (int ks = 0; ks < 4; ++ks)
+                    QM[rb] = mfma16h(afragK(S + kOffQ, 16 * rb + m, ks, G), bM[ks], QM[rb]);
+            }
+            const f16x8 ub[2] = {bfrag(U[0], U[1]), bfrag(U[2], U[3])};
+            const long long t0 = c * kC;
+            const bool full = t0 + kC <= g.L;
+            typedef typename std::conditional<OUT_F32, float, bf16>::type OT;
+            OT* obase = static_cast<OT*>(g.o) + ((long long)bh * g.L + t0 + 4 * G) * kD + col;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x4 PU = mfma16h(afragT(S + kOffP, 16 * rb + m, 0, G), ub[0], zero4);
+                if (rb >= 2) PU = mfma16h(afragT(S + kOffP, 16 * rb + m, 1, G), ub[1], PU);
+                OT* orow = obase + 16 * rb * kD;
+                float ov[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = scale * (e4[rb][i] * QM[rb][i] + PU[i]);
+                if (full) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) orow[i * kD] = (OT)ov[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (t0 + 16 * rb + 4 * G + i < g.L) orow[i * kD] = (OT)ov[i];
                 }
             }
         }
-        // M = e^{g_C} M0 + K^T diag(e^{g_C - g}) U
-        const float egC = __expf(gC);
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Mr[kb][i] *= egC;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                Mr[kb] = mfma16h(afrag(B.Kt, kTP, 16 * kb + m, kt, G), usb[kt], Mr[kb]);
-        }
-        if (more) {
-            stage_store(sr, buf[(c + 1) & 1], tid);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) vc[i] = vn[i];
-        }
-        __syncthreads();
     }
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
@@ -428,11 +431,15 @@ hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream) {
                        (int)nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t smem = 2 * sizeof(ScanBuf);   // > 64 KiB: raise the launch limit (current device)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gla_scan_bf16_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    const size_t smem = 2 * kStageBytes;   // > 64 KiB: raise the launch limit (current device)
+    const void* fn = g.out_f32 ? reinterpret_cast<const void*>(gla_scan_bf16_kernel<true>)
+                               : reinterpret_cast<const void*>(gla_scan_bf16_kernel<false>);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gla_scan_bf16_kernel, dim3((unsigned)(g.BH * 2)), dim3(256), smem, stream, g);
+    if (g.out_f32)
+        hipLaunchKernelGGL(gla_scan_bf16_kernel<true>, dim3((unsigned)(g.BH * 2)), dim3(256), smem, stream, g);
+    else
+        hipLaunchKernelGGL(gla_scan_bf16_kernel<false>, dim3((unsigned)(g.BH * 2)), dim3(256), smem, stream, g);
     return hipGetLastError();
 }
 
