@@ -27,9 +27,10 @@ if ROOT not in sys.path:
 METRIC = "hybrid temporal-attn fwd tokens/s at L=32760,H=16,d=128; % MFMA peak"
 PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0              # MI355X HBM3E
-ATTN_KERNEL = "win_attn_bf16_kernel<2>"
-PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+ATTN_KERNEL = "win_attn_bf16_kernel<1, 2>"   # one branch per pass, 2-stage K/V ring
+PMC_FILE = os.path.join(ROOT, "profiles", "win_attn_bf16_hybrid_fwd_B2H16L32760_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "hybrid_linear_temporal_hta_amd", "csrc", "win_attn.hip")
+ATTN_LAUNCHES = 2                   # SWA pass, then DSWA pass (adds the SWA+GLA partial)
 
 
 def attn_flops(w) -> float:
@@ -51,41 +52,128 @@ def gla_bytes(w, out_bytes=4) -> float:
 
 
 def pmc_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs,
-    valid only while the kernel source is the one they were taken on."""
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), valid only
+    while the kernel source is the one they were taken on."""
     try:
         rec = json.load(open(PMC_FILE))
         sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
         if rec.get("source_sha256") != sha:
             return None
         return float(rec["hbm_bytes_per_launch"])
-    except Exception:
+    except (OSError, ValueError, KeyError):
         return None
 
 
-def cpu_baseline(w, x):
-    """The fp64 oracle, untuned, on a bounded sample: one (batch, head) slice of
-    the workload -- SWA + DSWA for all its L query rows and the GLA recurrence
-    over its L tokens. That slice is 1/H of the per-token work of L tokens."""
+def copy_calibration(steps: int):
+    """A plain copy of known size for counter calibration: hta_stream_init
+    filling a 13-frame ring from 13 frames of K and of V (B2 H16 P1560 d128
+    bf16), one copy_frames_kernel launch per frame and tensor, each reading and
+    writing B*H*P*d*2 bytes."""
+    import torch
+    from hybrid_linear_temporal_hta_amd import hta
+    from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS
+    w = WORKLOADS["hybrid_stream"]
+    dev = torch.device("cuda:0")
+    k = torch.randn(w.B, w.H, w.ring * w.P, w.dk, device=dev).to(w.dtype)
+    v = torch.randn(w.B, w.H, w.ring * w.P, w.dv, device=dev).to(w.dtype)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    st = hta.Stream(w.B, w.H, w.P, w.dk, w.dtype, prm, w.ring, device=dev)
+    for _ in range(steps):
+        hta.hta_stream_init(st, k, v, w.ring, None)
+    torch.cuda.synchronize()
+    nbytes = w.B * w.H * w.P * w.dk * 2
+    print(json.dumps({"copy_kernel": "copy_frames_kernel", "launches": 2 * w.ring * steps,
+                      "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes}))
+
+
+def cpu_baseline(w, x, heads: int):
+    """The fp64 oracle, untuned, on a bounded sample: `heads` heads of batch 0
+    -- SWA + DSWA for all their L query rows and the GLA recurrence over their
+    L tokens. A token of the metric carries H heads, so the sample is worth
+    L * heads / H tokens."""
     import numpy as np
     import oracle
-    q = x["q"][0:1, 0:1].double().cpu().numpy()
-    k = x["k"][0:1, 0:1].double().cpu().numpy()
-    v = x["v"][0:1, 0:1].double().cpu().numpy()
-    a = x["alpha"][0:1, 0:1].double().cpu().numpy()
-    b = x["beta"][0:1, 0:1].double().cpu().numpy()
-    rows = np.arange(w.L, dtype=np.int64)
+    sl = (slice(0, 1), slice(0, heads))
+    q = x["q"][sl].double().cpu().numpy()
+    k = x["k"][sl].double().cpu().numpy()
+    v = x["v"][sl].double().cpu().numpy()
+    a = x["alpha"][sl].double().cpu().numpy()
+    b = x["beta"][sl].double().cpu().numpy()
     t0 = time.perf_counter()
-    oracle.swa_rows(q, k, v, w.T, w.P, w.window, rows)
-    oracle.dswa_rows(q, k, v, w.T, w.P, w.taps, w.dilation, rows)
+    oracle.swa(q, k, v, w.T, w.P, w.window)
+    oracle.dswa(q, k, v, w.T, w.P, w.taps, w.dilation)
     oracle.gla(q, k, v, a, b)
     dt = time.perf_counter() - t0
-    tokens = w.L / w.H
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+    tokens = w.L * heads / w.H
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"one (batch, head) slice: SWA+DSWA for all {w.L} query rows and the GLA "
-                      f"recurrence over {w.L} tokens (= {tokens:.1f} tokens x {w.H} heads), "
-                      f"{dt:.1f} s wall"}
+            "sample": f"{heads} of {w.H} heads of batch 0: SWA + DSWA for all {w.L} query rows "
+                      f"and the GLA recurrence over all {w.L} tokens of each head "
+                      f"(= {tokens:.0f} tokens of {w.H} heads), {dt:.1f} s wall"}
+
+
+def hybrid_step_fn(hta, w, x, state, o, ws, prm, stream):
+    """One hybrid forward: GLA into o, then SWA and DSWA adding onto o."""
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, o, w.P, w.chunk,
+                        0.0, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        hta.hta_swa_dswa_fwd(x["q"], x["k"], x["v"], o, w.P, prm, add=o, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+    return step
+
+
+def setup(hta, w, x, dev):
+    import torch
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    state = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
+    o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device=dev)
+    nws = hta.hta_workspace_bytes(hta.HTA_OP_GLA, hta.make_shape(x["q"], x["v"], w.P, o), prm)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    return prm, state, o, ws
+
+
+def timed(step, steps, warmup):
+    """Wall time and per-phase HIP-event times (ms) of `steps` calls after `warmup`."""
+    import torch
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gla_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return wall * 1e3 / steps, gla_ms, attn_ms
+
+
+def long_horizon(hta, dev, steps):
+    """The 336-frame workload (B1 H16, L=524160): tokens/s and attention FLOP/s,
+    to set beside the 21-frame figures (flatness in L)."""
+    import torch
+    from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["long_horizon"]
+    x = make_inputs(w, device=dev)
+    prm, state, o, ws = setup(hta, w, x, dev)
+    step = hybrid_step_fn(hta, w, x, state, o, ws, prm, torch.cuda.current_stream())
+    ms, gla_ms, attn_ms = timed(step, steps, 1)
+    fl = attn_flops(w)
+    res = {"workload": "B1 H16 T336 P1560 d128 (L=524160)", "steps": steps,
+           "ms_per_step": round(ms, 3), "tokens_per_s": round(w.B * w.L / (ms / 1e3), 1),
+           "attn_ms": round(attn_ms, 3), "gla_ms": round(gla_ms, 3),
+           "attn_tflops": round(fl / (attn_ms / 1e3) / 1e12, 1),
+           "attn_tap_frames_per_token": round(fl / (4.0 * w.dk * w.P * w.B * w.H * w.L), 3)}
+    del x, o, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -94,12 +182,19 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--stream-steps", type=int, default=64)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--long-horizon-steps", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads of batch 0 the CPU oracle baseline runs (0: skip it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="CALLS",
+                    help="only run CALLS ring fills (copy kernel of known size) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
     from hybrid_linear_temporal_hta_amd import hta
@@ -112,45 +207,22 @@ def main():
     nP = w.T * w.P
     x = {k: (t[:, :, :nP].contiguous() if k in ("q", "k", "v", "alpha", "beta") else t)
          for k, t in full.items()}
-    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
-    state = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
-    o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device=dev)
-    ws = torch.empty(max(hta.hta_workspace_bytes(hta.HTA_OP_GLA, hta.make_shape(x["q"], x["v"], w.P, o),
-                                                 prm), 1), dtype=torch.uint8, device=dev)
+    prm, state, o, ws = setup(hta, w, x, dev)
     stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, o, w.P, w.chunk,
-                        0.0, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        hta.hta_swa_dswa_fwd(x["q"], x["k"], x["v"], o, w.P, prm, add=o, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gla_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    step = hybrid_step_fn(hta, w, x, state, o, ws, prm, stream)
+    ms_per_step, gla_ms, attn_ms = timed(step, args.steps, args.warmup)
     tokens = w.B * w.L
     value = tokens / (ms_per_step / 1e3)
 
     fl = attn_flops(w)
-    achieved = fl / (attn_ms / 1e3) / 1e12
+    launch_ms = attn_ms / ATTN_LAUNCHES
+    fl_launch = fl / ATTN_LAUNCHES       # SWA and DSWA have equal tap-frame counts here
+    achieved = fl_launch / (launch_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
                 "traffic": pmc_traffic(), "kernel": ATTN_KERNEL,
-                "flop_per_launch": fl, "avg_launch_ms": round(attn_ms, 4)}
+                "launches_per_step": ATTN_LAUNCHES, "flop_per_launch": fl_launch,
+                "avg_launch_ms": round(launch_ms, 4)}
     gb = gla_bytes(w)
     gla = {"kernels": "gla_prep_bf16_kernel + gla_scan_bf16_kernel", "avg_ms": round(gla_ms, 4),
            "algorithmic_bytes": gb, "achieved_GBps": round(gb / (gla_ms / 1e3) / 1e9, 1),
@@ -187,8 +259,12 @@ def main():
                 "commit_only_ms_per_step": round(commit_ms, 4),
                 "commit_only_algorithmic_bytes": commit_bytes,
                 "commit_only_frac_hbm": round(commit_bytes / (commit_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del frames, st
+    del full
+    torch.cuda.empty_cache()
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, x)
+    lh = long_horizon(hta, dev, args.long_horizon_steps) if args.long_horizon_steps > 0 else None
+    cpu = cpu_baseline(w, x, args.cpu_heads) if args.cpu_heads > 0 else None
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -198,7 +274,8 @@ def main():
                                   "SWA W=3, DSWA 4 taps dil 4, GLA chunk 64",
                       "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.dk,
                       "parallelism": "single GPU"},
-           "roofline": roofline, "gla": gla, "stream": sres, "cpu_baseline": cpu}
+           "roofline": roofline, "gla": gla, "stream": sres, "long_horizon": lh,
+           "cpu_baseline": cpu}
     print(json.dumps(out))
 
 

@@ -1,0 +1,160 @@
+"""Summaries of rocprofv3 CSV output for the HTA kernels.
+
+Two subcommands, both reading what ``rocprofv3 --output-format csv`` writes:
+
+  stats    per-kernel call count and durations from ``*_kernel_stats.csv``,
+           written as a short text table with the command that produced it.
+  traffic  HBM bytes per dispatch of one kernel from two ``--pmc`` runs
+           (``FETCH_SIZE``, then ``WRITE_SIZE``; KiB per dispatch), each scaled
+           by the same counter's reading on a plain copy kernel whose bytes are
+           known (``copy_frames_kernel`` under ``bench.py --copy-calibration``).
+           The result is JSON keyed to the sha256 of the kernel's source file,
+           so a reader can tell when the kernel changed after the counters
+           were taken.
+
+Usage:
+  python -m hybrid_linear_temporal_hta_amd.profiling stats CSV --out FILE --command CMD
+  python -m hybrid_linear_temporal_hta_amd.profiling traffic --kernel SUBSTR \\
+      --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N \\
+      --source FILE --out FILE --command CMD
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+COPY_KERNEL = "copy_frames_kernel"
+
+
+def _short(name: str) -> str:
+    """Kernel name without argument lists of templated host types."""
+    name = re.sub(r"\(anonymous namespace\)::", "", name)
+    name = re.sub(r"^void ", "", name)
+    i = name.find("(")
+    return name[:i] if i > 0 else name
+
+
+def _find(path: str, suffix: str) -> str:
+    if os.path.isfile(path):
+        return path
+    hits = sorted(glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {path}")
+    return hits[0]
+
+
+def kernel_stats(path: str):
+    rows = []
+    with open(_find(path, "kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append({"kernel": _short(r["Name"]), "calls": int(r["Calls"]),
+                         "total_ns": float(r["TotalDurationNs"]), "avg_ns": float(r["AverageNs"]),
+                         "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]),
+                         "pct": float(r["Percentage"])})
+    rows.sort(key=lambda r: -r["total_ns"])
+    return rows
+
+
+def trace_by_grid(path: str, prefix: str = "hta::"):
+    """Durations from ``*_kernel_trace.csv`` grouped by (kernel, grid size), so
+    launches of one kernel on different workloads are told apart."""
+    groups = {}
+    with open(_find(path, "kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            name = _short(r["Kernel_Name"])
+            if not name.startswith(prefix):
+                continue
+            key = (name, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
+            groups.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = []
+    for (name, wgs), d in groups.items():
+        out.append({"kernel": name, "workgroups": wgs, "calls": len(d),
+                    "avg_us": sum(d) / len(d), "min_us": min(d), "max_us": max(d)})
+    out.sort(key=lambda r: -r["avg_us"] * r["calls"])
+    return out
+
+
+def counter_per_dispatch(path: str, counter: str, kernel: str):
+    """Mean over dispatches of `kernel` (substring) of one counter's value, and
+    the dispatch count. Values of one dispatch spread over several rows (one per
+    counter dimension) are summed first."""
+    per = {}
+    with open(_find(path, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or kernel not in r["Kernel_Name"]:
+                continue
+            d = r["Dispatch_Id"]
+            per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} rows for kernel {kernel!r} in {path}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.csv)
+    lines = [f"# rocprofv3 kernel statistics: {a.title}", "", "Command:", "", "    " + a.command, "",
+             f"{'kernel':<58} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+    for r in rows[:a.top]:
+        lines.append(f"{r['kernel'][:58]:<58} {r['calls']:>6} {r['avg_ns'] / 1e3:>10.1f} "
+                     f"{r['min_ns'] / 1e3:>10.1f} {r['max_ns'] / 1e3:>10.1f} {r['pct']:>6.2f}")
+    lines += ["", "Library kernels by launch shape (from the kernel trace):", "",
+              f"{'kernel':<46} {'workgroups':>10} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"]
+    for r in trace_by_grid(a.csv):
+        lines.append(f"{r['kernel'][:46]:<46} {r['workgroups']:>10} {r['calls']:>6} "
+                     f"{r['avg_us']:>10.1f} {r['min_us']:>10.1f} {r['max_us']:>10.1f}")
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    sys.stdout.write(text)
+
+
+def cmd_traffic(a):
+    cf, ncf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
+    cw, ncw = counter_per_dispatch(a.copy_write, "WRITE_SIZE", COPY_KERNEL)
+    kf, nkf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
+    kw, nkw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    # the copy kernel reads and writes copy_bytes each: bytes per counted KiB
+    f_fetch = a.copy_bytes / cf
+    f_write = a.copy_bytes / cw
+    rec = {"kernel": a.kernel, "source": os.path.relpath(a.source, os.path.dirname(a.out) + "/.."),
+           "source_sha256": hashlib.sha256(open(a.source, "rb").read()).hexdigest(),
+           "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+           "dispatches": [nkf, nkw],
+           "copy_kernel": COPY_KERNEL, "copy_bytes_per_dispatch": a.copy_bytes,
+           "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_dispatches": [ncf, ncw],
+           "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write,
+           "hbm_read_bytes_per_launch": kf * f_fetch, "hbm_write_bytes_per_launch": kw * f_write,
+           "hbm_bytes_per_launch": kf * f_fetch + kw * f_write,
+           "command": a.command}
+    with open(a.out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m hybrid_linear_temporal_hta_amd.profiling")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--out", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="")
+    s.add_argument("--top", type=int, default=12)
+    t = sub.add_parser("traffic")
+    for k in ("kernel", "fetch", "write", "copy_fetch", "copy_write", "source", "out", "command"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", dest="copy_bytes", type=float, required=True)
+    a = ap.parse_args(argv)
+    (cmd_stats if a.cmd == "stats" else cmd_traffic)(a)
+
+
+if __name__ == "__main__":
+    main()
