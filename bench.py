@@ -13,7 +13,6 @@ GPU (sharding is described in the design notes, not measured).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -56,9 +55,9 @@ def pmc_traffic():
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), valid only
     while the kernel source is the one they were taken on."""
     try:
+        from hybrid_linear_temporal_hta_amd.profiling import source_digest
         rec = json.load(open(PMC_FILE))
-        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != sha:
+        if rec.get("source_digest") != source_digest(ATTN_SRC):
             return None
         return float(rec["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):

@@ -21,8 +21,9 @@
 //   prep (one workgroup per chunk, all chunks in parallel): g, A and Pm from
 //     K K^T and Q K^T on v_mfma_f32_32x32x16_bf16, T by a register-resident
 //     forward substitution in fp32, and the chunk's operand block -- K, Q (fp16),
-//     T, Pm (fp16), g, beta (fp32) -- written contiguously in exactly the LDS
-//     layout the scan consumes (bank-conflict-free swizzles included).
+//     T, Pm (fp16), e^{g}, e^{g_C - g}, beta (fp32) -- written contiguously in
+//     exactly the LDS layout the scan consumes (bank-conflict-free swizzles
+//     included).
 //   scan (one workgroup per (batch, head, 64 value columns), chunks in order):
 //     each wave owns 16 value columns of the fp32 state as eight 16x16 MFMA
 //     accumulator tiles. K M0, Q M0, T X, Pm U and K^T U run on

@@ -16,12 +16,15 @@
 //   * O^T += V^T P^T reuses the logits' register layout directly as the B
 //     fragment (key order permuted consistently in both operands), so P never
 //     goes through LDS;
-//   * key/value tiles of 64 keys are staged through LDS, double buffered; V is
-//     transposed in registers on the way in so that A fragments of V^T are two
-//     8-byte LDS reads;
-//   * both branches in one pass: the query's own frame (offset 0, common to
-//     SWA and DSWA) is processed once and its partial softmax state seeds the
-//     second branch, saving one of the seven tap frames of an interior query;
+//   * key/value tiles of 64 keys stream into a two-stage LDS ring with direct
+//     global->LDS loads (16 bytes per lane, no register round trip), issued
+//     one tile ahead; A fragments of V^T are transposed LDS reads
+//     (ds_read_b64_tr_b16) of the row-major V tile;
+//   * one branch per launch by default: the SWA pass writes its fp32 partial
+//     (plus the optional added partial), the DSWA pass adds onto it. A fused
+//     two-branch variant (the query's own frame, common to both, processed
+//     once and its softmax state seeding the second branch) exists but needs
+//     more registers, which halves occupancy; the split passes run faster;
 //   * running max is updated lazily (only when a logit exceeds it by more than
 //     8 in log2 units), so the O rescale is rare; exp2 with the log2(e) scale
 //     folded into one FMA;

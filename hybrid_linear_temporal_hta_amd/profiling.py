@@ -8,9 +8,9 @@ Two subcommands, both reading what ``rocprofv3 --output-format csv`` writes:
            (``FETCH_SIZE``, then ``WRITE_SIZE``; KiB per dispatch), each scaled
            by the same counter's reading on a plain copy kernel whose bytes are
            known (``copy_frames_kernel`` under ``bench.py --copy-calibration``).
-           The result is JSON keyed to the sha256 of the kernel's source file,
-           so a reader can tell when the kernel changed after the counters
-           were taken.
+           The result is JSON keyed to a digest of the kernel's source file
+           (comments excluded), so a reader can tell when the kernel changed
+           after the counters were taken.
 
 Usage:
   python -m hybrid_linear_temporal_hta_amd.profiling stats CSV --out FILE --command CMD
@@ -30,6 +30,16 @@ import re
 import sys
 
 COPY_KERNEL = "copy_frames_kernel"
+
+
+def source_digest(path: str) -> str:
+    """sha256 of a C/C++/HIP source with comments and blank lines removed, so
+    that documentation edits do not mark counter figures as stale."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def _short(name: str) -> str:
@@ -124,7 +134,7 @@ def cmd_traffic(a):
     f_fetch = a.copy_bytes / cf
     f_write = a.copy_bytes / cw
     rec = {"kernel": a.kernel, "source": os.path.relpath(a.source, os.path.dirname(a.out) + "/.."),
-           "source_sha256": hashlib.sha256(open(a.source, "rb").read()).hexdigest(),
+           "source_digest": source_digest(a.source),
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
            "dispatches": [nkf, nkw],
            "copy_kernel": COPY_KERNEL, "copy_bytes_per_dispatch": a.copy_bytes,
