@@ -35,6 +35,8 @@
 //     the fp32 sum, or rounds it once to bf16.
 // fp32 kernel (d = 64 or 128): a plain per-row online softmax on the vector
 // ALU (4 lanes per query row); used for fp32 inputs, whose workloads are tiny.
+#include <type_traits>
+
 #include "device_common.h"
 #include "hta_internal.h"
 
@@ -48,10 +50,6 @@ constexpr int kBK = 64;          // keys per LDS tile
 constexpr int kRowB = kD * 2;    // bytes per K / V row in LDS (unpadded, chunk-swizzled)
 constexpr int kTileB = kBK * kRowB;
 constexpr float kLazyLog2 = 8.0f;
-#ifndef HTA_ATTN_STAGES
-#define HTA_ATTN_STAGES 2
-#endif
-constexpr int kStages = HTA_ATTN_STAGES;   // LDS ring depth of K/V tiles
 
 // 16-byte chunk c of LDS row r lives in slot c ^ swz(r): conflict-free for both
 // the K fragment reads (32 rows x one chunk) and the transposed V reads.
@@ -94,56 +92,105 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// One global_load_lds_dwordx4: 16 bytes from gptr (per lane) into LDS at
-// lds_base + 16 * lane (lds_base wave-uniform). Written as asm so that the
-// compiler does not serialise it against the LDS reads of other stages (it
-// cannot tell the buffers apart); completion is tracked by wait_vmcnt. It has
-// no register outputs.
-__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
-    typedef __attribute__((address_space(3))) const char lds_char;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// One global_load_lds_dwordx4: 16 bytes from sbase + voff (sbase wave-uniform,
+// voff per lane) into LDS at lds + 16 * lane (lds wave-uniform). Written as asm
+// so that the compiler does not serialise it against the LDS reads of the other
+// stage (it cannot tell the buffers apart); completion is tracked by wait_vmcnt.
+// It has no register outputs.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds), "v"(gptr)
+                 : "s"(lds), "v"(voff), "s"(sbase)
                  : "m0");
 }
 
-// Enqueue one 64-key tile of K and V straight into LDS (global_load_lds_dwordx4):
-// wave w, instruction i writes LDS chunks [64 (4w + i), +64) of each tile, lane l
-// chunk 64 (4w + i) + l = row r, slot c ^ swz(r). Rows past the frame's end
-// re-read the last valid row (finite values; their logits are masked).
-__device__ __forceinline__ void issue_tile(char* ks, char* vs, const bf16* kbase,
-                                           const bf16* vbase, int nvalid, int wave, int lane) {
+// Per-lane byte offsets that stay fixed for the whole kernel.
+struct LaneOffs {
+    uint32_t k[8];     // K fragment ks of key row n (32-key block 0, stage 0)
+    uint32_t v[4];     // V^T fragment of d-block db, rows 4(g/2) + j (block 0, stage 0)
+    uint32_t dma[4];   // source offset within a tile of DMA instruction i (row r, slot c)
+    int dma_row[4];    // ... and its row, for the clamped copy of a ragged tile
+    int dma_col[4];    // ... and its column
+};
+
+__device__ __forceinline__ void lane_offsets(LaneOffs& L, int wave, int lane) {
+    const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) L.k[ks] = n * kRowB + 16 * ((2 * ks + h) ^ swz(n));
+    // V^T fragments by transposed LDS reads: within each 16-lane group g, lane
+    // 4j + a addresses row (key) 4(g/2) + j (+8, +16 gg, +32 kb: immediates),
+    // columns 16(g%2) + 4a .. +3 of the d-block; the read hands lane 4a + b
+    // column b of rows j = 0..3. swz of those rows depends only on the lane.
+    const int g = lane >> 4, sl = lane & 15, jr = sl >> 2, ac = sl & 3;
+    const int r0 = 4 * (g >> 1) + jr;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int col = 32 * db + 16 * (g & 1) + 4 * ac;
+        L.v[db] = r0 * kRowB + 16 * ((col >> 3) ^ swz(r0)) + 8 * ((col >> 2) & 1);
+    }
+    // DMA: wave w, instruction i fills LDS chunks [64 (4w + i), +64) of a tile;
+    // lane l fills chunk 64 (4w + i) + l = row r, slot c ^ swz(r).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = 64 * (4 * wave + i) + lane;
         const int r = p >> 4;
         const int c = (p & 15) ^ swz(r);
-        const long long off = (long long)min(r, nvalid - 1) * kD + c * 8;
-        dma16(kbase + off, ks + 1024 * (4 * wave + i));
-        dma16(vbase + off, vs + 1024 * (4 * wave + i));
+        L.dma_row[i] = r;
+        L.dma_col[i] = c * 8;
+        L.dma[i] = (uint32_t)(r * kD + c * 8) * 2;
+    }
+}
+
+// Enqueue one 64-key tile of K and V straight into LDS stage `st`. Rows past the
+// frame's end (ragged tile) re-read the last valid row: finite values, masked logits.
+__device__ __forceinline__ void issue_tile(uint32_t ldsK, uint32_t ldsV, const bf16* kb,
+                                           const bf16* vb, int nvalid, int wave,
+                                           const LaneOffs& L) {
+    if (nvalid == kBK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = 1024u * (4 * wave + i);
+            dma16(L.dma[i], kb, ldsK + off);
+            dma16(L.dma[i], vb, ldsV + off);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = 1024u * (4 * wave + i);
+            const uint32_t src = (uint32_t)(min(L.dma_row[i], nvalid - 1) * kD + L.dma_col[i]) * 2;
+            dma16(src, kb, ldsK + off);
+            dma16(src, vb, ldsV + off);
+        }
     }
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, lazy online softmax, O^T += V^T P^T.
+// Ks / Vs are the tile's LDS stage (compile-time addresses once inlined, so the
+// per-lane offsets plus immediates address every fragment). RAGGED: the tile
+// holds nvalid < 64 keys (the last tile of a frame).
+template <bool RAGGED>
 __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const char* Ks,
-                                            const char* Vs, int nvalid, float c, int lane) {
-    const int n = lane & 31, h = lane >> 5;
-    const bool two = nvalid > 32;   // second 32-key block has valid keys
+                                            const char* Vs, const LaneOffs& L, int nvalid,
+                                            float c, int lane) {
+    const int h = lane >> 5;
+    const bool two = !RAGGED || nvalid > 32;   // second 32-key block has valid keys
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+        if (RAGGED && kb == 1 && !two) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = kb == 0 || two ? 0.f : -INFINITY;
-        if (kb == 1 && !two) continue;
-        const int r = kb * 32 + n;
+            for (int i = 0; i < 16; ++i) s[1][i] = -INFINITY;
+            continue;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + r * kRowB + 16 * ((2 * ks + h) ^ swz(r)));
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * kRowB + L.k[ks]);
             s[kb] = mfma32(kf, qf[ks], s[kb]);
         }
     }
-    if (nvalid < kBK) {
+    if (RAGGED) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -185,38 +232,38 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
                 lsum = add_pair(bf16x2{pf[kb][gg][j], pf[kb][gg][j + 1]}, lsum);
         }
     a.l += lsum;
-    // V^T fragments by transposed LDS reads: within each 16-lane group g, lane
-    // 4j + a addresses row (key) base + 4(g/2) + j, columns 16(g%2) + 4a .. +3 of
-    // the d-block; the read hands lane 4a + b column b of rows j = 0..3.
-    const int g = lane >> 4, sl = lane & 15, jr = sl >> 2, ac = sl & 3;
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        const int col = 32 * db + 16 * (g & 1) + 4 * ac;
-        const int c16 = col >> 3, half = (col >> 2) & 1;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int gg = 0; gg < 2; ++gg) {
-                if (kb == 1 && !two) continue;
-                const int r0 = kb * 32 + 16 * gg + 4 * (g >> 1) + jr;
-                const int r1 = r0 + 8;
-                typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(Vs + r0 * kRowB + 16 * (c16 ^ swz(r0)) + 8 * half));
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4*)(Vs + r1 * kRowB + 16 * (c16 ^ swz(r1)) + 8 * half));
+                if (RAGGED && kb == 1 && !two) continue;
+                const char* vr = Vs + (kb * 32 + 16 * gg) * kRowB + L.v[db];
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vr);
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vr + 8 * kRowB));
                 a.o[db] = mfma32(cat(lo, hi), pf[kb][gg], a.o[db]);
             }
-    }
 }
+
+// Walks the tiles of a workgroup in order: segment (tap frame) sg, tile tk.
+struct TileCursor {
+    int sg, tk;
+    const bf16* kf;   // K / V of the current segment's frame
+    const bf16* vf;
+};
 
 // Two waves per SIMD for the single-branch kernel (fits 256 registers without
 // spilling); the fused two-branch kernel keeps two accumulator sets and runs at one.
-template <int NBR, int NST>
+template <int NBR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3 - NBR, 3 - NBR)))
 void win_attn_bf16_kernel(WinLaunch w) {
-    __shared__ __attribute__((aligned(1024))) char Kst[NST][kTileB];
-    __shared__ __attribute__((aligned(1024))) char Vst[NST][kTileB];
+    __shared__ __attribute__((aligned(1024))) char Kst[2][kTileB];
+    __shared__ __attribute__((aligned(1024))) char Vst[2][kTileB];
+    typedef __attribute__((address_space(3))) char lds_char;
+    const uint32_t ldsK = (uint32_t)(uintptr_t)(lds_char*)&Kst[0][0];
+    const uint32_t ldsV = (uint32_t)(uintptr_t)(lds_char*)&Vst[0][0];
 
     const int nqt = (w.P + kBQ - 1) / kBQ;
     const int nwg = w.BH * w.Tq * nqt;
@@ -226,9 +273,11 @@ void win_attn_bf16_kernel(WinLaunch w) {
     const int bh = wid / (nqt * w.Tq);
     const long long fa = w.frame0 + fq;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
+    LaneOffs L;
+    lane_offsets(L, wave, lane);
 
     const bf16* kbh = static_cast<const bf16*>(w.k) + (long long)bh * w.kv_bh;
     const bf16* vbh = static_cast<const bf16*>(w.v) + (long long)bh * w.kv_bh;
@@ -239,21 +288,28 @@ void win_attn_bf16_kernel(WinLaunch w) {
     const int ntk = (w.P + kBK - 1) / kBK;
     const int nit = nseg * ntk;
 
-    auto tile_src = [&](int it, const bf16*& kb, const bf16*& vb, int& nv) {
-        const int sg = it / ntk, tk = it - sg * ntk;
-        const long long ofs = seg_frame(w, fa, sg, nSegA) * w.kv_frame + (long long)tk * kBK * kD;
-        kb = kbh + ofs;
-        vb = vbh + ofs;
-        nv = min(kBK, w.P - tk * kBK);
+    auto seg_base = [&](TileCursor& t) {
+        const long long ofs = seg_frame(w, fa, t.sg, nSegA) * w.kv_frame;
+        t.kf = kbh + ofs;
+        t.vf = vbh + ofs;
     };
-#pragma unroll
-    for (int st = 0; st < NST - 1; ++st) {
-        if (st < nit) {
-            const bf16 *kb, *vb;
-            int nv;
-            tile_src(st, kb, vb, nv);
-            issue_tile(Kst[st], Vst[st], kb, vb, nv, wave, lane);
+    auto advance = [&](TileCursor& t) {
+        if (++t.tk == ntk) {
+            t.tk = 0;
+            if (++t.sg < nseg) seg_base(t);
         }
+    };
+    auto issue = [&](const TileCursor& t, uint32_t stage) {
+        const long long ofs = (long long)t.tk * kBK * kD;
+        issue_tile(ldsK + stage * kTileB, ldsV + stage * kTileB, t.kf + ofs, t.vf + ofs,
+                   min(kBK, w.P - t.tk * kBK), wave, L);
+    };
+
+    TileCursor ti{0, 0, kbh, vbh};   // next tile to stage
+    if (nit > 0) {
+        seg_base(ti);
+        issue(ti, 0);
+        advance(ti);
     }
 
     // Query fragments (B operand of S^T = K Q^T).
@@ -274,25 +330,28 @@ void win_attn_bf16_kernel(WinLaunch w) {
     acc_init(A);
     acc_init(Bacc);
 
-    for (int it = 0; it < nit; ++it) {
-        // tile `it` landed (its loads were issued NST-1 tiles ago) ...
-        if (NST >= 3 && it + 1 < nit) wait_vmcnt<8 * (NST >= 3 ? NST - 2 : 0)>();
-        else wait_vmcnt<0>();
-        __syncthreads();   // ... for every wave; and the buffer refilled next was read by all
-        if (it + NST - 1 < nit) {
-            const bf16 *kb, *vb;
-            int nv;
-            tile_src(it + NST - 1, kb, vb, nv);
-            issue_tile(Kst[(it + NST - 1) % NST], Vst[(it + NST - 1) % NST], kb, vb, nv, wave, lane);
+    int sg = 0, tk = 0;   // tile being consumed
+    // One tile in stage ST (compile-time, so LDS addresses fold into immediates).
+    auto step = [&](int it, auto stage_tag) {
+        constexpr int ST = decltype(stage_tag)::value;
+        wait_vmcnt<0>();   // this tile's loads (issued one tile ago) have landed ...
+        __syncthreads();   // ... for every wave; and the stage refilled next was read by all
+        if (it + 1 < nit) {
+            issue(ti, ST ^ 1);
+            advance(ti);
         }
-        const int sg = it / ntk, tk = it - sg * ntk;
         const int nvalid = min(kBK, w.P - tk * kBK);
-        const int cur = it % NST;
         if (wave_rows) {   // waves whose 32 query rows all lie past the frame only stage tiles
-            if (NBR == 1 || sg < nSegA) attend_tile(A, qf, Kst[cur], Vst[cur], nvalid, c, lane);
-            else attend_tile(Bacc, qf, Kst[cur], Vst[cur], nvalid, c, lane);
+            Acc& acc = (NBR == 1 || sg < nSegA) ? A : Bacc;
+            if (nvalid == kBK) attend_tile<false>(acc, qf, Kst[ST], Vst[ST], L, nvalid, c, lane);
+            else attend_tile<true>(acc, qf, Kst[ST], Vst[ST], L, nvalid, c, lane);
         }
         if (NBR == 2 && sg == 0 && tk == ntk - 1) Bacc = A;   // own frame seeds branch B
+        if (++tk == ntk) { tk = 0; ++sg; }
+    };
+    for (int it = 0; it < nit; it += 2) {
+        step(it, std::integral_constant<int, 0>{});
+        if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     }
 
     // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add), rounded once.
@@ -427,9 +486,9 @@ hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream) {
         const long long nwg = (long long)w.BH * w.Tq * nqt;
         if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
         if (w.nbr == 2)
-            hipLaunchKernelGGL((win_attn_bf16_kernel<2, kStages>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
+            hipLaunchKernelGGL((win_attn_bf16_kernel<2>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
         else
-            hipLaunchKernelGGL((win_attn_bf16_kernel<1, kStages>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
+            hipLaunchKernelGGL((win_attn_bf16_kernel<1>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
         return hipGetLastError();
     }
     const int nqt = (w.P + 63) / 64;
