@@ -166,22 +166,17 @@ __device__ __forceinline__ void issue_tile(uint32_t ldsK, uint32_t ldsV, const b
 
 // One 64-key tile for one wave: S^T = K Q^T, lazy online softmax, O^T += V^T P^T.
 // Ks / Vs are the tile's LDS stage (compile-time addresses once inlined, so the
-// per-lane offsets plus immediates address every fragment). RAGGED: the tile
-// holds nvalid < 64 keys (the last tile of a frame).
-template <bool RAGGED>
+// per-lane offsets plus immediates address every fragment). A ragged tile (the
+// last of a frame, nvalid < 64 keys) runs the same code with its missing keys'
+// logits set to -inf: one code path touches the accumulators, so they keep
+// their registers across iterations.
 __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const char* Ks,
                                             const char* Vs, const LaneOffs& L, int nvalid,
                                             float c, int lane) {
     const int h = lane >> 5;
-    const bool two = !RAGGED || nvalid > 32;   // second 32-key block has valid keys
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        if (RAGGED && kb == 1 && !two) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[1][i] = -INFINITY;
-            continue;
-        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
@@ -190,7 +185,7 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
             s[kb] = mfma32(kf, qf[ks], s[kb]);
         }
     }
-    if (RAGGED) {
+    if (__builtin_expect(nvalid < kBK, 0)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -239,7 +234,6 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int gg = 0; gg < 2; ++gg) {
-                if (RAGGED && kb == 1 && !two) continue;
                 const char* vr = Vs + (kb * 32 + 16 * gg) * kRowB + L.v[db];
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vr);
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vr + 8 * kRowB));
@@ -343,8 +337,7 @@ void win_attn_bf16_kernel(WinLaunch w) {
         const int nvalid = min(kBK, w.P - tk * kBK);
         if (wave_rows) {   // waves whose 32 query rows all lie past the frame only stage tiles
             Acc& acc = (NBR == 1 || sg < nSegA) ? A : Bacc;
-            if (nvalid == kBK) attend_tile<false>(acc, qf, Kst[ST], Vst[ST], L, nvalid, c, lane);
-            else attend_tile<true>(acc, qf, Kst[ST], Vst[ST], L, nvalid, c, lane);
+            attend_tile(acc, qf, Kst[ST], Vst[ST], L, nvalid, c, lane);
         }
         if (NBR == 2 && sg == 0 && tk == ntk - 1) Bacc = A;   // own frame seeds branch B
         if (++tk == ntk) { tk = 0; ++sg; }
