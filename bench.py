@@ -1,11 +1,13 @@
 """Benchmark: hybrid temporal-attention forward tokens/s on one MI355X.
 
-One step = one full hybrid forward (GLA branch, then SWA + DSWA with the GLA
-partial added in the epilogue: the two launches hta_hybrid_fwd makes) over one
-batch of the workload B=2, H=16, d=128, T=21 frames x P=1560 tokens (L=32760),
-bf16 q/k/v, fp32 accumulation and output, inputs resident in HBM. After the
-timed forward steps the 64-frame streaming continuation of the same workload
-is timed as well (reported under "stream").
+One step = one hta_hybrid_fwd call over one batch of the workload B=2, H=16,
+d=128, T=21 frames x P=1560 tokens (L=32760), bf16 q/k/v, fp32 accumulation
+and output, inputs resident in HBM. Inside the call the GLA branch runs on the
+library's auxiliary stream beside the SWA pass; the DSWA pass then adds both
+partials. The dominant kernel's roofline is timed on the same attention
+launches run alone; the GLA branch is timed alone as well. After the forward
+steps the 64-frame streaming continuation of the same workload is timed
+(reported under "stream"), then the 336-frame long-horizon workload.
 
 Prints ONE JSON line. With --gpus above 1 it exits: this build runs on a single
 GPU (sharding is described in the design notes, not measured).
@@ -112,46 +114,50 @@ def cpu_baseline(w, x, heads: int):
                       f"(= {tokens:.0f} tokens of {w.H} heads), {dt:.1f} s wall"}
 
 
-def hybrid_step_fn(hta, w, x, state, o, ws, prm, stream):
-    """One hybrid forward: GLA into o, then SWA and DSWA adding onto o."""
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, o, w.P, w.chunk,
-                        0.0, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        hta.hta_swa_dswa_fwd(x["q"], x["k"], x["v"], o, w.P, prm, add=o, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-    return step
-
-
 def setup(hta, w, x, dev):
     import torch
     prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
     state = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
     o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device=dev)
-    nws = hta.hta_workspace_bytes(hta.HTA_OP_GLA, hta.make_shape(x["q"], x["v"], w.P, o), prm)
+    nws = hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, hta.make_shape(x["q"], x["v"], w.P, o), prm)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     return prm, state, o, ws
 
 
-def timed(step, steps, warmup):
-    """Wall time and per-phase HIP-event times (ms) of `steps` calls after `warmup`."""
+def timed_wall(fn, steps, warmup):
+    """Wall time (ms) per call of `steps` calls after `warmup`, bracketed by
+    device synchronisation."""
     import torch
     for _ in range(warmup):
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i])
+    for _ in range(steps):
+        fn()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gla_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    return wall * 1e3 / steps, gla_ms, attn_ms
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def timed_events(fn, steps, warmup, stream):
+    """Mean HIP-event time (ms) of `fn` on `stream` over `steps` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+
+
+def hybrid_call(hta, w, x, state, o, ws, prm, stream):
+    """One hybrid forward through the library's entry point."""
+    return lambda: hta.hta_hybrid_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, o,
+                                      w.P, prm, workspace=ws, stream=stream)
 
 
 def long_horizon(hta, dev, steps):
@@ -162,8 +168,13 @@ def long_horizon(hta, dev, steps):
     w = WORKLOADS["long_horizon"]
     x = make_inputs(w, device=dev)
     prm, state, o, ws = setup(hta, w, x, dev)
-    step = hybrid_step_fn(hta, w, x, state, o, ws, prm, torch.cuda.current_stream())
-    ms, gla_ms, attn_ms = timed(step, steps, 1)
+    stream = torch.cuda.current_stream()
+    ms = timed_wall(hybrid_call(hta, w, x, state, o, ws, prm, stream), steps, 1)
+    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd(x["q"], x["k"], x["v"], o, w.P, prm,
+                                                        add=o, stream=stream), steps, 0, stream)
+    gla_ms = timed_events(lambda: hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                                  state, o, w.P, w.chunk, 0.0, ws, stream),
+                          steps, 0, stream)
     fl = attn_flops(w)
     res = {"workload": "B1 H16 T336 P1560 d128 (L=524160)", "steps": steps,
            "ms_per_step": round(ms, 3), "tokens_per_s": round(w.B * w.L / (ms / 1e3), 1),
@@ -208,10 +219,20 @@ def main():
          for k, t in full.items()}
     prm, state, o, ws = setup(hta, w, x, dev)
     stream = torch.cuda.current_stream()
-    step = hybrid_step_fn(hta, w, x, state, o, ws, prm, stream)
-    ms_per_step, gla_ms, attn_ms = timed(step, args.steps, args.warmup)
+    # The metric: the library's hybrid forward (GLA beside the SWA pass, then DSWA).
+    ms_per_step = timed_wall(hybrid_call(hta, w, x, state, o, ws, prm, stream), args.steps,
+                             args.warmup)
     tokens = w.B * w.L
     value = tokens / (ms_per_step / 1e3)
+    # Roofline of the dominant kernel: the same two attention launches, alone on
+    # the stream, timed with HIP events on that stream.
+    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd(x["q"], x["k"], x["v"], o, w.P, prm,
+                                                        add=o, stream=stream),
+                           args.steps, 1, stream)
+    # The GLA branch alone (prep + scan), for its own HBM fraction.
+    gla_ms = timed_events(lambda: hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                                  state, o, w.P, w.chunk, 0.0, ws, stream),
+                          args.steps, 1, stream)
 
     fl = attn_flops(w)
     launch_ms = attn_ms / ATTN_LAUNCHES

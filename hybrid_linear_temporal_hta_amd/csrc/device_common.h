@@ -78,7 +78,17 @@ __device__ __forceinline__ float add_pair(bf16x2 a, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, one, acc, false);
 }
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Combine lane l with lane l ^ 32 (the two halves of a wave) on the VALU:
+// v_permlane32_swap with both operands x returns (x[lo], x[lo]) and (x[hi], x[hi])
+// laid out so that every lane sees x of its own half and of the other half.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Round-robin dispatch puts workgroup b on XCD b % 8. Remap so that each XCD
 // walks one contiguous range of the logical work order (shared K/V stays in

@@ -422,16 +422,19 @@ size_t gla_bf16_workspace_bytes(int BH, long long L, int chunk) {
     return (size_t)BH * (size_t)nch * kChunkBytes;
 }
 
-hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream) {
+hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream, int parts) {
     if (g.BH == 0 || g.L == 0) return hipSuccess;
     if (g.d != kD || g.chunk != kC) return hipErrorInvalidValue;
     const long long nch = (g.L + kC - 1) / kC;
     if (g.ws_bytes < gla_bf16_workspace_bytes(g.BH, g.L, g.chunk)) return hipErrorInvalidValue;
     if ((long long)g.BH * nch > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gla_prep_bf16_kernel, dim3((unsigned)(g.BH * nch)), dim3(256), 0, stream, g,
-                       (int)nch);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (parts & kGlaPrep) {
+        hipLaunchKernelGGL(gla_prep_bf16_kernel, dim3((unsigned)(g.BH * nch)), dim3(256), 0, stream,
+                           g, (int)nch);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (!(parts & kGlaScan)) return hipSuccess;
     const size_t smem = 2 * kStageBytes;   // > 64 KiB: raise the launch limit (current device)
     const void* fn = g.out_f32 ? reinterpret_cast<const void*>(gla_scan_bf16_kernel<true>)
                                : reinterpret_cast<const void*>(gla_scan_bf16_kernel<false>);

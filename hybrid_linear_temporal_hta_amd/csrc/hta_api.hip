@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/hta.h"
 #include "hta_internal.h"
 
@@ -99,17 +101,58 @@ size_t out_bytes(const hta_shape* s) {
 size_t gate_bytes(const hta_shape* s) { return (size_t)s->B * s->H * (size_t)s->T * s->P * 4; }
 size_t state_bytes(const hta_shape* s) { return (size_t)s->B * s->H * s->dk * s->dv * 4; }
 
-// Workspace: [GLA scratch][fp32 partial of the GLA branch (bf16 hybrid only)].
+// Workspace: [GLA scratch][fp32 GLA partial][fp32 SWA partial (bf16 o only)].
 size_t gla_ws(const hta_shape* s, int chunk) {
     if (s->dtype == HTA_F32) return kAlign;
     const long long L = (long long)s->T * s->P;
     return align_up(hta::gla_bf16_workspace_bytes(s->B * s->H, L, chunk));
 }
-// fp32 output: the GLA branch is written straight into o and the attention
-// epilogue adds to it in place; bf16 output keeps the fp32 GLA partial here.
-size_t partial_ws(const hta_shape* s) {
-    if (s->out_dtype == HTA_F32) return 0;
+// bf16 inputs: the GLA branch runs beside the SWA pass, each into an fp32
+// partial of its own (the SWA one is o itself when o is fp32), and the DSWA
+// pass adds both. fp32 inputs (small workloads) run the branches in sequence
+// with the GLA partial in o.
+size_t fp32_seq_bytes(const hta_shape* s) {
     return align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 4);
+}
+size_t partial_ws(const hta_shape* s) {
+    if (s->dtype == HTA_F32) return 0;
+    return fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2);
+}
+
+// One auxiliary stream and two events per device, created on first use and
+// kept until the process exits: the hybrid forks its GLA branch onto the
+// auxiliary stream so that the latency-bound chunk scan (few workgroups) runs
+// beside the SWA pass. The mutex makes each fork/join sequence atomic with
+// respect to other host threads sharing the events.
+struct Aux {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mu;
+Aux g_aux[kMaxDevices];
+
+hipError_t aux_for_current_device(Aux** out) {   // g_aux_mu held
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    Aux& a = g_aux[dev];
+    if (!a.s) {
+        Aux n;
+        e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            if (n.join) (void)hipEventDestroy(n.join);
+            if (n.fork) (void)hipEventDestroy(n.fork);
+            if (n.s) (void)hipStreamDestroy(n.s);
+            return e;
+        }
+        a = n;
+    }
+    *out = &a;
+    return hipSuccess;
 }
 
 hta::WinLaunch win_base(const hta_shape* s, const void* q, const void* k, const void* v, void* o,
@@ -205,6 +248,41 @@ hta::GlaLaunch gla_base(const hta_shape* s, const void* q, const void* k, const 
 
 hipError_t run_gla(const hta::GlaLaunch& g, hipStream_t st) {
     return g.dtype == HTA_F32 ? hta::launch_gla_f32(g, st) : hta::launch_gla_bf16(g, st);
+}
+
+// bf16 hybrid: the GLA prep (chunk-parallel, the whole chip) on `sm`, then the
+// GLA scan (one workgroup per (b, h, 64 value columns), latency-bound) also on
+// `sm`, while the SWA pass (into fp32 `mid`) runs on the auxiliary stream,
+// forked from `sm` after the prep. The scan is next in its queue when the prep
+// ends, so its few workgroups take their CUs before the attention workgroups
+// (which can never share a CU with a scan workgroup: LDS) fill the chip. The
+// DSWA pass waits for the SWA pass and adds both partials, writing w.o.
+hipError_t run_hybrid_overlapped(const hta::GlaLaunch& g, const hta::WinLaunch& w, float* mid,
+                                 const hta_params* p, hipStream_t sm) {
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    Aux* a = nullptr;
+    hipError_t e = aux_for_current_device(&a);
+    if (e != hipSuccess) return e;
+    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
+    if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return e;
+    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaScan)) != hipSuccess) return e;
+    hta::WinLaunch sw = w;
+    sw.nbr = 1;
+    taps_swa(sw.taps, p->swa_window);
+    sw.o = mid;
+    sw.out_f32 = 1;
+    sw.add = nullptr;
+    sw.add2 = nullptr;
+    if ((e = hta::launch_win_attn(sw, a->s)) != hipSuccess) return e;
+    if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return e;
+    hta::WinLaunch dw = w;
+    dw.nbr = 1;
+    taps_dswa(dw.taps, p->dswa_taps, p->dswa_dilation);
+    dw.add = mid;
+    dw.add2 = static_cast<const float*>(g.o);
+    return hta::launch_win_attn(dw, sm);
 }
 
 }  // namespace
@@ -347,18 +425,27 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void*
                                 need)) != HTA_OK)
         return st;
     hipStream_t sm = static_cast<hipStream_t>(stream);
-    // 1. GLA branch -> fp32 partial (bf16 output) or straight into o (fp32 output).
-    float* partial = shape->out_dtype == HTA_BF16
-                         ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need_gla)
-                         : static_cast<float*>(o);
-    hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, partial, params->gla_chunk,
+    char* wsb = static_cast<char*>(workspace);
+    if (shape->dtype == HTA_BF16) {
+        float* gpart = reinterpret_cast<float*>(wsb + need_gla);
+        float* mid = shape->out_dtype == HTA_F32
+                         ? static_cast<float*>(o)
+                         : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(shape));
+        hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, gpart, params->gla_chunk,
+                                    params->gla_scale, workspace, need_gla);
+        g.out_f32 = 1;
+        hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
+        hipError_t e = run_hybrid_overlapped(g, w, mid, params, sm);
+        return e == hipSuccess ? HTA_OK : hip_fail(e);
+    }
+    // fp32 inputs: GLA into o, then SWA + DSWA adding it in place.
+    hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, o, params->gla_chunk,
                                 params->gla_scale, workspace, need_gla);
     g.out_f32 = 1;
     hipError_t e = run_gla(g, sm);
     if (e != hipSuccess) return hip_fail(e);
-    // 2. SWA + DSWA in one pass; the epilogue adds the GLA partial and rounds once.
     hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
-    w.add = partial;
+    w.add = static_cast<float*>(o);
     e = run_swa_dswa(w, params->swa_window, params->dswa_taps, params->dswa_dilation, sm);
     return e == hipSuccess ? HTA_OK : hip_fail(e);
 }
@@ -428,6 +515,16 @@ int hta_stream_init(hta_stream_ctx* ctx, const void* k_prefix, const void* v_pre
     return HTA_OK;
 }
 
+// The frame's queries against the ring: frame n in slot n mod R.
+static hta::WinLaunch ring_launch(const hta_stream_ctx* ctx, const hta_shape& s, const void* q,
+                                  void* o, long long n) {
+    hta::WinLaunch w = win_base(&s, q, ctx->ring_k, ctx->ring_v, o, ctx->p.attn_scale);
+    w.kv_bh = (long long)ctx->R * s.P * s.dk;
+    w.frame0 = n;
+    w.R = ctx->R;
+    return w;
+}
+
 int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, void* o, void* workspace,
                     size_t workspace_bytes, void* stream) {
@@ -464,25 +561,32 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
         e = hta::launch_copy_frames(v, ctx->ring_v, BH, fe, (long long)ctx->R * fe, 0, slot * fe,
                                     fe, elem_bytes(s.dtype), sm);
     if (e != hipSuccess) return hip_fail(e);
-    // 2. GLA over the frame's P tokens from the carried state (chunks start at the frame).
-    float* partial = nullptr;
-    if (o) partial = s.out_dtype == HTA_BF16
-                         ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need_gla)
-                         : static_cast<float*>(o);
-    hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, partial, ctx->p.gla_chunk,
-                                ctx->p.gla_scale, workspace, need_gla);
-    g.out_f32 = 1;
-    e = run_gla(g, sm);
-    if (e != hipSuccess) return hip_fail(e);
-    // 3. Attention of the frame's queries over the ring, plus the GLA partial.
-    if (o) {
-        hta::WinLaunch w = win_base(&s, q, ctx->ring_k, ctx->ring_v, o, ctx->p.attn_scale);
-        w.kv_bh = (long long)ctx->R * s.P * s.dk;
-        w.frame0 = n;
-        w.R = ctx->R;
-        w.add = partial;
-        e = run_swa_dswa(w, ctx->p.swa_window, ctx->p.dswa_taps, ctx->p.dswa_dilation, sm);
+    // 2. GLA over the frame's P tokens from the carried state (chunks start at
+    //    the frame), and 3. the frame's queries over the ring plus the GLA
+    //    partial -- the two side by side for bf16 inputs.
+    char* wsb = static_cast<char*>(workspace);
+    if (o && s.dtype == HTA_BF16) {
+        float* gpart = reinterpret_cast<float*>(wsb + need_gla);
+        float* mid = s.out_dtype == HTA_F32
+                         ? static_cast<float*>(o)
+                         : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(&s));
+        hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, gpart, ctx->p.gla_chunk,
+                                    ctx->p.gla_scale, workspace, need_gla);
+        g.out_f32 = 1;
+        e = run_hybrid_overlapped(g, ring_launch(ctx, s, q, o, n), mid, &ctx->p, sm);
         if (e != hipSuccess) return hip_fail(e);
+    } else {
+        hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, o, ctx->p.gla_chunk,
+                                    ctx->p.gla_scale, workspace, need_gla);
+        g.out_f32 = 1;
+        e = run_gla(g, sm);
+        if (e != hipSuccess) return hip_fail(e);
+        if (o) {
+            hta::WinLaunch w = ring_launch(ctx, s, q, o, n);
+            w.add = static_cast<float*>(o);
+            e = run_swa_dswa(w, ctx->p.swa_window, ctx->p.dswa_taps, ctx->p.dswa_dilation, sm);
+            if (e != hipSuccess) return hip_fail(e);
+        }
     }
     ctx->n_frames = n + 1;
     return HTA_OK;

@@ -27,6 +27,7 @@ struct WinLaunch {
     const void* v;
     void* o;
     const float* add;       // optional fp32 partial [BH][Tq*P][dv] added to o (may equal o for fp32)
+    const float* add2;      // optional second fp32 partial, same layout (never equals o)
     long long q_bh;         // elements between (b,h) slices of q / o / add
     long long kv_bh;        // elements between (b,h) slices of k / v
     long long kv_frame;     // elements between consecutive key frames (P*d)
@@ -67,7 +68,10 @@ struct GlaLaunch {
 
 // Chunked GLA: fp32 (vector ALU) and bf16 (MFMA) paths.
 hipError_t launch_gla_f32(const GlaLaunch& g, hipStream_t stream);
-hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream);
+// bf16 GLA: the chunk-parallel prep kernel, then the sequential scan kernel
+// (parts selects either or both, so the two can go on different streams).
+constexpr int kGlaPrep = 1, kGlaScan = 2;
+hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream, int parts = kGlaPrep | kGlaScan);
 size_t gla_bf16_workspace_bytes(int BH, long long L, int chunk);
 
 // Per-(b,h) strided copy of `elems` elements (16-byte multiples) from

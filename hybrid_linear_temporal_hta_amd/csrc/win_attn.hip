@@ -31,7 +31,7 @@
 //   * the softmax denominator sums the same bf16-rounded weights that feed the
 //     PV product (v_dot2_f32_bf16 against ones), so the output is an exact
 //     convex combination of those weights;
-//   * the epilogue adds an optional fp32 partial (the GLA branch) and writes
+//   * the epilogue adds up to two fp32 partials (the other branches) and writes
 //     the fp32 sum, or rounds it once to bf16.
 // fp32 kernel (d = 64 or 128): a plain per-row online softmax on the vector
 // ALU (4 lanes per query row); used for fp32 inputs, whose workloads are tiny.
@@ -51,9 +51,11 @@ constexpr int kRowB = kD * 2;    // bytes per K / V row in LDS (unpadded, chunk-
 constexpr int kTileB = kBK * kRowB;
 constexpr float kLazyLog2 = 8.0f;
 
-// 16-byte chunk c of LDS row r lives in slot c ^ swz(r): conflict-free for both
-// the K fragment reads (32 rows x one chunk) and the transposed V reads.
-__device__ __forceinline__ int swz(int r) { return (r & 7) << 1; }
+// 16-byte chunk c of LDS row r lives in slot c ^ swz(r), a rotation of the row's
+// low four bits: on gfx950's 64-bank LDS this is conflict-free for both the K
+// fragment reads (32 rows x one chunk) and the transposed V reads (4 rows x 4
+// chunks per 16 lanes), as the SQ_LDS_BANK_CONFLICT counter confirms.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 struct Acc {
     f32x16 o[4];   // O^T fragments: d-block db, element i -> d = 32 db + 8(i/4) + 4 h + i%4
@@ -108,6 +110,7 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t
 struct LaneOffs {
     uint32_t k[8];     // K fragment ks of key row n (32-key block 0, stage 0)
     uint32_t v[4];     // V^T fragment of d-block db, rows 4(g/2) + j (block 0, stage 0)
+    uint32_t vh[4];    // ... and rows 8 + 4(g/2) + j (swz differs in row bit 3)
     uint32_t dma[4];   // source offset within a tile of DMA instruction i (row r, slot c)
     int dma_row[4];    // ... and its row, for the clamped copy of a ragged tile
     int dma_col[4];    // ... and its column
@@ -120,13 +123,15 @@ __device__ __forceinline__ void lane_offsets(LaneOffs& L, int wave, int lane) {
     // V^T fragments by transposed LDS reads: within each 16-lane group g, lane
     // 4j + a addresses row (key) 4(g/2) + j (+8, +16 gg, +32 kb: immediates),
     // columns 16(g%2) + 4a .. +3 of the d-block; the read hands lane 4a + b
-    // column b of rows j = 0..3. swz of those rows depends only on the lane.
+    // column b of rows j = 0..3. swz depends on row bits 0-3 only, so rows
+    // +16 and +32 share these offsets and rows +8 get their own.
     const int g = lane >> 4, sl = lane & 15, jr = sl >> 2, ac = sl & 3;
-    const int r0 = 4 * (g >> 1) + jr;
+    const int r0 = 4 * (g >> 1) + jr, r1 = r0 + 8;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
         const int col = 32 * db + 16 * (g & 1) + 4 * ac;
         L.v[db] = r0 * kRowB + 16 * ((col >> 3) ^ swz(r0)) + 8 * ((col >> 2) & 1);
+        L.vh[db] = r1 * kRowB + 16 * ((col >> 3) ^ swz(r1)) + 8 * ((col >> 2) & 1);
     }
     // DMA: wave w, instruction i fills LDS chunks [64 (4w + i), +64) of a tile;
     // lane l fills chunk 64 (4w + i) + l = row r, slot c ^ swz(r).
@@ -199,7 +204,7 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-    mt = fmaxf(mt, wave_xor32(mt));
+    mt = halves_max(mt);
     const bool grow = (mt - a.m) * c > kLazyLog2;
     if (__any(grow)) {
         const float mn = grow ? mt : a.m;
@@ -234,9 +239,9 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int gg = 0; gg < 2; ++gg) {
-                const char* vr = Vs + (kb * 32 + 16 * gg) * kRowB + L.v[db];
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vr);
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vr + 8 * kRowB));
+                const char* vb = Vs + (kb * 32 + 16 * gg) * kRowB;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + L.v[db]));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + L.vh[db]));
                 a.o[db] = mfma32(cat(lo, hi), pf[kb][gg], a.o[db]);
             }
 }
@@ -347,13 +352,14 @@ void win_attn_bf16_kernel(WinLaunch w) {
         if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     }
 
-    // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add), rounded once.
+    // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add) (+ add2), rounded once.
     if (qrow >= w.P) return;
-    const float invA = 1.f / (A.l + wave_xor32(A.l));
+    const float invA = 1.f / halves_sum(A.l);
     float invB = 0.f;
-    if (NBR == 2) invB = 1.f / (Bacc.l + wave_xor32(Bacc.l));
+    if (NBR == 2) invB = 1.f / halves_sum(Bacc.l);
     const long long orow = (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
     const float* ap = w.add ? w.add + orow : nullptr;
+    const float* ap2 = w.add2 ? w.add2 + orow : nullptr;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -367,6 +373,11 @@ void win_attn_bf16_kernel(WinLaunch w) {
             }
             if (ap) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(ap + d0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] += x[i];
+            }
+            if (ap2) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(ap2 + d0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) r[i] += x[i];
             }
@@ -459,6 +470,7 @@ __global__ __launch_bounds__(256) void win_attn_f32_kernel(WinLaunch w) {
     if (!valid) return;
     float* op = static_cast<float*>(w.o) + qoff;
     const float* ap = w.add ? w.add + qoff : nullptr;
+    const float* ap2 = w.add2 ? w.add2 + qoff : nullptr;
     const float iA = 1.f / lA;
     const float iB = NBR == 2 ? 1.f / lB : 0.f;
 #pragma unroll
@@ -466,6 +478,7 @@ __global__ __launch_bounds__(256) void win_attn_f32_kernel(WinLaunch w) {
         float r = accA[i] * iA;
         if (NBR == 2) r += accB[i] * iB;
         if (ap) r += ap[4 * i + sub];
+        if (ap2) r += ap2[4 * i + sub];
         op[4 * i + sub] = r;
     }
 }

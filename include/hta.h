@@ -23,7 +23,10 @@
  *     strength beta in [0, 1] (the pages: beta = sigmoid(.), alpha in (0,1)).
  *   - GLA state: fp32 [B][H][dk][dv] holding S^T (S is dv x dk: v_old = S k).
  *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
- *     caller. The library allocates no device memory and keeps no global state.
+ *     caller. The library allocates no device memory. Its only global state:
+ *     one auxiliary HIP stream (non-blocking, default priority) and two events
+ *     per device, created on the first bf16 hybrid or stream step and kept
+ *     until the process exits; see hta_hybrid_fwd.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
  *     the null stream). Results are valid once the stream has synchronised.
  *   - All arguments are checked before anything is enqueued. On a non-zero
@@ -141,9 +144,15 @@ int hta_gla_fwd(const hta_shape* shape, const void* q, const void* k, const void
 /*
  * hta_hybrid_fwd -- the whole layer (three-branch figure): o = o_swa + o_dswa + o_gla
  * with shared q, k, v. state as in hta_gla_fwd. workspace: >=
- * hta_workspace_bytes(HTA_OP_HYBRID, shape, params). Enqueues exactly what
- * hta_gla_fwd (writing its fp32 partial into o, or into the workspace for a
- * bf16 o) followed by hta_swa_dswa_fwd (add = that partial) would.
+ * hta_workspace_bytes(HTA_OP_HYBRID, shape, params).
+ * bf16 inputs: the GLA branch (into an fp32 partial in the workspace) runs on
+ * the library's auxiliary stream, forked from `stream` by an event, beside the
+ * SWA pass on `stream` (into o when out_dtype is HTA_F32, else into a second
+ * fp32 workspace partial); `stream` then waits for the GLA branch and the
+ * DSWA pass adds both partials, rounding once. Everything the call enqueues is
+ * ordered after the work already on `stream`, and later work on `stream` is
+ * ordered after all of it. The fork/join is serialised across host threads.
+ * fp32 inputs: GLA into o, then SWA + DSWA adding it, all on `stream`.
  */
 int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params,
                    const void* q, const void* k, const void* v,
@@ -185,8 +194,10 @@ int hta_stream_init(hta_stream_ctx* ctx, const void* k_prefix, const void* v_pre
  *      SWA over frames n..n-W+1 and DSWA over n - j*dil, read from the ring.
  * q, k, v: [B][H][P][d]; alpha, beta: [B][H][P]; o: [B][H][P][dv] or NULL
  * (commit only). workspace: >= hta_workspace_bytes(HTA_OP_STREAM_STEP,
- * &ctx->s with T = 1, &ctx->p). ctx->n_frames is incremented after a
- * successful enqueue. A context must not be used by two threads at once.
+ * &ctx->s with T = 1, &ctx->p). With bf16 inputs and o != NULL, steps 2 and 3
+ * overlap as in hta_hybrid_fwd (GLA on the auxiliary stream). ctx->n_frames
+ * is incremented after a successful enqueue. A context must not be used by
+ * two threads at once.
  */
 int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, void* o,

@@ -118,11 +118,20 @@ def test_workspace_bytes_rules():
     assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, s, prm) == 0     # T must be 1
     s1 = shape(T=1)
     assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, s1, prm) > 0
-    # fp32 output: the GLA partial lives in o, so the hybrid needs no extra buffer
-    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape(out=hta.HTA_F32), prm) == \
-        hta.hta_workspace_bytes(hta.HTA_OP_GLA, shape(out=hta.HTA_F32), prm)
+    # bf16 inputs: the GLA branch runs beside the SWA pass with an fp32 partial of
+    # its own; a bf16 o also needs an fp32 buffer for the SWA pass.
+    so = shape(out=hta.HTA_F32)
+    part = so.B * so.H * so.T * so.P * so.dv * 4
+    part = (part + 255) // 256 * 256
+    gla = hta.hta_workspace_bytes(hta.HTA_OP_GLA, so, prm)
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, so, prm) == gla + part
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape(), prm) == gla + 2 * part
+    # fp32 inputs run the branches in sequence with the GLA partial in o
     f32 = shape(dtype=hta.HTA_F32, d=64)
-    assert hta.hta_workspace_bytes(hta.HTA_OP_GLA, f32, hta.make_params(chunk=16)) > 0
+    prm16 = hta.make_params(chunk=16)
+    assert hta.hta_workspace_bytes(hta.HTA_OP_GLA, f32, prm16) > 0
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, f32, prm16) == \
+        hta.hta_workspace_bytes(hta.HTA_OP_GLA, f32, prm16)
 
 
 def test_stream_ring_too_small():
