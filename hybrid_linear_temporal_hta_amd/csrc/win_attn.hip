@@ -51,6 +51,7 @@ constexpr int kRowB = kD * 2;    // bytes per K / V row in LDS (unpadded, chunk-
 constexpr int kTileB = kBK * kRowB;
 constexpr float kLazyLog2 = 8.0f;
 
+
 // 16-byte chunk c of LDS row r lives in slot c ^ swz(r), a rotation of the row's
 // low four bits: on gfx950's 64-bank LDS this is conflict-free for both the K
 // fragment reads (32 rows x one chunk) and the transposed V reads (4 rows x 4
@@ -100,9 +101,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 // stage (it cannot tell the buffers apart); completion is tracked by wait_vmcnt.
 // It has no register outputs.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+    // the base is wave-uniform; readfirstlane pins it to SGPRs for the asm operand
+    // (readfirstlane returns int: widen each half as uint32_t, never sign-extended)
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds), "v"(voff), "s"(sbase)
+                 : "s"(lds), "v"(voff), "s"(sb)
                  : "m0");
 }
 
