@@ -28,7 +28,7 @@ if ROOT not in sys.path:
 METRIC = "hybrid temporal-attn fwd tokens/s at L=32760,H=16,d=128; % MFMA peak"
 PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0              # MI355X HBM3E
-ATTN_KERNEL = "win_attn_bf16_kernel<1, 2>"   # one branch per pass, 2-stage K/V ring
+ATTN_KERNEL = "win_attn_bf16_kernel<1>"   # one branch per pass
 PMC_FILE = os.path.join(ROOT, "profiles", "win_attn_bf16_hybrid_fwd_B2H16L32760_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "hybrid_linear_temporal_hta_amd", "csrc", "win_attn.hip")
 ATTN_LAUNCHES = 2                   # SWA pass, then DSWA pass (adds the SWA+GLA partial)

@@ -73,20 +73,36 @@ def kernel_stats(path: str):
 
 def trace_by_grid(path: str, prefix: str = "hta::"):
     """Durations from ``*_kernel_trace.csv`` grouped by (kernel, grid size), so
-    launches of one kernel on different workloads are told apart."""
-    groups = {}
+    launches of one kernel on different workloads are told apart. Also the
+    longest uninterrupted run of such launches (no other kernel in between, in
+    dispatch order): a loop that launches only this kernel, timed alone."""
+    rows = []
     with open(_find(path, "kernel_trace.csv")) as f:
         for r in csv.DictReader(f):
-            name = _short(r["Kernel_Name"])
-            if not name.startswith(prefix):
-                continue
-            key = (name, int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])))
-            groups.setdefault(key, []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            rows.append((int(r["Start_Timestamp"]), _short(r["Kernel_Name"]),
+                         int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    groups, runs = {}, {}
+    prev, cur = None, []
+    for _, name, wgs, dur in rows + [(0, None, 0, 0.0)]:
+        key = (name, wgs)
+        if key != prev and cur:
+            if len(cur) > len(runs.get(prev, [])):
+                runs[prev] = cur
+            cur = []
+        if name is None:
+            break
+        prev = key
+        cur.append(dur)
+        if name.startswith(prefix):
+            groups.setdefault(key, []).append(dur)
     out = []
     for (name, wgs), d in groups.items():
+        run = runs.get((name, wgs), [])
         out.append({"kernel": name, "workgroups": wgs, "calls": len(d),
-                    "avg_us": sum(d) / len(d), "min_us": min(d), "max_us": max(d)})
+                    "avg_us": sum(d) / len(d), "min_us": min(d), "max_us": max(d),
+                    "run_calls": len(run), "run_avg_us": sum(run) / len(run) if run else 0.0})
     out.sort(key=lambda r: -r["avg_us"] * r["calls"])
     return out
 
@@ -114,11 +130,15 @@ def cmd_stats(a):
     for r in rows[:a.top]:
         lines.append(f"{r['kernel'][:58]:<58} {r['calls']:>6} {r['avg_ns'] / 1e3:>10.1f} "
                      f"{r['min_ns'] / 1e3:>10.1f} {r['max_ns'] / 1e3:>10.1f} {r['pct']:>6.2f}")
-    lines += ["", "Library kernels by launch shape (from the kernel trace):", "",
-              f"{'kernel':<46} {'workgroups':>10} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}"]
+    lines += ["", "Library kernels by launch shape (from the kernel trace); run = the longest",
+              "stretch of consecutive launches of that kernel and shape with no other kernel",
+              "in between (a loop timing it alone):", "",
+              f"{'kernel':<34} {'workgroups':>10} {'calls':>6} {'avg_us':>9} {'min_us':>9} "
+              f"{'max_us':>9} {'run':>5} {'run_avg_us':>10}"]
     for r in trace_by_grid(a.csv):
-        lines.append(f"{r['kernel'][:46]:<46} {r['workgroups']:>10} {r['calls']:>6} "
-                     f"{r['avg_us']:>10.1f} {r['min_us']:>10.1f} {r['max_us']:>10.1f}")
+        lines.append(f"{r['kernel'][:34]:<34} {r['workgroups']:>10} {r['calls']:>6} "
+                     f"{r['avg_us']:>9.1f} {r['min_us']:>9.1f} {r['max_us']:>9.1f} "
+                     f"{r['run_calls']:>5} {r['run_avg_us']:>10.1f}")
     text = "\n".join(lines) + "\n"
     with open(a.out, "w") as f:
         f.write(text)
