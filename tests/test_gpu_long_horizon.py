@@ -1,0 +1,55 @@
+"""GPU parity at the long-horizon workload: B1 H16 d128, T=336 frames of P=1560
+tokens (L=524160), bf16 q/k/v, hybrid forward with fp32 output.
+
+The oracle covers the last two frames of the output and the final GLA state:
+SWA/DSWA rows from their definition over a 14-frame slice of the history that
+holds every tap those frames reach (frames 322..335: SWA 333..335, DSWA down to
+322), and the GLA branch from the token-by-token recurrence over all 524160
+tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, assert_parity, f64
+from hybrid_linear_temporal_hta_amd import hta
+from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.slow
+def test_long_horizon_last_frames_and_state():
+    w = WORKLOADS["long_horizon"]
+    print(f"[case] long horizon {w.name} B{w.B} H{w.H} T{w.T} P{w.P}", flush=True)
+    x = make_inputs(w, device="cuda", frames=w.T)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    st = torch.zeros(w.B, w.H, w.dk, w.dv, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device="cuda")
+    hta.hta_hybrid_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, w.P, prm)
+    torch.cuda.synchronize()
+    reach = max(w.window - 1, (w.taps - 1) * w.dilation)   # 12 frames back
+    n_last = 2
+    F0 = w.T - n_last - reach                              # first frame of the slice
+    Th = w.T - F0
+    got = f64(o[:, :, (w.T - n_last) * w.P:])
+    st_gpu = f64(st)
+    sl = slice(F0 * w.P, w.T * w.P)
+    qh, kh, vh = (f64(x[n][:, :, sl]) for n in ("q", "k", "v"))
+    BH = w.B * w.H
+    pos = np.arange((Th - n_last) * w.P, Th * w.P)
+    rows = (np.arange(BH)[:, None] * (Th * w.P) + pos[None, :]).reshape(-1)
+    print(f"[case] oracle SWA/DSWA on {rows.size} rows over a {Th}-frame slice", flush=True)
+    ref_att = oracle.swa_rows(qh, kh, vh, Th, w.P, w.window, rows) + \
+        oracle.dswa_rows(qh, kh, vh, Th, w.P, w.taps, w.dilation, rows)
+    del qh, kh, vh
+    print("[case] oracle GLA recurrence over all tokens", flush=True)
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    alpha, beta = x["alpha"].cpu(), x["beta"].cpu()
+    del x
+    ref_g, ref_st = oracle.gla(q, k, v, alpha, beta)
+    del q, k, v
+    assert_parity(st_gpu, ref_st, w.dtype, "long-horizon final state")
+    ref = ref_att.reshape(w.B, w.H, n_last * w.P, w.dv) + ref_g[:, :, (w.T - n_last) * w.P:]
+    assert_parity(got, ref, w.dtype, "long-horizon last two frames")
