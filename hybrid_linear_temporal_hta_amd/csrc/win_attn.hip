@@ -187,16 +187,14 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
                                             float c, int lane) {
     const int h = lane >> 5;
     f32x16 s[2];
+    const f32x16 zero = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int kb = 0; kb < 2; ++kb) {
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * kRowB + L.k[ks]);
-            s[kb] = mfma32(kf, qf[ks], s[kb]);
+            s[kb] = mfma32(kf, qf[ks], ks == 0 ? zero : s[kb]);
         }
-    }
     if (__builtin_expect(nvalid < kBK, 0)) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -241,11 +239,11 @@ __device__ __forceinline__ void attend_tile(Acc& a, const bf16x8 (&qf)[8], const
     a.l += lsum;
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
-            for (int gg = 0; gg < 2; ++gg) {
+            for (int db = 0; db < 4; ++db) {
                 const char* vb = Vs + (kb * 32 + 16 * gg) * kRowB;
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + L.v[db]));
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + L.vh[db]));
