@@ -21,9 +21,15 @@
 //   prep (one workgroup per chunk, all chunks in parallel): g, A and Pm from
 //     K K^T and Q K^T on v_mfma_f32_32x32x16_bf16, T by a register-resident
 //     forward substitution in fp32, and the chunk's operand block -- K, Q (fp16),
-//     T, Pm (fp16), e^{g}, e^{g_C - g}, beta (fp32) -- written contiguously in
-//     exactly the LDS layout the scan consumes (bank-conflict-free swizzles
-//     included).
+//     T, Pm (fp16), e^{g}, e^{g_C - g}, beta, e^{gp} (fp32) -- written
+//     contiguously in exactly the LDS layout the scan consumes (bank-conflict-free
+//     swizzles included).
+//
+// The printed form of the update (GlaLaunch::form = 1: the erase term uses the
+// state before the forget gate, S_t = alpha S - beta (S k) k^T + beta v k^T)
+// differs only where the chunk predicts values from the state: A and the K M0
+// term of X take e^{g_{i-1}} (exclusive cumulative sum, "gp") instead of e^{g_i}.
+// Pm, the output and the state update are the same.
 //   scan (one workgroup per (batch, head, 64 value columns), chunks in order):
 //     each wave owns 16 value columns of the fp32 state as eight 16x16 MFMA
 //     accumulator tiles. K M0, Q M0, T X, Pm U and K^T U run on
@@ -54,11 +60,13 @@ constexpr int kOffP = 40960;           // Pm fp16, same layout
 constexpr int kOffE = 49152;           // e^{g_t} fp32 [64]
 constexpr int kOffD = 49408;           // e^{g_C - g_t} fp32 [64]
 constexpr int kOffB = 49664;           // beta fp32 [64] (0 past the end of the sequence)
+constexpr int kOffX = 49920;           // e^{gp_t} fp32 [64]: scale of K M0 in X (gp = g, or
+                                       // g_{t-1} for the printed form)
 constexpr int kBlockMain = 49152;      // K, Q, T, Pm: 48 KiB = 12 x 4 KiB
-constexpr int kTailChunks = 48;        // eg, ed, beta: 768 bytes = 48 x 16
-constexpr size_t kChunkBytes = 49920;  // + eg, ed, beta
-constexpr int kOffV = 49920;           // LDS only: V tile bf16 [64 tokens][64 columns]
-constexpr int kStageBytes = kOffV + 64 * 64 * 2;   // 58112
+constexpr int kTailChunks = 64;        // eg, ed, beta, egp: 1 KiB = 64 x 16
+constexpr size_t kChunkBytes = 50176;  // + eg, ed, beta, egp
+constexpr int kOffV = 50176;           // LDS only: V tile bf16 [64 tokens][64 columns]
+constexpr int kStageBytes = kOffV + 64 * 64 * 2;   // 58368
 
 // 256-byte rows (K, Q): chunk c of row r in slot c ^ swz64(r).
 __device__ __forceinline__ int swz64(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
@@ -83,6 +91,7 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
     __shared__ __attribute__((aligned(16))) bf16 Ks[kC * kKsP];
     __shared__ __attribute__((aligned(16))) float As[kC * kAsP];   // A[i][(j&3)*16 + (j>>2)]
     __shared__ float gs[kC];
+    __shared__ float gps[kC];   // decay exponent of the erase path (see kOffX)
     __shared__ float bs[kC];
 
     const int cid = blockIdx.x;
@@ -120,11 +129,15 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
         }
         const float b = lane < n ? g.beta[(long long)bh * g.L + t0 + lane] : 0.f;
         const float gC = __shfl(la, 63, 64);
+        const float prev = __shfl_up(la, 1, 64);
+        const float gp = g.form ? (lane == 0 ? 0.f : prev) : la;
         gs[lane] = la;
+        gps[lane] = gp;
         bs[lane] = b;
         reinterpret_cast<float*>(blk + kOffE)[lane] = __expf(la);
         reinterpret_cast<float*>(blk + kOffD)[lane] = __expf(gC - la);
         reinterpret_cast<float*>(blk + kOffB)[lane] = b;
+        reinterpret_cast<float*>(blk + kOffX)[lane] = __expf(gp);
     }
     __syncthreads();
 
@@ -155,7 +168,8 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
         for (int e = 0; e < 16; ++e) {
             const int i = mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
             const float dec = (j <= i) ? __expf(gs[i] - gs[j]) : 0.f;
-            As[i * kAsP + (j & 3) * 16 + (j >> 2)] = (j < i) ? bs[i] * dec * kk[e] : 0.f;
+            const float deca = (j < i) ? __expf(gps[i] - gs[j]) : 0.f;
+            As[i * kAsP + (j & 3) * 16 + (j >> 2)] = (j < i) ? bs[i] * deca * kk[e] : 0.f;
             *reinterpret_cast<f16*>(blk + kOffP + offT(i, j)) = (f16)((j <= i) ? dec * qk[e] : 0.f);
         }
     }
@@ -295,6 +309,7 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
         const float* esm = reinterpret_cast<const float*>(S + kOffE);
         const float* dsm = reinterpret_cast<const float*>(S + kOffD);
         const float* bsm = reinterpret_cast<const float*>(S + kOffB);
+        const float* xsm = reinterpret_cast<const float*>(S + kOffX);
 
         // K M0 and Q M0 (fragments of the critical path read ahead of their use)
         f16x8 kf[4][4];
@@ -320,10 +335,11 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
             for (int kt = 0; kt < 2; ++kt)
                 if (kt == 0 || rb >= 2) tf[rb][kt] = afragT(S + kOffT, 16 * rb + m, kt, G);
         // Per-token factors of this lane's rows 16rb + 4G + i, four at a time.
-        f32x4 e4[4], d4[4], b4[4];
+        f32x4 e4[4], d4[4], b4[4], x4[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             e4[rb] = *reinterpret_cast<const f32x4*>(esm + 16 * rb + 4 * G);
+            x4[rb] = *reinterpret_cast<const f32x4*>(xsm + 16 * rb + 4 * G);
             d4[rb] = *reinterpret_cast<const f32x4*>(dsm + 16 * rb + 4 * G);
             b4[rb] = *reinterpret_cast<const f32x4*>(bsm + 16 * rb + 4 * G);
         }
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                X[rb][i] = b4[rb][i] * (bf2f(v4[rb][i]) - e4[rb][i] * KM[rb][i]);
+                X[rb][i] = b4[rb][i] * (bf2f(v4[rb][i]) - x4[rb][i] * KM[rb][i]);
         const f16x8 xb[2] = {bfrag(X[0], X[1]), bfrag(X[2], X[3])};
         // U = T X (T lower triangular: row blocks 0,1 only see k-step 0)
         f32x4 U[4];

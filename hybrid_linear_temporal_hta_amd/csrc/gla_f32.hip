@@ -32,6 +32,8 @@ __global__ __launch_bounds__(256) void gla_f32_kernel(GlaLaunch g) {
     __shared__ float As[C * C];        // A, then Pm
     __shared__ float gs[C];
     __shared__ float egs[C];
+    __shared__ float gps[C];    // decay exponent of the erase path: g_i, or g_{i-1} (printed form)
+    __shared__ float egps[C];
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
@@ -56,20 +58,24 @@ __global__ __launch_bounds__(256) void gla_f32_kernel(GlaLaunch g) {
             float acc = 0.f;
             for (int i = 0; i < n; ++i) {
                 const float lg = logf(al[t0 + i]);
+                const float prev = acc;
                 acc += (lg < kLogFloor) ? kLogFloor : lg;   // NaN passes through
                 gs[i] = acc;
                 egs[i] = expf(acc);
+                gps[i] = g.form ? prev : acc;
+                egps[i] = expf(gps[i]);
             }
         }
         __syncthreads();
-        // A[i][j] = beta_i e^{g_i - g_j} k_i.k_j for j < i.
+        // A[i][j] = beta_i e^{gp_i - g_j} k_i.k_j for j < i (gp = g, or g_{i-1} for the
+        // printed form, whose erase term reads the state before the decay).
         for (int e = tid; e < n * n; e += 256) {
             const int i = e / n, j = e - i * n;
             float a = 0.f;
             if (j < i) {
                 float s = 0.f;
                 for (int r = 0; r < D; ++r) s += Kc[i * D + r] * Kc[j * D + r];
-                a = be[t0 + i] * expf(gs[i] - gs[j]) * s;
+                a = be[t0 + i] * expf(gps[i] - gs[j]) * s;
             }
             As[i * C + j] = a;
         }
@@ -80,7 +86,7 @@ __global__ __launch_bounds__(256) void gla_f32_kernel(GlaLaunch g) {
             const int cc = isW ? col : col - D;
             float* X = isW ? Ws : Us;
             for (int i = 0; i < n; ++i) {
-                float x = isW ? be[t0 + i] * egs[i] * Kc[i * D + cc] : be[t0 + i] * Vc[i * D + cc];
+                float x = isW ? be[t0 + i] * egps[i] * Kc[i * D + cc] : be[t0 + i] * Vc[i * D + cc];
                 for (int j = 0; j < i; ++j) x -= As[i * C + j] * X[j * D + cc];
                 X[i * D + cc] = x;
             }

@@ -86,6 +86,8 @@ int check_params(const hta_shape* s, const hta_params* p) {
     if ((st = check_chunk(s->dtype, p->gla_chunk)) != HTA_OK) return st;
     if ((st = check_scale(p->attn_scale)) != HTA_OK) return st;
     if (!isfinite(p->gla_scale)) return HTA_ERR_UNSUPPORTED;
+    if (p->gla_form != HTA_GLA_GATED_DELTA && p->gla_form != HTA_GLA_PRINTED)
+        return HTA_ERR_UNSUPPORTED;
     return HTA_OK;
 }
 
@@ -230,7 +232,7 @@ hipError_t run_swa_dswa(hta::WinLaunch w, int window, int taps, int dil, hipStre
 
 hta::GlaLaunch gla_base(const hta_shape* s, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, float* state, void* o,
-                        int chunk, float scale, void* ws, size_t ws_bytes) {
+                        int chunk, float scale, void* ws, size_t ws_bytes, int form = 0) {
     hta::GlaLaunch g;
     memset(&g, 0, sizeof(g));
     g.q = q; g.k = k; g.v = v; g.alpha = alpha; g.beta = beta; g.state = state; g.o = o;
@@ -243,6 +245,7 @@ hta::GlaLaunch gla_base(const hta_shape* s, const void* q, const void* k, const 
     g.dtype = s->dtype;
     g.ws = ws;
     g.ws_bytes = ws_bytes;
+    g.form = form;
     return g;
 }
 
@@ -413,6 +416,26 @@ int hta_gla_fwd(const hta_shape* shape, const void* q, const void* k, const void
     return e == hipSuccess ? HTA_OK : hip_fail(e);
 }
 
+int hta_gla_fwd_ex(const hta_shape* shape, const hta_params* params, const void* q, const void* k,
+                   const void* v, const float* alpha, const float* beta, float* state, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_shape(shape)) != HTA_OK) return st;
+    if (!params) return HTA_ERR_NULL;
+    if ((st = check_chunk(shape->dtype, params->gla_chunk)) != HTA_OK) return st;
+    if (!isfinite(params->gla_scale)) return HTA_ERR_UNSUPPORTED;
+    if (params->gla_form != HTA_GLA_GATED_DELTA && params->gla_form != HTA_GLA_PRINTED)
+        return HTA_ERR_UNSUPPORTED;
+    const size_t need = gla_ws(shape, params->gla_chunk);
+    if ((st = check_gla_buffers(shape, q, k, v, alpha, beta, state, o, workspace, workspace_bytes,
+                                need)) != HTA_OK)
+        return st;
+    hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, o, params->gla_chunk,
+                                params->gla_scale, workspace, need, params->gla_form);
+    hipError_t e = run_gla(g, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
 int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void* q, const void* k,
                    const void* v, const float* alpha, const float* beta, float* state, void* o,
                    void* workspace, size_t workspace_bytes, void* stream) {
@@ -432,7 +455,7 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void*
                          ? static_cast<float*>(o)
                          : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(shape));
         hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, gpart, params->gla_chunk,
-                                    params->gla_scale, workspace, need_gla);
+                                    params->gla_scale, workspace, need_gla, params->gla_form);
         g.out_f32 = 1;
         hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
         hipError_t e = run_hybrid_overlapped(g, w, mid, params, sm);
@@ -440,7 +463,7 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void*
     }
     // fp32 inputs: GLA into o, then SWA + DSWA adding it in place.
     hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, o, params->gla_chunk,
-                                params->gla_scale, workspace, need_gla);
+                                params->gla_scale, workspace, need_gla, params->gla_form);
     g.out_f32 = 1;
     hipError_t e = run_gla(g, sm);
     if (e != hipSuccess) return hip_fail(e);
@@ -571,13 +594,13 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
                          ? static_cast<float*>(o)
                          : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(&s));
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, gpart, ctx->p.gla_chunk,
-                                    ctx->p.gla_scale, workspace, need_gla);
+                                    ctx->p.gla_scale, workspace, need_gla, ctx->p.gla_form);
         g.out_f32 = 1;
         e = run_hybrid_overlapped(g, ring_launch(ctx, s, q, o, n), mid, &ctx->p, sm);
         if (e != hipSuccess) return hip_fail(e);
     } else {
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, o, ctx->p.gla_chunk,
-                                    ctx->p.gla_scale, workspace, need_gla);
+                                    ctx->p.gla_scale, workspace, need_gla, ctx->p.gla_form);
         g.out_f32 = 1;
         e = run_gla(g, sm);
         if (e != hipSuccess) return hip_fail(e);

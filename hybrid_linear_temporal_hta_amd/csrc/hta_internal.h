@@ -58,6 +58,7 @@ struct GlaLaunch {
     int BH, d, chunk;
     float scale;
     int dtype;
+    int form;               // 0: GatedDeltaNet reading, 1: the printed update (erase not gated)
     void* ring_k;           // optional: copy k/v of these tokens into a ring slot
     void* ring_v;
     long long ring_bh;      // elements between (b,h) slices of the ring

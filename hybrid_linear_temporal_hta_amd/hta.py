@@ -35,9 +35,12 @@ HTA_OP_GLA = 1
 HTA_OP_HYBRID = 2
 HTA_OP_STREAM_STEP = 3
 
+HTA_GLA_GATED_DELTA = 0   # S = alpha (S - beta (S k) k^T) + beta v k^T
+HTA_GLA_PRINTED = 1       # S = alpha S - beta (S k) k^T + beta v k^T
+
 EXPORTED = (
     "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_swa_dswa_fwd", "hta_gla_fwd",
-    "hta_hybrid_fwd",
+    "hta_gla_fwd_ex", "hta_hybrid_fwd",
     "hta_stream_init", "hta_stream_step", "hta_status_string", "hta_last_hip_error",
     "hta_version",
 )
@@ -52,7 +55,8 @@ class Shape(ctypes.Structure):
 class Params(ctypes.Structure):
     _fields_ = [("swa_window", ctypes.c_int), ("dswa_taps", ctypes.c_int),
                 ("dswa_dilation", ctypes.c_int), ("gla_chunk", ctypes.c_int),
-                ("attn_scale", ctypes.c_float), ("gla_scale", ctypes.c_float)]
+                ("attn_scale", ctypes.c_float), ("gla_scale", ctypes.c_float),
+                ("gla_form", ctypes.c_int)]
 
 
 class StreamCtx(ctypes.Structure):
@@ -94,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.hta_swa_dswa_fwd.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp]
     L.hta_gla_fwd.restype = i
     L.hta_gla_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, i, f, vp, sz, vp]
+    L.hta_gla_fwd_ex.restype = i
+    L.hta_gla_fwd_ex.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.hta_hybrid_fwd.restype = i
     L.hta_hybrid_fwd.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.hta_stream_init.restype = i
@@ -151,9 +157,11 @@ def make_shape(q: torch.Tensor, v: torch.Tensor, P: int, o: torch.Tensor | None 
     return Shape(B, H, L // P, P, dk, v.shape[-1], _dtype_code(q), out)
 
 
-def make_params(window=3, taps=4, dilation=4, chunk=64, attn_scale=0.0, gla_scale=0.0) -> Params:
+def make_params(window=3, taps=4, dilation=4, chunk=64, attn_scale=0.0, gla_scale=0.0,
+                gla_form=0) -> Params:
+    """gla_form: HTA_GLA_GATED_DELTA (0) or HTA_GLA_PRINTED (1)."""
     return Params(int(window), int(taps), int(dilation), int(chunk), float(attn_scale),
-                  float(gla_scale))
+                  float(gla_scale), int(gla_form))
 
 
 def hta_workspace_bytes(op: int, shape: Shape, params: Params | None) -> int:
@@ -191,6 +199,17 @@ def hta_gla_fwd(q, k, v, alpha, beta, state, o, P: int, chunk: int = 64, scale: 
     _check(lib().hta_gla_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                              _ptr(state), _ptr(o), int(chunk), float(scale), _ptr(workspace),
                              workspace.numel(), _stream(stream)), "hta_gla_fwd")
+
+
+def hta_gla_fwd_ex(q, k, v, alpha, beta, state, o, P: int, params: Params, workspace=None,
+                   stream=None):
+    s = make_shape(q, v, P, o)
+    need = hta_workspace_bytes(HTA_OP_GLA, s, params)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().hta_gla_fwd_ex(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "hta_gla_fwd_ex")
 
 
 def hta_hybrid_fwd(q, k, v, alpha, beta, state, o, P: int, params: Params, workspace=None,

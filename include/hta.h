@@ -85,7 +85,21 @@ typedef struct {
     int   gla_chunk;      /* C: tokens per chunk of the chunked GLA         */
     float attn_scale;     /* softmax scale; 0 selects 1/sqrt(dk)            */
     float gla_scale;      /* GLA output scale; 0 selects 1                  */
+    int   gla_form;       /* HTA_GLA_GATED_DELTA (0) or HTA_GLA_PRINTED (1) */
 } hta_params;
+
+/*
+ * GLA update forms (GLA paragraph and update equations of the Kairos page):
+ *   HTA_GLA_GATED_DELTA -- the GatedDeltaNet update the page names as the basis:
+ *       S_t = alpha_t (S_{t-1} - beta_t (S_{t-1} k_t) k_t^T) + beta_t v_t k_t^T;
+ *   HTA_GLA_PRINTED     -- the three printed lines taken literally (v_old = S k,
+ *       v_new = beta v + (1 - beta) v_old, S = alpha S - v_old k^T + v_new k^T),
+ *       i.e. S_t = alpha_t S_{t-1} - beta_t (S_{t-1} k_t) k_t^T + beta_t v_t k_t^T:
+ *       the forget gate does not scale the erase term.
+ * Both give o_t = gla_scale * S_t q_t.
+ */
+#define HTA_GLA_GATED_DELTA 0
+#define HTA_GLA_PRINTED     1
 
 /* Operations whose workspace size hta_workspace_bytes() reports. */
 #define HTA_OP_GLA          1
@@ -142,8 +156,19 @@ int hta_gla_fwd(const hta_shape* shape, const void* q, const void* k, const void
                 void* stream);
 
 /*
+ * hta_gla_fwd_ex -- hta_gla_fwd with the chunk, the output scale and the update
+ * form taken from params (gla_chunk, gla_scale, gla_form; the attention fields
+ * are ignored). Same buffers, workspace and error behaviour as hta_gla_fwd;
+ * HTA_ERR_UNSUPPORTED for a gla_form other than the two above.
+ */
+int hta_gla_fwd_ex(const hta_shape* shape, const hta_params* params,
+                   const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, float* state, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * hta_hybrid_fwd -- the whole layer (three-branch figure): o = o_swa + o_dswa + o_gla
- * with shared q, k, v. state as in hta_gla_fwd. workspace: >=
+ * with shared q, k, v; the GLA branch in params->gla_form. state as in hta_gla_fwd. workspace: >=
  * hta_workspace_bytes(HTA_OP_HYBRID, shape, params).
  * bf16 inputs: the GLA branch (into an fp32 partial in the workspace) runs on
  * the library's auxiliary stream, forked from `stream` by an event, beside the

@@ -145,3 +145,22 @@ def test_stream_ring_too_small():
         hta.HTA_ERR_WORKSPACE
     assert lib.hta_stream_init(ctypes.byref(ctx), None, None, 3, None, None) == hta.HTA_ERR_NULL
     assert ctx.n_frames == 0
+
+
+def test_gla_form_validation():
+    """gla_form must be one of the two update forms; hta_gla_fwd_ex checks it
+    before anything else touches the buffers."""
+    s = shape()
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, s, hta.make_params(gla_form=2)) == 0
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, s,
+                                   hta.make_params(gla_form=hta.HTA_GLA_PRINTED)) > 0
+    lib = hta.lib()
+    need = hta.hta_workspace_bytes(hta.HTA_OP_GLA, s, hta.make_params())
+    call = lambda form, ws=W, p=True: lib.hta_gla_fwd_ex(
+        ctypes.byref(s), ctypes.byref(hta.make_params(gla_form=form)) if p else None,
+        F, G, Hh, A, Bt, S, O, ws, need, None)
+    assert call(2) == hta.HTA_ERR_UNSUPPORTED
+    assert call(-1) == hta.HTA_ERR_UNSUPPORTED
+    assert call(0, p=False) == hta.HTA_ERR_NULL
+    assert call(hta.HTA_GLA_PRINTED, ws=None) == hta.HTA_ERR_WORKSPACE
+

@@ -52,6 +52,9 @@ CASES = [
     (1, 1, 1, 300, 128, torch.bfloat16, 3, 4, 4),
     (1, 2, 16, 16, 64, torch.float32, 4, 4, 2),
     (1, 1, 6, 70, 128, torch.float32, 3, 3, 2),
+    # the pages' dilations (6 and 12 frames) over 61 latent frames
+    (1, 2, 61, 48, 128, torch.bfloat16, 3, 4, 6),
+    (1, 1, 61, 40, 128, torch.bfloat16, 3, 4, 12),
 ]
 
 

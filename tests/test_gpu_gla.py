@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import TOL, assert_parity, assert_parity_rounded, f64
+from helpers import TOL, assert_parity, assert_parity_rounded, f64, rel_max_err
 from hybrid_linear_temporal_hta_amd import hta
 from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, Workload, make_inputs
 
@@ -124,3 +124,42 @@ def test_hybrid_full_size_sampled():
         oracle.dswa_rows(q, k, v, w.T, w.P, w.taps, w.dilation, rows) + \
         ref_g.reshape(-1, 128)[rows]
     assert_parity(f64(o).reshape(-1, 128)[rows], ref, w.dtype, "hybrid full-size sampled o")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gla_printed_form_parity(dtype):
+    """The printed update (forget gate not applied to the erase term) against the
+    oracle's token recurrence of the same form; low alpha makes the two forms
+    differ by a large margin, which the test also checks."""
+    print(f"[case] gla printed form {dtype}", flush=True)
+    w = _w(1, 2, 4, 150, dtype=dtype, seed=77, alpha_mu=0.5)
+    x = make_inputs(w, device="cuda", frames=w.T)
+    prm = hta.make_params(chunk=64 if dtype == torch.bfloat16 else 32,
+                          gla_form=hta.HTA_GLA_PRINTED)
+    st = torch.zeros(w.B, w.H, 128, 128, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, 128, dtype=torch.float32, device="cuda")
+    hta.hta_gla_fwd_ex(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, w.P, prm)
+    torch.cuda.synchronize()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    ref_o, ref_st = oracle.gla_literal(q, k, v, x["alpha"], x["beta"])
+    assert_parity(o, ref_o, dtype, "gla printed form o")
+    assert_parity(st, ref_st, dtype, "gla printed form state")
+    gd_o, _ = oracle.gla(q, k, v, x["alpha"], x["beta"])
+    assert rel_max_err(gd_o, ref_o) > 0.05, "the two update forms should differ here"
+
+
+def test_hybrid_printed_form():
+    print("[case] hybrid printed form", flush=True)
+    w = _w(1, 2, 5, 100, seed=78, alpha_mu=1.0, q_unit=False, k_unit=True, qv_std=1.0)
+    x = make_inputs(w, device="cuda", frames=w.T)
+    prm = hta.make_params(3, 4, 2, 64, gla_form=hta.HTA_GLA_PRINTED)
+    st = torch.zeros(w.B, w.H, 128, 128, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, 128, dtype=torch.float32, device="cuda")
+    hta.hta_hybrid_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, w.P, prm)
+    torch.cuda.synchronize()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    ref_g, ref_st = oracle.gla_literal(q, k, v, x["alpha"], x["beta"])
+    ref = oracle.swa(q, k, v, w.T, w.P, 3) + oracle.dswa(q, k, v, w.T, w.P, 4, 2) + ref_g
+    assert_parity(o, ref, w.dtype, "hybrid printed form o")
+    assert_parity(st, ref_st, w.dtype, "hybrid printed form state")
+

@@ -37,8 +37,8 @@ def _start_stream(w, full, T0, prm, out_dtype=torch.float32):
     return s, o
 
 
-def _run_and_check(w, T0, N, check_steps=None, rows=None):
-    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+def _run_and_check(w, T0, N, check_steps=None, rows=None, form=0):
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, gla_form=form)
     full = make_inputs(w, device="cuda", frames=T0 + N)
     s, _ = _start_stream(w, full, T0, prm)
     outs = {}
@@ -52,7 +52,8 @@ def _run_and_check(w, T0, N, check_steps=None, rows=None):
     assert s.n_frames == T0 + N
     # oracle on the whole history
     q, k, v = f64(full["q"]), f64(full["k"]), f64(full["v"])
-    ref_g, ref_st = oracle.gla(q, k, v, full["alpha"], full["beta"])
+    gla_ref = oracle.gla_literal if form == hta.HTA_GLA_PRINTED else oracle.gla
+    ref_g, ref_st = gla_ref(q, k, v, full["alpha"], full["beta"])
     assert_parity(s.state, ref_st, w.dtype, f"stream final state after {N} steps")
     for n, o in outs.items():
         fr = T0 + n
@@ -77,6 +78,15 @@ def test_stream_small(dtype):
     w = Workload("case", 1, 2, 5, 150, 128, 128, dtype, window=3, taps=4, dilation=4, chunk=64,
                  k_unit=True, alpha_mu=3.0, ring=13, seed=41)
     _run_and_check(w, T0=5, N=14)
+
+
+def test_stream_dilation_12_printed_form():
+    """The pages' dilation of 12 frames (ring of 37 frames) with the printed GLA
+    update: outputs of every step against the whole-history definition."""
+    print("[case] stream dil 12, printed GLA form", flush=True)
+    w = Workload("case", 1, 2, 30, 48, 128, 128, torch.bfloat16, window=3, taps=4, dilation=12,
+                 chunk=64, k_unit=True, alpha_mu=2.0, ring=37, seed=45)
+    _run_and_check(w, T0=30, N=10, form=hta.HTA_GLA_PRINTED)
 
 
 def test_stream_from_empty_prefix():
