@@ -19,6 +19,7 @@ import torch
 
 import oracle
 from oracle.gla_chunked import gla_chunked
+from oracle.project import project
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -350,3 +351,89 @@ def test_stream_frame_from_history_equals_batch_rows():
         hk, hv = k[:, :, :(n + 1) * P], v[:, :, :(n + 1) * P]
         o_s = oracle.stream_frame(hk, hv, q[:, :, n * P:(n + 1) * P], P, 3, 4, 4)
         np.testing.assert_allclose(o_s, o_b[:, :, n * P:(n + 1) * P], rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------- projections
+
+def test_golden_projection_worked_example():
+    """Hand-worked single token: column order q | k | v | alpha | beta, the L2
+    normalisation of q and k, and sigmoid(0) = 1/2 for both gates."""
+    g = json.load(open(os.path.join(GOLDEN, "project_tiny_worked.json")))
+    x = np.array([[[float(_frac(a)) for a in g["x"][0]]]])
+    w = np.array([[float(_frac(a)) for a in row] for row in g["w_rows"]])
+    q, k, v, al, be = project(x, w, H=1, dk=2, dv=2)
+    fx = lambda key: np.array([[float(_frac(a)) for a in row] for row in g[key]])
+    assert np.allclose(q[0, 0], fx("q"), atol=1e-15, rtol=0)
+    assert np.allclose(k[0, 0], fx("k"), atol=1e-15, rtol=0)
+    assert np.allclose(v[0, 0], fx("v"), atol=1e-15, rtol=0)
+    assert al[0, 0, 0] == 0.5 and be[0, 0, 0] == 0.5
+    q2, k2, *_ = project(x, w, H=1, dk=2, dv=2, norm_q=False, norm_k=False)
+    assert np.allclose(q2[0, 0], fx("q_raw"), atol=1e-15, rtol=0)
+    assert np.allclose(k2[0, 0], fx("k_raw"), atol=1e-15, rtol=0)
+
+
+def _rand_proj(seed, B=2, L=9, Dm=16, H=3, dk=4, dv=5):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((B, L, Dm))
+    w = r.standard_normal((Dm, 2 * H * dk + H * dv + 2 * H)) / np.sqrt(Dm)
+    return x, w, H, dk, dv
+
+
+def test_projection_gate_special_values():
+    """sigmoid at 0, at ln 3 (exactly 3/4) and its symmetry, through the gate columns."""
+    x = np.array([[[0.0], [np.log(3.0)], [-np.log(3.0)]]])          # B=1, L=3, Dm=1
+    w = np.zeros((1, 2 * 1 * 1 + 1 + 2))                             # H=1, dk=dv=1
+    w[0, 3] = 1.0                                                    # alpha column
+    w[0, 4] = -1.0                                                   # beta column
+    _, _, _, al, be = project(x, w, H=1, dk=1, dv=1)
+    assert np.allclose(al[0, 0], [0.5, 0.75, 0.25], atol=1e-15, rtol=0)
+    assert np.allclose(be[0, 0], [0.5, 0.25, 0.75], atol=1e-15, rtol=0)
+
+
+def test_projection_unit_norm_and_zero_rows():
+    x, w, H, dk, dv = _rand_proj(1)
+    x[0, 3] = 0.0                                                     # a zero token
+    q, k, v, al, be = project(x, w, H, dk, dv)
+    n = np.sqrt((q * q).sum(-1))
+    assert np.allclose(np.delete(n, 3, axis=2), 1.0, atol=1e-14)
+    assert np.all(q[0, :, 3] == 0) and np.all(k[0, :, 3] == 0)
+    assert np.all((al > 0) & (al < 1)) and np.all((be > 0) & (be < 1))
+
+
+def test_projection_linear_before_normalisation_and_token_local():
+    """Without normalisation q, k, v are linear in x, and each token's outputs
+    depend only on that token (permuting tokens permutes every output)."""
+    x, w, H, dk, dv = _rand_proj(2)
+    x2 = np.random.default_rng(3).standard_normal(x.shape)
+    a = project(2.0 * x - 0.5 * x2, w, H, dk, dv, False, False)
+    b = project(x, w, H, dk, dv, False, False)
+    c = project(x2, w, H, dk, dv, False, False)
+    for i in range(3):
+        assert np.allclose(a[i], 2.0 * b[i] - 0.5 * c[i], atol=1e-12)
+    perm = np.random.default_rng(4).permutation(x.shape[1])
+    p = project(x[:, perm], w, H, dk, dv)
+    base = project(x, w, H, dk, dv)
+    for i in range(3):
+        assert np.allclose(p[i], base[i][:, :, perm], atol=1e-14)
+    for i in (3, 4):
+        assert np.allclose(p[i], base[i][:, :, perm], atol=1e-14)
+
+
+def test_projection_head_blocks_map_to_heads():
+    """Swapping two heads' column blocks in w (in every group) swaps those heads
+    in every output."""
+    x, w, H, dk, dv = _rand_proj(5)
+    groups = [(0, dk), (H * dk, dk), (2 * H * dk, dv), (2 * H * dk + H * dv, 1),
+              (2 * H * dk + H * dv + H, 1)]
+    w2 = w.copy()
+    for off, d in groups:
+        a = slice(off, off + d)
+        b = slice(off + 2 * d, off + 3 * d)                          # heads 0 and 2
+        w2[:, a], w2[:, b] = w[:, b], w[:, a]
+    base = project(x, w, H, dk, dv)
+    sw = project(x, w2, H, dk, dv)
+    for i in range(5):
+        assert np.allclose(sw[i][:, 0], base[i][:, 2], atol=1e-14)
+        assert np.allclose(sw[i][:, 2], base[i][:, 0], atol=1e-14)
+        assert np.allclose(sw[i][:, 1], base[i][:, 1], atol=1e-14)
+
