@@ -186,6 +186,29 @@ def long_horizon(hta, dev, steps):
     return res
 
 
+def projection(hta, dev, steps):
+    """The input side (NEXT to the hot path): per-token q, k, v, alpha, beta for the
+    workload's tokens (B2, L = 32760) from model width 2048 (= H x d), one GEMM
+    of 2 * M * Dm * N FLOP with the fused epilogue; its MFMA roofline."""
+    import torch
+    B, L, H, Dm = 2, 32760, 16, 2048
+    N = 3 * H * 128 + 2 * H
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    x = torch.randn(B, L, Dm, generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn(Dm, N, generator=g, device=dev) / Dm ** 0.5).to(torch.bfloat16)
+    q, k, v = (torch.empty(B, H, L, 128, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    al, be = (torch.empty(B, H, L, device=dev) for _ in range(2))
+    stream = torch.cuda.current_stream()
+    ms = timed_events(lambda: hta.hta_project_fwd(x, w, q, k, v, al, be, 1560, stream=stream),
+                      steps, 2, stream)
+    fl = 2.0 * B * L * Dm * N
+    tf = fl / (ms / 1e3) / 1e12
+    return {"kernel": "project_kernel", "workload": "B2 L32760 H16 d128, model width 2048",
+            "avg_launch_ms": round(ms, 4), "flop_per_launch": fl, "achieved_TFLOPs": round(tf, 1),
+            "frac_mfma": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +216,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--stream-steps", type=int, default=64)
     ap.add_argument("--long-horizon-steps", type=int, default=2)
+    ap.add_argument("--project-steps", type=int, default=10)
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU oracle baseline runs (0: skip it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="CALLS",
@@ -284,6 +308,7 @@ def main():
     torch.cuda.empty_cache()
 
     lh = long_horizon(hta, dev, args.long_horizon_steps) if args.long_horizon_steps > 0 else None
+    proj = projection(hta, dev, args.project_steps) if args.project_steps > 0 else None
     cpu = cpu_baseline(w, x, args.cpu_heads) if args.cpu_heads > 0 else None
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -294,7 +319,7 @@ def main():
                                   "SWA W=3, DSWA 4 taps dil 4, GLA chunk 64",
                       "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.dk,
                       "parallelism": "single GPU"},
-           "roofline": roofline, "gla": gla, "stream": sres, "long_horizon": lh,
+           "roofline": roofline, "gla": gla, "stream": sres, "long_horizon": lh, "project": proj,
            "cpu_baseline": cpu}
     print(json.dumps(out))
 

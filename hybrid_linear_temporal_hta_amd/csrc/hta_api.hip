@@ -473,6 +473,42 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void*
     return e == hipSuccess ? HTA_OK : hip_fail(e);
 }
 
+int hta_project_fwd(const hta_shape* s, int d_model, const void* x, const void* w, void* q,
+                    void* k, void* v, float* alpha, float* beta, int flags, void* stream) {
+    if (!s) return HTA_ERR_NULL;
+    hta_shape s1 = *s;
+    s1.out_dtype = s1.dtype;
+    int st;
+    if ((st = check_shape(&s1)) != HTA_OK) return st;
+    if (s->dtype != HTA_BF16 || s->dk != 128 || s->dv != 128) return HTA_ERR_UNSUPPORTED;
+    if (s->H % 4 != 0 || 2 * s->H > 128) return HTA_ERR_UNSUPPORTED;
+    if (d_model < 64 || d_model % 64 != 0) return HTA_ERR_UNSUPPORTED;
+    if (flags & ~(HTA_NORM_Q | HTA_NORM_K)) return HTA_ERR_UNSUPPORTED;
+    if (!x || !w || !q || !k || !v || !alpha || !beta) return HTA_ERR_NULL;
+    const long long L = (long long)s->T * s->P;
+    const long long M = (long long)s->B * L;
+    const long long N = 3LL * s->H * 128 + 2LL * s->H;
+    if ((double)M * d_model >= (double)(1LL << 62)) return HTA_ERR_SHAPE;
+    const long long nmt = (M + 127) / 128;
+    if (nmt * (3LL * s->H + 1) > 0x7fffffffLL) return HTA_ERR_SHAPE;
+    const size_t nseq = seq_bytes(&s1, 128), ngate = gate_bytes(&s1);
+    const Range in[2] = {range_of(x, (size_t)M * d_model * 2), range_of(w, (size_t)d_model * N * 2)};
+    const Range out[5] = {range_of(q, nseq), range_of(k, nseq), range_of(v, nseq),
+                          range_of(alpha, ngate), range_of(beta, ngate)};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (overlap(out[i], in[j])) return HTA_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(out[i], out[j])) return HTA_ERR_ALIAS;
+    }
+    hta::ProjLaunch p;
+    memset(&p, 0, sizeof(p));
+    p.x = x; p.w = w; p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+    p.M = M; p.L = L; p.Dm = d_model; p.N = (int)N; p.H = s->H; p.flags = flags; p.nmt = nmt;
+    hipError_t e = hta::launch_project(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
 static int check_ctx(const hta_stream_ctx* c) {
     if (!c) return HTA_ERR_NULL;
     hta_shape s1 = c->s;

@@ -67,6 +67,22 @@ struct GlaLaunch {
     size_t ws_bytes;
 };
 
+// Per-token projections and gates (bf16 MFMA GEMM + fused epilogue).
+struct ProjLaunch {
+    const void* x;          // [M][Dm] bf16, M = B * L tokens
+    const void* w;          // [Dm][N] bf16, N = 3 * H * 128 + 2 * H
+    void* q;                // [B][H][L][128] bf16
+    void* k;
+    void* v;
+    float* alpha;           // [B][H][L] fp32
+    float* beta;
+    long long M, L;
+    int Dm, N, H;
+    int flags;              // bit 0: L2-normalise q, bit 1: L2-normalise k
+    long long nmt;          // token tiles of 128
+};
+hipError_t launch_project(const ProjLaunch& p, hipStream_t stream);
+
 // Chunked GLA: fp32 (vector ALU) and bf16 (MFMA) paths.
 hipError_t launch_gla_f32(const GlaLaunch& g, hipStream_t stream);
 // bf16 GLA: the chunk-parallel prep kernel, then the sequential scan kernel

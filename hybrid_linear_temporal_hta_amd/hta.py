@@ -35,12 +35,15 @@ HTA_OP_GLA = 1
 HTA_OP_HYBRID = 2
 HTA_OP_STREAM_STEP = 3
 
+HTA_NORM_Q = 1
+HTA_NORM_K = 2
+
 HTA_GLA_GATED_DELTA = 0   # S = alpha (S - beta (S k) k^T) + beta v k^T
 HTA_GLA_PRINTED = 1       # S = alpha S - beta (S k) k^T + beta v k^T
 
 EXPORTED = (
     "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_swa_dswa_fwd", "hta_gla_fwd",
-    "hta_gla_fwd_ex", "hta_hybrid_fwd",
+    "hta_gla_fwd_ex", "hta_hybrid_fwd", "hta_project_fwd",
     "hta_stream_init", "hta_stream_step", "hta_status_string", "hta_last_hip_error",
     "hta_version",
 )
@@ -102,6 +105,8 @@ def lib() -> ctypes.CDLL:
     L.hta_gla_fwd_ex.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.hta_hybrid_fwd.restype = i
     L.hta_hybrid_fwd.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.hta_project_fwd.restype = i
+    L.hta_project_fwd.argtypes = [sp, i, vp, vp, vp, vp, vp, vp, vp, i, vp]
     L.hta_stream_init.restype = i
     L.hta_stream_init.argtypes = [ctypes.POINTER(StreamCtx), vp, vp, i, vp, vp]
     L.hta_stream_step.restype = i
@@ -210,6 +215,17 @@ def hta_gla_fwd_ex(q, k, v, alpha, beta, state, o, P: int, params: Params, works
     _check(lib().hta_gla_fwd_ex(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "hta_gla_fwd_ex")
+
+
+def hta_project_fwd(x, w, q, k, v, alpha, beta, P: int, flags: int = HTA_NORM_Q | HTA_NORM_K,
+                    stream=None):
+    """x [B, L, Dm] bf16, w [Dm, 3*H*128 + 2*H] bf16 -> q, k, v [B, H, L, 128] bf16 and
+    alpha, beta [B, H, L] fp32 (all preallocated)."""
+    B, H, L, d = q.shape
+    s = Shape(B, H, L // P, P, d, v.shape[3], HTA_BF16, HTA_BF16)
+    _check(lib().hta_project_fwd(ctypes.byref(s), int(x.shape[2]), _ptr(x), _ptr(w), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), int(flags),
+                                 _stream(stream)), "hta_project_fwd")
 
 
 def hta_hybrid_fwd(q, k, v, alpha, beta, state, o, P: int, params: Params, workspace=None,

@@ -228,6 +228,29 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
                     const float* alpha, const float* beta, void* o,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * hta_project_fwd -- the input side of the GLA branch (GLA paragraph: q = W_Q x,
+ * k = W_K x, v = W_V x, beta = sigmoid(W_beta x), and a forget gate in (0, 1)
+ * computed from the input, read as alpha = sigmoid(W_alpha x)), for every
+ * token at once, in the layouts the other entry points take.
+ *   shape: B, H, T, P (L = T*P tokens per sequence), dk = dv = 128, dtype
+ *          HTA_BF16 (out_dtype ignored); H a multiple of 4 with 2H <= 128.
+ *   x:     [B][L][d_model] bf16 token features, d_model a multiple of 64.
+ *   w:     [d_model][N] bf16, N = 3*H*128 + 2*H; columns q heads 0..H-1, then k
+ *          heads, v heads, H alpha columns, H beta columns.
+ *   q, k, v: [B][H][L][128] bf16 outputs; alpha, beta: [B][H][L] fp32.
+ *   flags: HTA_NORM_Q and / or HTA_NORM_K L2-normalise q / k per token and
+ *          head (a zero vector stays zero).
+ * fp32 accumulation; each output rounded once. Outputs must not overlap the
+ * inputs or each other. HTA_ERR_UNSUPPORTED for other dtypes, head dims,
+ * head counts or model widths.
+ */
+#define HTA_NORM_Q 1
+#define HTA_NORM_K 2
+int hta_project_fwd(const hta_shape* shape, int d_model, const void* x, const void* w,
+                    void* q, void* k, void* v, float* alpha, float* beta, int flags,
+                    void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* hta_status_string(int status);
 

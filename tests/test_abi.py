@@ -164,3 +164,24 @@ def test_gla_form_validation():
     assert call(0, p=False) == hta.HTA_ERR_NULL
     assert call(hta.HTA_GLA_PRINTED, ws=None) == hta.HTA_ERR_WORKSPACE
 
+
+def test_project_argument_checks():
+    """hta_project_fwd rejects what its kernel does not cover, before any launch."""
+    lib = hta.lib()
+    X, Wt = ctypes.c_void_p(0x90000000), ctypes.c_void_p(0xA0000000)
+    Q, K, V = ctypes.c_void_p(0xB0000000), ctypes.c_void_p(0xC0000000), ctypes.c_void_p(0xD0000000)
+    Al, Be = ctypes.c_void_p(0xE0000000), ctypes.c_void_p(0xF0000000)
+    call = lambda s, dm=256, flags=3, **kw: lib.hta_project_fwd(
+        ctypes.byref(s) if s is not None else None, dm, kw.get("x", X), Wt, kw.get("q", Q), K, V,
+        Al, Be, flags, None)
+    ok = shape(B=1, H=4, T=2, P=16)
+    assert call(None) == hta.HTA_ERR_NULL
+    assert call(ok, x=None) == hta.HTA_ERR_NULL
+    assert call(shape(B=1, H=4, T=2, P=16, dtype=hta.HTA_F32, d=128)) == hta.HTA_ERR_UNSUPPORTED
+    assert call(shape(B=1, H=2, T=2, P=16)) == hta.HTA_ERR_UNSUPPORTED      # H % 4
+    assert call(shape(B=1, H=68, T=2, P=16)) == hta.HTA_ERR_UNSUPPORTED     # 2H > 128
+    assert call(ok, dm=100) == hta.HTA_ERR_UNSUPPORTED                      # d_model % 64
+    assert call(ok, flags=4) == hta.HTA_ERR_UNSUPPORTED
+    assert call(ok, q=K) == hta.HTA_ERR_ALIAS                               # q overlaps k
+    assert call(ok, q=X) == hta.HTA_ERR_ALIAS                               # output on input
+
