@@ -68,6 +68,23 @@ def _load():
             fn = getattr(lib, name)
             fn.restype = i
             fn.argtypes = [i, i, ll, i, i, _dp, _dp, _dp, _dp, _dp, d, _dp, _dp]
+        for name in ("oracle_swa_bwd", "oracle_dswa_bwd"):
+            fn = getattr(lib, name)
+            fn.restype = i
+            fn.argtypes = [i, i, i, i, i, i, _dp, _dp, _dp, _dp] + \
+                ([i, i] if name == "oracle_dswa_bwd" else [i]) + [d, _dp, _dp, _dp]
+        lib.oracle_window_stats.restype = i
+        lib.oracle_window_stats.argtypes = [i, i, i, i, i, i, i, _dp, _dp, _dp, _dp, i, i, d,
+                                            ll, _llp, _dp, _dp]
+        lib.oracle_window_dq_rows.restype = i
+        lib.oracle_window_dq_rows.argtypes = [i, i, i, i, i, i, i, _dp, _dp, _dp, _dp, i, i, d,
+                                              ll, _llp, _dp]
+        lib.oracle_window_dkv_rows.restype = i
+        lib.oracle_window_dkv_rows.argtypes = [i, i, i, i, i, i, i, _dp, _dp, _dp, _dp, _dp, _dp,
+                                               i, i, d, ll, _llp, _dp, _dp]
+        lib.oracle_gla_bwd.restype = i
+        lib.oracle_gla_bwd.argtypes = [i, i, i, ll, i, i, _dp, _dp, _dp, _dp, _dp, d, _dp, _dp,
+                                       _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.oracle_num_threads.restype = i
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -234,3 +251,160 @@ def stream_frame(k_hist, v_hist, q_new, P: int, window: int, taps: int, dilation
     o = swa_rows(None, k_hist, v_hist, T, P, window, flat, attn_scale, qrows=qr) + \
         dswa_rows(None, k_hist, v_hist, T, P, taps, dilation, flat, attn_scale, qrows=qr)
     return o.reshape(B, H, pos.size, dv)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: exact gradients of the definitions above (chain rule written
+# out in oracle.c; pinned by finite differences in the tests).
+# ---------------------------------------------------------------------------
+
+_KIND = {"swa": 0, "dswa": 1}
+
+
+def _window_args(kind: str, window_or_taps: int, dilation: int):
+    if kind not in _KIND:
+        raise ValueError("kind must be 'swa' or 'dswa'")
+    return _KIND[kind], int(window_or_taps), int(dilation if kind == "dswa" else 0)
+
+
+def swa_bwd(q, k, v, dout, T: int, P: int, window: int, scale: float | None = None):
+    """Gradients (dq, dk, dv) of SWA for output gradient dout."""
+    return _window_bwd("swa", q, k, v, dout, T, P, window, 0, scale)
+
+
+def dswa_bwd(q, k, v, dout, T: int, P: int, taps: int, dilation: int,
+             scale: float | None = None):
+    """Gradients (dq, dk, dv) of DSWA for output gradient dout."""
+    return _window_bwd("dswa", q, k, v, dout, T, P, taps, dilation, scale)
+
+
+def _window_bwd(kind, q, k, v, dout, T, P, a, b, scale):
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, L, dk, dv = _dims(q, k, v)
+    if L != T * P or dout.shape != v.shape:
+        raise ValueError("L must equal T*P and dout match v")
+    s = default_scale(dk) if not scale else float(scale)
+    dq, dkk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    lib = _load()
+    if kind == "swa":
+        st = lib.oracle_swa_bwd(B, H, T, P, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                int(a), s, _ptr(dq), _ptr(dkk), _ptr(dvv))
+    else:
+        st = lib.oracle_dswa_bwd(B, H, T, P, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                 int(a), int(b), s, _ptr(dq), _ptr(dkk), _ptr(dvv))
+    _check(st, f"oracle_{kind}_bwd")
+    return dq, dkk, dvv
+
+
+def window_stats(kind: str, q, k, v, dout, T: int, P: int, window_or_taps: int,
+                 dilation: int, rows, scale: float | None = None):
+    """Per-row softmax statistics for the listed flat query rows (bh*L + t):
+    (lse, D) with lse the log-sum-exp of the scaled logits over the row's
+    window and D = dout_t . o_t."""
+    kd, a, b = _window_args(kind, window_or_taps, dilation)
+    k, v = _f64(k), _f64(v)
+    B, H, L, dk = k.shape
+    dv = v.shape[3]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    qr = np.ascontiguousarray(_f64(q).reshape(-1, dk)[rows])
+    dr = np.ascontiguousarray(_f64(dout).reshape(-1, dv)[rows])
+    lse, D = np.empty(rows.size), np.empty(rows.size)
+    s = default_scale(dk) if not scale else float(scale)
+    _check(_load().oracle_window_stats(kd, B, H, T, P, dk, dv, _ptr(qr), _ptr(dr), _ptr(k),
+                                       _ptr(v), a, b, s, rows.size, rows.ctypes.data_as(_llp),
+                                       _ptr(lse), _ptr(D)), "oracle_window_stats")
+    return lse, D
+
+
+def window_dq_rows(kind: str, q, k, v, dout, T: int, P: int, window_or_taps: int,
+                   dilation: int, rows, scale: float | None = None):
+    """dq of SWA/DSWA for the listed flat query rows; returns [n, dk]."""
+    kd, a, b = _window_args(kind, window_or_taps, dilation)
+    k, v = _f64(k), _f64(v)
+    B, H, L, dk = k.shape
+    dv = v.shape[3]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    qr = np.ascontiguousarray(_f64(q).reshape(-1, dk)[rows])
+    dr = np.ascontiguousarray(_f64(dout).reshape(-1, dv)[rows])
+    out = np.empty((rows.size, dk))
+    s = default_scale(dk) if not scale else float(scale)
+    _check(_load().oracle_window_dq_rows(kd, B, H, T, P, dk, dv, _ptr(qr), _ptr(dr), _ptr(k),
+                                         _ptr(v), a, b, s, rows.size,
+                                         rows.ctypes.data_as(_llp), _ptr(out)),
+           "oracle_window_dq_rows")
+    return out
+
+
+def window_dkv_rows(kind: str, q, k, v, dout, T: int, P: int, window_or_taps: int,
+                    dilation: int, rows, scale: float | None = None):
+    """dk, dv of SWA/DSWA for the listed flat key rows ([n, dk], [n, dv]).
+
+    The statistics are computed only for the queries that attend to those
+    rows (query frames f_k + j * step of each key frame f_k)."""
+    kd, a, b = _window_args(kind, window_or_taps, dilation)
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, L, dk, dv = _dims(q, k, v)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    step = 1 if kind == "swa" else b
+    need = set()
+    for r in rows.tolist():
+        bh, kf = divmod(r, L)[0], (r % L) // P
+        for j in range(a):
+            fq = kf + j * step
+            if fq >= T:
+                break
+            need.add((bh, fq))
+    qrows = np.array(sorted(bh * L + fq * P + p for bh, fq in need for p in range(P)),
+                     dtype=np.int64)
+    lse_full, D_full = np.zeros(B * H * L), np.zeros(B * H * L)
+    if qrows.size:
+        lse, D = window_stats(kind, q, k, v, dout, T, P, a, b, qrows, scale)
+        lse_full[qrows], D_full[qrows] = lse, D
+    dko, dvo = np.empty((rows.size, dk)), np.empty((rows.size, dv))
+    s = default_scale(dk) if not scale else float(scale)
+    _check(_load().oracle_window_dkv_rows(kd, B, H, T, P, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(dout), _ptr(lse_full), _ptr(D_full), a, b, s,
+                                          rows.size, rows.ctypes.data_as(_llp), _ptr(dko),
+                                          _ptr(dvo)), "oracle_window_dkv_rows")
+    return dko, dvo
+
+
+def gla_bwd(q, k, v, alpha, beta, dout, state0=None, dstate_final=None,
+            scale: float = 1.0, form: int = 0):
+    """Gradients of the GLA recurrence (form 0: GatedDeltaNet reading, 1: the
+    printed update) for output gradient dout and, optionally, a gradient of the
+    final state (dL/dM_L, [B,H,dk,dv]).
+
+    Returns dict(dq, dk, dv, dalpha, dbeta, dstate0) with dstate0 = dL/dM_0.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, L, dk, dv = _dims(q, k, v)
+    alpha, beta = _f64(alpha), _f64(beta)
+    if alpha.shape != (B, H, L) or beta.shape != (B, H, L) or dout.shape != v.shape:
+        raise ValueError("alpha, beta must be [B, H, L] and dout match v")
+    s0 = np.zeros((B, H, dk, dv)) if state0 is None else _f64(state0)
+    dsf = None if dstate_final is None else _f64(dstate_final)
+    if s0.shape != (B, H, dk, dv) or (dsf is not None and dsf.shape != s0.shape):
+        raise ValueError("states must be [B, H, dk, dv]")
+    out = dict(dq=np.empty_like(q), dk=np.empty_like(k), dv=np.empty_like(v),
+               dalpha=np.empty_like(alpha), dbeta=np.empty_like(beta),
+               dstate0=np.empty_like(s0))
+    _check(_load().oracle_gla_bwd(int(form), B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(alpha), _ptr(beta), float(scale), _ptr(s0), _ptr(dout),
+                                  _ptr(dsf) if dsf is not None else None,
+                                  _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                  _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dstate0"])),
+           "oracle_gla_bwd")
+    return out
+
+
+def hybrid_bwd(q, k, v, alpha, beta, dout, T: int, P: int, window: int, taps: int,
+               dilation: int, state0=None, dstate_final=None, attn_scale: float | None = None,
+               gla_scale: float = 1.0, form: int = 0):
+    """Gradients of the hybrid sum: each branch's gradient for the shared
+    output gradient, summed over branches for q, k, v."""
+    s = swa_bwd(q, k, v, dout, T, P, window, attn_scale)
+    d = dswa_bwd(q, k, v, dout, T, P, taps, dilation, attn_scale)
+    g = gla_bwd(q, k, v, alpha, beta, dout, state0, dstate_final, gla_scale, form)
+    return dict(dq=s[0] + d[0] + g["dq"], dk=s[1] + d[1] + g["dk"], dv=s[2] + d[2] + g["dv"],
+                dalpha=g["dalpha"], dbeta=g["dbeta"], dstate0=g["dstate0"])

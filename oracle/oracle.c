@@ -279,3 +279,396 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass: the exact gradient of the forward definitions above.       */
+/*                                                                          */
+/* The pages train the model built from these layers (the curriculum over    */
+/* 81- and 241-frame clips in [P1] section 二、方法), so each layer also needs  */
+/* its vector-Jacobian product: given dO = dL/dO, return dL/dq, dL/dk, dL/dv  */
+/* (and, for GLA, dL/dalpha, dL/dbeta and dL/dS_0). Nothing here is taken     */
+/* from the pages beyond the forward definitions; the rules are the chain     */
+/* rule written out.                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Softmax statistics of one query row over its window: log-sum-exp of the
+ * scaled logits, and D = dO_t . o_t (the row's output dotted with its output
+ * gradient). Used by the backward rules
+ *   p_s  = exp(z_s - lse),  dp_s = dO_t . v_s,  ds_s = p_s (dp_s - D),
+ *   dq_t = scale sum_s ds_s k_s,  dk_s += scale ds_s q_t,  dv_s += p_s dO_t.
+ */
+static int row_stats(const double *qrow, const double *dorow, const double *kbh,
+                     const double *vbh, int P, int dk, int dv, const int *frames, int nf,
+                     double scale, double *lse_out, double *D_out)
+{
+    double *o = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!o) return ORC_ENOMEM;
+    int st = attend_frames(qrow, kbh, vbh, P, dk, dv, frames, nf, scale, o);
+    if (st == ORC_OK) {
+        double m = -INFINITY;
+        for (int a = 0; a < nf; ++a)
+            for (int p = 0; p < P; ++p) {
+                const double *kr = kbh + ((long)frames[a] * P + p) * dk;
+                double s = 0.0;
+                for (int i = 0; i < dk; ++i) s += qrow[i] * kr[i];
+                s *= scale;
+                if (s > m) m = s;
+            }
+        double den = 0.0;
+        for (int a = 0; a < nf; ++a)
+            for (int p = 0; p < P; ++p) {
+                const double *kr = kbh + ((long)frames[a] * P + p) * dk;
+                double s = 0.0;
+                for (int i = 0; i < dk; ++i) s += qrow[i] * kr[i];
+                den += exp(s * scale - m);
+            }
+        *lse_out = m + log(den);
+        double D = 0.0;
+        for (int j = 0; j < dv; ++j) D += dorow[j] * o[j];
+        *D_out = D;
+    }
+    free(o);
+    return st;
+}
+
+static int window_frames(int kind, int f, int a, int b, int *frames)
+{
+    return (kind == 0) ? swa_frames(f, a, frames) : dswa_frames(f, a, b, frames);
+}
+
+/*
+ * Full backward of SWA (kind 0, a = window) or DSWA (kind 1, a = taps,
+ * b = dilation) over every token. Parallel over (batch, head); inside one
+ * slice the query rows run in order and scatter into dk, dv.
+ */
+static int window_bwd(int kind, int B, int H, int T, int P, int dk, int dv,
+                      const double *q, const double *k, const double *v, const double *dout,
+                      int a, int b, double scale, double *dq, double *dkk, double *dvv)
+{
+    if (B < 1 || H < 1 || T < 1 || P < 1 || dk < 1 || dv < 1 || a < 1) return ORC_EARG;
+    if (kind == 1 && b < 1) return ORC_EARG;
+    const long long L = (long long)T * P;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < (long long)B * H; ++bh) {
+        const double *qb = q + bh * L * dk, *kb = k + bh * L * dk, *vb = v + bh * L * dv;
+        const double *dob = dout + bh * L * dv;
+        double *dqb = dq + bh * L * dk, *dkb = dkk + bh * L * dk, *dvb = dvv + bh * L * dv;
+        int *frames = (int *)malloc(sizeof(int) * (size_t)a);
+        if (!frames) { status = ORC_ENOMEM; continue; }
+        for (long long e = 0; e < L * dk; ++e) { dqb[e] = 0.0; dkb[e] = 0.0; }
+        for (long long e = 0; e < L * dv; ++e) dvb[e] = 0.0;
+        for (long long t = 0; t < L; ++t) {
+            const double *qt = qb + t * dk, *dot = dob + t * dv;
+            int nf = window_frames(kind, (int)(t / P), a, b, frames);
+            double lse, D;
+            int st = row_stats(qt, dot, kb, vb, P, dk, dv, frames, nf, scale, &lse, &D);
+            if (st != ORC_OK) { status = st; break; }
+            for (int f = 0; f < nf; ++f)
+                for (int p = 0; p < P; ++p) {
+                    long long s = (long long)frames[f] * P + p;
+                    const double *ks = kb + s * dk, *vs = vb + s * dv;
+                    double z = 0.0, dp = 0.0;
+                    for (int i = 0; i < dk; ++i) z += qt[i] * ks[i];
+                    for (int j = 0; j < dv; ++j) dp += dot[j] * vs[j];
+                    double pr = exp(z * scale - lse);
+                    double ds = pr * (dp - D);
+                    for (int i = 0; i < dk; ++i) {
+                        dqb[t * dk + i] += scale * ds * ks[i];
+                        dkb[s * dk + i] += scale * ds * qt[i];
+                    }
+                    for (int j = 0; j < dv; ++j) dvb[s * dv + j] += pr * dot[j];
+                }
+        }
+        free(frames);
+    }
+    return status;
+}
+
+int oracle_swa_bwd(int B, int H, int T, int P, int dk, int dv,
+                   const double *q, const double *k, const double *v, const double *dout,
+                   int window, double scale, double *dq, double *dkk, double *dvv)
+{
+    return window_bwd(0, B, H, T, P, dk, dv, q, k, v, dout, window, 0, scale, dq, dkk, dvv);
+}
+
+int oracle_dswa_bwd(int B, int H, int T, int P, int dk, int dv,
+                    const double *q, const double *k, const double *v, const double *dout,
+                    int taps, int dilation, double scale, double *dq, double *dkk, double *dvv)
+{
+    return window_bwd(1, B, H, T, P, dk, dv, q, k, v, dout, taps, dilation, scale, dq, dkk, dvv);
+}
+
+/*
+ * Per-row statistics (lse, D) for listed flat query rows; the query and
+ * output-gradient vectors of those rows are passed compactly ([n][dk], [n][dv]).
+ */
+int oracle_window_stats(int kind, int B, int H, int T, int P, int dk, int dv,
+                        const double *qrows, const double *dorows,
+                        const double *k, const double *v, int a, int b, double scale,
+                        long long n_rows, const long long *rows, double *lse, double *D)
+{
+    if (B < 1 || H < 1 || T < 1 || P < 1 || dk < 1 || dv < 1 || a < 1) return ORC_EARG;
+    if (kind == 1 && b < 1) return ORC_EARG;
+    const long long L = (long long)T * P, total = (long long)B * H * L;
+    for (long long r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= total) return ORC_EARG;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long long r = 0; r < n_rows; ++r) {
+        long long bh = rows[r] / L, t = rows[r] % L;
+        int *frames = (int *)malloc(sizeof(int) * (size_t)a);
+        if (!frames) { status = ORC_ENOMEM; continue; }
+        int nf = window_frames(kind, (int)(t / P), a, b, frames);
+        int st = row_stats(qrows + r * dk, dorows + r * dv, k + bh * L * dk, v + bh * L * dv,
+                           P, dk, dv, frames, nf, scale, lse + r, D + r);
+        if (st != ORC_OK) status = st;
+        free(frames);
+    }
+    return status;
+}
+
+/*
+ * dq for listed flat query rows (row-local: the row's whole window).
+ * qrows, dorows: [n][dk], [n][dv]; dq_out: [n][dk].
+ */
+int oracle_window_dq_rows(int kind, int B, int H, int T, int P, int dk, int dv,
+                          const double *qrows, const double *dorows,
+                          const double *k, const double *v, int a, int b, double scale,
+                          long long n_rows, const long long *rows, double *dq_out)
+{
+    if (B < 1 || H < 1 || T < 1 || P < 1 || dk < 1 || dv < 1 || a < 1) return ORC_EARG;
+    if (kind == 1 && b < 1) return ORC_EARG;
+    const long long L = (long long)T * P, total = (long long)B * H * L;
+    for (long long r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= total) return ORC_EARG;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long long r = 0; r < n_rows; ++r) {
+        long long bh = rows[r] / L, t = rows[r] % L;
+        const double *kb = k + bh * L * dk, *vb = v + bh * L * dv;
+        const double *qt = qrows + r * dk, *dot = dorows + r * dv;
+        double *dqt = dq_out + r * dk;
+        int *frames = (int *)malloc(sizeof(int) * (size_t)a);
+        if (!frames) { status = ORC_ENOMEM; continue; }
+        int nf = window_frames(kind, (int)(t / P), a, b, frames);
+        double lse, D;
+        int st = row_stats(qt, dot, kb, vb, P, dk, dv, frames, nf, scale, &lse, &D);
+        for (int i = 0; i < dk; ++i) dqt[i] = 0.0;
+        if (st != ORC_OK) { status = st; free(frames); continue; }
+        for (int f = 0; f < nf; ++f)
+            for (int p = 0; p < P; ++p) {
+                long long s = (long long)frames[f] * P + p;
+                const double *ks = kb + s * dk, *vs = vb + s * dv;
+                double z = 0.0, dp = 0.0;
+                for (int i = 0; i < dk; ++i) z += qt[i] * ks[i];
+                for (int j = 0; j < dv; ++j) dp += dot[j] * vs[j];
+                double ds = exp(z * scale - lse) * (dp - D);
+                for (int i = 0; i < dk; ++i) dqt[i] += scale * ds * ks[i];
+            }
+        free(frames);
+    }
+    return status;
+}
+
+/*
+ * dk, dv for listed flat key rows: sum over every query whose window holds the
+ * key's frame. lse and D are per-row statistics laid out [B*H*L]; only the
+ * entries of those queries are read. dk_out: [n][dk], dv_out: [n][dv].
+ */
+int oracle_window_dkv_rows(int kind, int B, int H, int T, int P, int dk, int dv,
+                           const double *q, const double *k, const double *v,
+                           const double *dout, const double *lse, const double *D,
+                           int a, int b, double scale, long long n_rows,
+                           const long long *rows, double *dk_out, double *dv_out)
+{
+    if (B < 1 || H < 1 || T < 1 || P < 1 || dk < 1 || dv < 1 || a < 1) return ORC_EARG;
+    if (kind == 1 && b < 1) return ORC_EARG;
+    const long long L = (long long)T * P, total = (long long)B * H * L;
+    for (long long r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= total) return ORC_EARG;
+    const int step = (kind == 0) ? 1 : b;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long long r = 0; r < n_rows; ++r) {
+        long long bh = rows[r] / L, s = rows[r] % L;
+        int kf = (int)(s / P);
+        const double *ks = k + rows[r] * dk, *vs = v + rows[r] * dv;
+        double *dks = dk_out + r * dk, *dvs = dv_out + r * dv;
+        for (int i = 0; i < dk; ++i) dks[i] = 0.0;
+        for (int j = 0; j < dv; ++j) dvs[j] = 0.0;
+        /* query frames whose window holds frame kf: kf + j*step, j < a */
+        for (int j = 0; j < a; ++j) {
+            long long fq = (long long)kf + (long long)j * step;
+            if (fq >= T) break;
+            for (int p = 0; p < P; ++p) {
+                long long t = bh * L + fq * P + p;
+                const double *qt = q + t * dk, *dot = dout + t * dv;
+                double z = 0.0, dp = 0.0;
+                for (int i = 0; i < dk; ++i) z += qt[i] * ks[i];
+                for (int jj = 0; jj < dv; ++jj) dp += dot[jj] * vs[jj];
+                double pr = exp(z * scale - lse[t]);
+                double ds = pr * (dp - D[t]);
+                for (int i = 0; i < dk; ++i) dks[i] += scale * ds * qt[i];
+                for (int jj = 0; jj < dv; ++jj) dvs[jj] += pr * dot[jj];
+            }
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * GLA backward, token by token in reverse (form 0: GatedDeltaNet reading,
+ * form 1: the printed update). With M = S^T (dk x dv) and u = M_{t-1}^T k_t:
+ *   form 0:  M_t = alpha M_{t-1} - alpha beta k u^T + beta k v^T
+ *   form 1:  M_t = alpha M_{t-1} -       beta k u^T + beta k v^T
+ *   o_t = scale M_t^T q_t.
+ * G holds dL/dM_t while walking t = L-1 .. 0:
+ *   G += scale q_t dO_t^T;  dq_t = scale M_t dO_t;  w = G^T k_t
+ *   dv_t = beta w
+ *   form 0: dalpha = <G, M_{t-1} - beta k u^T>, dbeta = w.(v - alpha u),
+ *           du = -alpha beta w, dk_t = beta G (v - alpha u) + M_{t-1} du
+ *   form 1: dalpha = <G, M_{t-1}>, dbeta = w.(v - u),
+ *           du = -beta w, dk_t = beta G (v - u) + M_{t-1} du
+ *   G <- alpha G + k du^T   (dL/dM_{t-1})
+ * dstate_final (dL/dM_L, may be NULL = 0) seeds G; dstate0 receives dL/dM_0.
+ * The forward states are recomputed from checkpoints every `ck` tokens.
+ */
+static int gla_bwd_run(int form, int B, int H, long long L, int dk, int dv,
+                       const double *q, const double *k, const double *v,
+                       const double *alpha, const double *beta, double scale,
+                       const double *state0, const double *dout, const double *dstate_final,
+                       double *dq, double *dkk, double *dvv, double *dalpha, double *dbeta,
+                       double *dstate0)
+{
+    if (B < 1 || H < 1 || L < 0 || dk < 1 || dv < 1) return ORC_EARG;
+    const long long ck = 64;
+    const long long nck = (L + ck - 1) / ck;
+    const long long DD = (long long)dk * dv;
+    int status = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long bh = 0; bh < (long long)B * H; ++bh) {
+        double *cks = (double *)malloc(sizeof(double) * (size_t)((nck + 1) * DD));
+        double *seg = (double *)malloc(sizeof(double) * (size_t)((ck + 1) * DD));
+        double *G = (double *)malloc(sizeof(double) * (size_t)DD);
+        double *u = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *w = (double *)malloc(sizeof(double) * (size_t)dv);
+        double *du = (double *)malloc(sizeof(double) * (size_t)dv);
+        if (!cks || !seg || !G || !u || !w || !du) {
+            status = ORC_ENOMEM;
+            free(cks); free(seg); free(G); free(u); free(w); free(du);
+            continue;
+        }
+        const double *qb = q + bh * L * dk, *kb = k + bh * L * dk, *vb = v + bh * L * dv;
+        const double *ab = alpha + bh * L, *bb = beta + bh * L, *dob = dout + bh * L * dv;
+        /* forward pass, keeping M at every checkpoint (M_0, M_ck, ...) */
+        memcpy(cks, state0 + bh * DD, sizeof(double) * (size_t)DD);
+        double *M = seg;
+        memcpy(M, cks, sizeof(double) * (size_t)DD);
+        for (long long t = 0; t < L; ++t) {
+            const double *kt = kb + t * dk, *vt = vb + t * dv;
+            const double a = ab[t], be = bb[t];
+            for (int j = 0; j < dv; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < dk; ++i) s += M[(long)i * dv + j] * kt[i];
+                u[j] = s;
+            }
+            const double ea = (form == 0) ? a * be : be;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j)
+                    M[(long)i * dv + j] = a * M[(long)i * dv + j] - ea * kt[i] * u[j]
+                                          + be * kt[i] * vt[j];
+            if ((t + 1) % ck == 0 && (t + 1) / ck <= nck)
+                memcpy(cks + ((t + 1) / ck) * DD, M, sizeof(double) * (size_t)DD);
+        }
+        /* reverse pass */
+        for (long long e = 0; e < DD; ++e)
+            G[e] = dstate_final ? dstate_final[bh * DD + e] : 0.0;
+        for (long long c = nck - 1; c >= 0; --c) {
+            const long long t0 = c * ck, t1 = (t0 + ck < L) ? t0 + ck : L;
+            /* recompute M_{t0} .. M_{t1} of this segment into seg[0 .. t1-t0] */
+            memcpy(seg, cks + c * DD, sizeof(double) * (size_t)DD);
+            for (long long t = t0; t < t1; ++t) {
+                const double *Mp = seg + (t - t0) * DD;
+                double *Mn = seg + (t - t0 + 1) * DD;
+                const double *kt = kb + t * dk, *vt = vb + t * dv;
+                const double a = ab[t], be = bb[t];
+                for (int j = 0; j < dv; ++j) {
+                    double s = 0.0;
+                    for (int i = 0; i < dk; ++i) s += Mp[(long)i * dv + j] * kt[i];
+                    u[j] = s;
+                }
+                const double ea = (form == 0) ? a * be : be;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        Mn[(long)i * dv + j] = a * Mp[(long)i * dv + j] - ea * kt[i] * u[j]
+                                               + be * kt[i] * vt[j];
+            }
+            for (long long t = t1 - 1; t >= t0; --t) {
+                const double *Mp = seg + (t - t0) * DD;      /* M_{t-1} */
+                const double *Mt = seg + (t - t0 + 1) * DD;  /* M_t */
+                const double *qt = qb + t * dk, *kt = kb + t * dk, *vt = vb + t * dv;
+                const double *dot = dob + t * dv;
+                const double a = ab[t], be = bb[t];
+                double *dqt = dq + (bh * L + t) * dk, *dkt = dkk + (bh * L + t) * dk;
+                double *dvt = dvv + (bh * L + t) * dv;
+                for (int i = 0; i < dk; ++i) {
+                    double s = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        G[(long)i * dv + j] += scale * qt[i] * dot[j];
+                        s += Mt[(long)i * dv + j] * dot[j];
+                    }
+                    dqt[i] = scale * s;
+                }
+                for (int j = 0; j < dv; ++j) {
+                    double s = 0.0, s2 = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        s += G[(long)i * dv + j] * kt[i];
+                        s2 += Mp[(long)i * dv + j] * kt[i];
+                    }
+                    w[j] = s;
+                    u[j] = s2;
+                }
+                const double ua = (form == 0) ? a : 1.0;   /* u enters as ua * u */
+                double da = 0.0, db = 0.0;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) {
+                        double erase = (form == 0) ? be * kt[i] * u[j] : 0.0;
+                        da += G[(long)i * dv + j] * (Mp[(long)i * dv + j] - erase);
+                    }
+                for (int j = 0; j < dv; ++j) {
+                    db += w[j] * (vt[j] - ua * u[j]);
+                    dvt[j] = be * w[j];
+                    du[j] = -ua * be * w[j];
+                }
+                for (int i = 0; i < dk; ++i) {
+                    double s = 0.0;
+                    for (int j = 0; j < dv; ++j)
+                        s += G[(long)i * dv + j] * be * (vt[j] - ua * u[j])
+                             + Mp[(long)i * dv + j] * du[j];
+                    dkt[i] = s;
+                }
+                dalpha[bh * L + t] = da;
+                dbeta[bh * L + t] = db;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        G[(long)i * dv + j] = a * G[(long)i * dv + j] + kt[i] * du[j];
+            }
+        }
+        memcpy(dstate0 + bh * DD, G, sizeof(double) * (size_t)DD);
+        free(cks); free(seg); free(G); free(u); free(w); free(du);
+    }
+    return status;
+}
+
+int oracle_gla_bwd(int form, int B, int H, long long L, int dk, int dv,
+                   const double *q, const double *k, const double *v,
+                   const double *alpha, const double *beta, double scale,
+                   const double *state0, const double *dout, const double *dstate_final,
+                   double *dq, double *dkk, double *dvv, double *dalpha, double *dbeta,
+                   double *dstate0)
+{
+    if (form != 0 && form != 1) return ORC_EARG;
+    return gla_bwd_run(form, B, H, L, dk, dv, q, k, v, alpha, beta, scale, state0, dout,
+                       dstate_final, dq, dkk, dvv, dalpha, dbeta, dstate0);
+}
