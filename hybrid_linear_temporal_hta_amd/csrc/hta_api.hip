@@ -288,6 +288,59 @@ hipError_t run_hybrid_overlapped(const hta::GlaLaunch& g, const hta::WinLaunch& 
     return hta::launch_win_attn(dw, sm);
 }
 
+// Backward of one attention branch. Workspace: per-row stats {lse log2(e), D}
+// with 64 rows of padding (the key pass stages 64-row tiles of it), then, for
+// bf16 inputs with an fp32 dout, dout rounded to bf16.
+size_t attn_bwd_stats_bytes(const hta_shape* s) {
+    return align_up(((size_t)s->B * s->H * (size_t)s->T * s->P + 64) * 8);
+}
+size_t attn_bwd_ws(const hta_shape* s) {
+    size_t n = attn_bwd_stats_bytes(s);
+    if (s->dtype == HTA_BF16 && s->out_dtype == HTA_F32)
+        n += align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 2);
+    return n;
+}
+
+hta::BwdLaunch bwd_base(const hta_shape* s, const void* q, const void* k, const void* v, void* dq,
+                        void* dk, void* dv, float scale, const hta::WinTaps& t) {
+    hta::BwdLaunch b;
+    memset(&b, 0, sizeof(b));
+    b.q = q; b.k = k; b.v = v; b.dq = dq; b.dk = dk; b.dv = dv;
+    b.out_f32 = s->dtype == HTA_F32 ? 1 : 0;
+    b.bh_elems = (long long)s->T * s->P * s->dk;
+    b.BH = s->B * s->H;
+    b.P = s->P;
+    b.T = s->T;
+    b.d = s->dk;
+    b.dtype = s->dtype;
+    b.scale = attn_scale_of(scale, s->dk);
+    b.ntaps = t.nA;
+    for (int j = 0; j < t.nA; ++j) b.off[j] = t.offA[j];
+    return b;
+}
+
+// prep (stats, and dout in bf16 if needed) into ws, then the query and key passes.
+hipError_t run_window_bwd(const hta_shape* s, hta::BwdLaunch b, const void* o, const float* lse,
+                          const void* dout, void* ws, hipStream_t st) {
+    char* w = static_cast<char*>(ws);
+    hta::BwdPrep p;
+    memset(&p, 0, sizeof(p));
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.stats = reinterpret_cast<float*>(w);
+    p.rows = (long long)s->B * s->H * s->T * s->P;
+    p.d = s->dv;
+    p.o_f32 = p.do_f32 = s->out_dtype == HTA_F32 ? 1 : 0;
+    p.round_do = s->dtype == HTA_BF16 ? 1 : 0;
+    if (s->dtype == HTA_BF16 && s->out_dtype == HTA_F32) p.dout_bf16 = w + attn_bwd_stats_bytes(s);
+    hipError_t e = hta::launch_win_bwd_prep(p, st);
+    if (e != hipSuccess) return e;
+    b.stats = p.stats;
+    b.dout = p.dout_bf16 ? p.dout_bf16 : dout;
+    return hta::launch_win_bwd(b, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,6 +371,7 @@ size_t hta_workspace_bytes(int op, const hta_shape* shape, const hta_params* par
         if (!params || check_chunk(shape->dtype, params->gla_chunk) != HTA_OK) return 0;
         return gla_ws(shape, params->gla_chunk);
     }
+    if (op == HTA_OP_ATTN_BWD) return attn_bwd_ws(shape);
     if (op == HTA_OP_HYBRID || op == HTA_OP_STREAM_STEP) {
         if (check_params(shape, params) != HTA_OK) return 0;
         if (op == HTA_OP_STREAM_STEP && shape->T != 1) return 0;
@@ -353,6 +407,87 @@ int hta_swa_fwd(const hta_shape* shape, const void* q, const void* k, const void
 int hta_dswa_fwd(const hta_shape* shape, const void* q, const void* k, const void* v, void* o,
                  int taps, int dilation_frames, float scale, void* stream) {
     return window_fwd(1, shape, q, k, v, o, taps, dilation_frames, scale, stream);
+}
+
+static int window_fwd_lse(int kind, const hta_shape* s, const void* q, const void* k,
+                          const void* v, void* o, float* lse, int a, int b, float scale,
+                          void* stream) {
+    int st;
+    if ((st = check_shape(s)) != HTA_OK) return st;
+    if (!q || !k || !v || !o || !lse) return HTA_ERR_NULL;
+    if ((st = (kind == 0 ? check_window(a) : check_dilated(a, b))) != HTA_OK) return st;
+    if ((st = check_scale(scale)) != HTA_OK) return st;
+    const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
+    const Range in[3] = {range_of(q, nq), range_of(k, nq), range_of(v, nv)};
+    const Range ro = range_of(o, out_bytes(s)), rl = range_of(lse, gate_bytes(s));
+    for (int j = 0; j < 3; ++j)
+        if (overlap(ro, in[j]) || overlap(rl, in[j])) return HTA_ERR_ALIAS;
+    if (overlap(ro, rl)) return HTA_ERR_ALIAS;
+    hta::WinLaunch w = win_base(s, q, k, v, o, scale);
+    w.nbr = 1;
+    w.lse = lse;
+    if (kind == 0) taps_swa(w.taps, a);
+    else taps_dswa(w.taps, a, b);
+    hipError_t e = hta::launch_win_attn(w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+int hta_swa_fwd_lse(const hta_shape* shape, const void* q, const void* k, const void* v, void* o,
+                    float* lse, int window_frames, float scale, void* stream) {
+    return window_fwd_lse(0, shape, q, k, v, o, lse, window_frames, 0, scale, stream);
+}
+
+int hta_dswa_fwd_lse(const hta_shape* shape, const void* q, const void* k, const void* v,
+                     void* o, float* lse, int taps, int dilation_frames, float scale,
+                     void* stream) {
+    return window_fwd_lse(1, shape, q, k, v, o, lse, taps, dilation_frames, scale, stream);
+}
+
+static int window_bwd(int kind, const hta_shape* s, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                      void* dv, int a, int b, float scale, void* ws, size_t ws_bytes,
+                      void* stream) {
+    int st;
+    if ((st = check_shape(s)) != HTA_OK) return st;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return HTA_ERR_NULL;
+    if ((st = (kind == 0 ? check_window(a) : check_dilated(a, b))) != HTA_OK) return st;
+    if ((st = check_scale(scale)) != HTA_OK) return st;
+    const size_t need = attn_bwd_ws(s);
+    if (!ws || ws_bytes < need) return HTA_ERR_WORKSPACE;
+    const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
+    const Range in[6] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                         range_of(o, out_bytes(s)), range_of(lse, gate_bytes(s)),
+                         range_of(dout, out_bytes(s))};
+    const Range outs[4] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv),
+                           range_of(ws, need)};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], in[j])) return HTA_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return HTA_ERR_ALIAS;
+    }
+    hta::WinTaps t;
+    if (kind == 0) taps_swa(t, a);
+    else taps_dswa(t, a, b);
+    hta::BwdLaunch bl = bwd_base(s, q, k, v, dq, dk, dv, scale, t);
+    hipError_t e = run_window_bwd(s, bl, o, lse, dout, ws, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+int hta_swa_bwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                int window_frames, float scale, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    return window_bwd(0, shape, q, k, v, o, lse, dout, dq, dk, dv, window_frames, 0, scale,
+                      workspace, workspace_bytes, stream);
+}
+
+int hta_dswa_bwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 int taps, int dilation_frames, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    return window_bwd(1, shape, q, k, v, o, lse, dout, dq, dk, dv, taps, dilation_frames, scale,
+                      workspace, workspace_bytes, stream);
 }
 
 int hta_swa_dswa_fwd(const hta_shape* s, const hta_params* p, const void* q, const void* k,

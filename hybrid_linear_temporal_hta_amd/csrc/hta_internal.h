@@ -40,9 +40,48 @@ struct WinLaunch {
     int out_f32;            // 1: o is fp32, 0: o is bf16
     int nbr;                // 1 or 2 branches
     WinTaps taps;
+    float* lse;             // optional [BH][Tq*P]: log-sum-exp of the scaled logits (one branch)
 };
 
 hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream);
+
+// Backward of one windowed-attention branch over a whole sequence (no ring).
+// Per-row statistics {lse * log2(e), D = dO . o} come first (launch_win_bwd_prep),
+// then the query pass (dq) and the key pass (dk, dv).
+struct BwdPrep {
+    const void* o;          // branch output [rows][d], fp32 or bf16
+    const void* dout;       // dL/do [rows][d], fp32 or bf16
+    const float* lse;       // [rows]
+    float* stats;           // out: [rows][2] = {lse * log2(e), D}
+    void* dout_bf16;        // optional out: dout rounded to bf16 (fp32 dout, bf16 inputs)
+    long long rows;
+    int d;
+    int o_f32, do_f32;
+    int round_do;           // D from the bf16-rounded dout (what the bf16 kernels multiply)
+};
+hipError_t launch_win_bwd_prep(const BwdPrep& p, hipStream_t stream);
+
+struct BwdLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;       // dtype of q (bf16 dout for bf16 inputs)
+    const float* stats;     // [BH][L][2] from the prep, 64 rows of padding after the end
+    void* dq;
+    void* dk;
+    void* dv;
+    const float* add_q;     // optional fp32 partials [BH][L][d] added before the store
+    const float* add_k;
+    const float* add_v;
+    int out_f32;            // gradients written as fp32 (1) or bf16 (0)
+    long long bh_elems;     // elements between (b,h) slices (L*d)
+    int BH, P, T, d, dtype;
+    float scale;
+    int ntaps;
+    int off[kMaxTaps];      // ascending frame offsets: query frame f reads key frames f - off[j]
+};
+constexpr int kBwdQuery = 1, kBwdKey = 2;
+hipError_t launch_win_bwd(const BwdLaunch& b, hipStream_t stream, int parts = kBwdQuery | kBwdKey);
 
 // Chunked GLA over one segment of tokens per (b,h).
 struct GlaLaunch {

@@ -39,24 +39,16 @@
 
 #include "device_common.h"
 #include "hta_internal.h"
+#include "win_tiles.h"
 
 namespace hta {
 
 namespace {
 
-constexpr int kD = 128;          // head dim of the bf16 kernel
+using namespace tiles;
+
 constexpr int kBQ = 128;         // query rows per workgroup
-constexpr int kBK = 64;          // keys per LDS tile
-constexpr int kRowB = kD * 2;    // bytes per K / V row in LDS (unpadded, chunk-swizzled)
-constexpr int kTileB = kBK * kRowB;
 constexpr float kLazyLog2 = 8.0f;
-
-
-// 16-byte chunk c of LDS row r lives in slot c ^ swz(r), a rotation of the row's
-// low four bits: on gfx950's 64-bank LDS this is conflict-free for both the K
-// fragment reads (32 rows x one chunk) and the transposed V reads (4 rows x 4
-// chunks per 16 lanes), as the SQ_LDS_BANK_CONFLICT counter confirms.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 struct Acc {
     f32x16 o[4];   // O^T fragments: d-block db, element i -> d = 32 db + 8(i/4) + 4 h + i%4
@@ -73,107 +65,11 @@ __device__ __forceinline__ void acc_init(Acc& a) {
     a.l = 0.f;
 }
 
-// Offsets are ascending, so the taps present for absolute query frame fa
-// (those with fa - off >= 0) are a prefix of each list.
-__device__ __forceinline__ int taps_present(const int* off, int n, long long fa) {
-    int c = 0;
-    for (int j = 0; j < n; ++j) c += (off[j] <= fa) ? 1 : 0;
-    return c;
-}
-
 // Storage index of the key frame of segment sg (branch A's present taps first).
 __device__ __forceinline__ long long seg_frame(const WinLaunch& w, long long fa, int sg, int nAv) {
     const int off = sg < nAv ? w.taps.offA[sg] : w.taps.offB[sg - nAv];
     const long long f = fa - off;
     return w.R > 0 ? (f % w.R) : f;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// One global_load_lds_dwordx4: 16 bytes from sbase + voff (sbase wave-uniform,
-// voff per lane) into LDS at lds + 16 * lane (lds wave-uniform). Written as asm
-// so that the compiler does not serialise it against the LDS reads of the other
-// stage (it cannot tell the buffers apart); completion is tracked by wait_vmcnt.
-// It has no register outputs.
-__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-    // the base is wave-uniform; readfirstlane pins it to SGPRs for the asm operand
-    // (readfirstlane returns int: widen each half as uint32_t, never sign-extended)
-    const uint64_t b = (uint64_t)(uintptr_t)sbase;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds), "v"(voff), "s"(sb)
-                 : "m0");
-}
-
-// Per-lane byte offsets that stay fixed for the whole kernel.
-struct LaneOffs {
-    uint32_t k[8];     // K fragment ks of key row n (32-key block 0, stage 0)
-    uint32_t v[4];     // V^T fragment of d-block db, rows 4(g/2) + j (block 0, stage 0)
-    uint32_t vh[4];    // ... and rows 8 + 4(g/2) + j (swz differs in row bit 3)
-    uint32_t dma[4];   // source offset within a tile of DMA instruction i (row r, slot c)
-    int dma_row[4];    // ... and its row, for the clamped copy of a ragged tile
-    int dma_col[4];    // ... and its column
-};
-
-__device__ __forceinline__ void lane_offsets(LaneOffs& L, int wave, int lane) {
-    const int n = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) L.k[ks] = n * kRowB + 16 * ((2 * ks + h) ^ swz(n));
-    // V^T fragments by transposed LDS reads: within each 16-lane group g, lane
-    // 4j + a addresses row (key) 4(g/2) + j (+8, +16 gg, +32 kb: immediates),
-    // columns 16(g%2) + 4a .. +3 of the d-block; the read hands lane 4a + b
-    // column b of rows j = 0..3. swz depends on row bits 0-3 only, so rows
-    // +16 and +32 share these offsets and rows +8 get their own.
-    const int g = lane >> 4, sl = lane & 15, jr = sl >> 2, ac = sl & 3;
-    const int r0 = 4 * (g >> 1) + jr, r1 = r0 + 8;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        const int col = 32 * db + 16 * (g & 1) + 4 * ac;
-        L.v[db] = r0 * kRowB + 16 * ((col >> 3) ^ swz(r0)) + 8 * ((col >> 2) & 1);
-        L.vh[db] = r1 * kRowB + 16 * ((col >> 3) ^ swz(r1)) + 8 * ((col >> 2) & 1);
-    }
-    // DMA: wave w, instruction i fills LDS chunks [64 (4w + i), +64) of a tile;
-    // lane l fills chunk 64 (4w + i) + l = row r, slot c ^ swz(r).
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = 64 * (4 * wave + i) + lane;
-        const int r = p >> 4;
-        const int c = (p & 15) ^ swz(r);
-        L.dma_row[i] = r;
-        L.dma_col[i] = c * 8;
-        L.dma[i] = (uint32_t)(r * kD + c * 8) * 2;
-    }
-}
-
-// Enqueue one 64-key tile of K and V straight into LDS stage `st`. Rows past the
-// frame's end (ragged tile) re-read the last valid row: finite values, masked logits.
-__device__ __forceinline__ void issue_tile(uint32_t ldsK, uint32_t ldsV, const bf16* kb,
-                                           const bf16* vb, int nvalid, int wave,
-                                           const LaneOffs& L) {
-    if (nvalid == kBK) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t off = 1024u * (4 * wave + i);
-            dma16(L.dma[i], kb, ldsK + off);
-            dma16(L.dma[i], vb, ldsV + off);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t off = 1024u * (4 * wave + i);
-            const uint32_t src = (uint32_t)(min(L.dma_row[i], nvalid - 1) * kD + L.dma_col[i]) * 2;
-            dma16(src, kb, ldsK + off);
-            dma16(src, vb, ldsV + off);
-        }
-    }
 }
 
 // One 64-key tile for one wave: S^T = K Q^T, lazy online softmax, O^T += V^T P^T.
@@ -306,7 +202,7 @@ void win_attn_bf16_kernel(WinLaunch w) {
     auto issue = [&](const TileCursor& t, uint32_t stage) {
         const long long ofs = (long long)t.tk * kBK * kD;
         issue_tile(ldsK + stage * kTileB, ldsV + stage * kTileB, t.kf + ofs, t.vf + ofs,
-                   min(kBK, w.P - t.tk * kBK), wave, L);
+                   min(kBK, w.P - t.tk * kBK), wave, lane, L);
     };
 
     TileCursor ti{0, 0, kbh, vbh};   // next tile to stage
@@ -359,7 +255,12 @@ void win_attn_bf16_kernel(WinLaunch w) {
 
     // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add) (+ add2), rounded once.
     if (qrow >= w.P) return;
-    const float invA = 1.f / halves_sum(A.l);
+    const float lA = halves_sum(A.l);
+    const float invA = 1.f / lA;
+    // log-sum-exp of the scaled logits: the weights summed in l are
+    // exp(scale (s - m)), m in raw logit units
+    if (NBR == 1 && w.lse && h == 0)
+        w.lse[(long long)bh * w.Tq * w.P + (long long)fq * w.P + qrow] = A.m * w.scale + logf(lA);
     float invB = 0.f;
     if (NBR == 2) invB = 1.f / halves_sum(Bacc.l);
     const long long orow = (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
@@ -473,6 +374,8 @@ __global__ __launch_bounds__(256) void win_attn_f32_kernel(WinLaunch w) {
         f32_branch<D>(w, fa, nSegA, qv, kbh, vbh, 0, nseg, sub, mA, lA, accA);
     }
     if (!valid) return;
+    if (NBR == 1 && w.lse && sub == 0)
+        w.lse[(long long)bh * w.Tq * w.P + (long long)fq * w.P + row] = mA + logf(lA);
     float* op = static_cast<float*>(w.o) + qoff;
     const float* ap = w.add ? w.add + qoff : nullptr;
     const float* ap2 = w.add2 ? w.add2 + qoff : nullptr;

@@ -34,6 +34,7 @@ HTA_BF16 = 1
 HTA_OP_GLA = 1
 HTA_OP_HYBRID = 2
 HTA_OP_STREAM_STEP = 3
+HTA_OP_ATTN_BWD = 4
 
 HTA_NORM_Q = 1
 HTA_NORM_K = 2
@@ -42,7 +43,8 @@ HTA_GLA_GATED_DELTA = 0   # S = alpha (S - beta (S k) k^T) + beta v k^T
 HTA_GLA_PRINTED = 1       # S = alpha S - beta (S k) k^T + beta v k^T
 
 EXPORTED = (
-    "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_swa_dswa_fwd", "hta_gla_fwd",
+    "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_swa_fwd_lse", "hta_dswa_fwd_lse",
+    "hta_swa_bwd", "hta_dswa_bwd", "hta_swa_dswa_fwd", "hta_gla_fwd",
     "hta_gla_fwd_ex", "hta_hybrid_fwd", "hta_project_fwd",
     "hta_stream_init", "hta_stream_step", "hta_status_string", "hta_last_hip_error",
     "hta_version",
@@ -97,6 +99,14 @@ def lib() -> ctypes.CDLL:
     L.hta_swa_fwd.argtypes = [sp, vp, vp, vp, vp, i, f, vp]
     L.hta_dswa_fwd.restype = i
     L.hta_dswa_fwd.argtypes = [sp, vp, vp, vp, vp, i, i, f, vp]
+    L.hta_swa_fwd_lse.restype = i
+    L.hta_swa_fwd_lse.argtypes = [sp, vp, vp, vp, vp, vp, i, f, vp]
+    L.hta_dswa_fwd_lse.restype = i
+    L.hta_dswa_fwd_lse.argtypes = [sp, vp, vp, vp, vp, vp, i, i, f, vp]
+    L.hta_swa_bwd.restype = i
+    L.hta_swa_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, f, vp, sz, vp]
+    L.hta_dswa_bwd.restype = i
+    L.hta_dswa_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, f, vp, sz, vp]
     L.hta_swa_dswa_fwd.restype = i
     L.hta_swa_dswa_fwd.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp]
     L.hta_gla_fwd.restype = i
@@ -185,6 +195,49 @@ def hta_dswa_fwd(q, k, v, o, P: int, taps: int, dilation_frames: int, scale: flo
     s = make_shape(q, v, P, o)
     _check(lib().hta_dswa_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(taps),
                               int(dilation_frames), float(scale), _stream(stream)), "hta_dswa_fwd")
+
+
+def hta_swa_fwd_lse(q, k, v, o, lse, P: int, window_frames: int, scale: float = 0.0,
+                    stream=None):
+    s = make_shape(q, v, P, o)
+    _check(lib().hta_swa_fwd_lse(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 int(window_frames), float(scale), _stream(stream)),
+           "hta_swa_fwd_lse")
+
+
+def hta_dswa_fwd_lse(q, k, v, o, lse, P: int, taps: int, dilation_frames: int,
+                     scale: float = 0.0, stream=None):
+    s = make_shape(q, v, P, o)
+    _check(lib().hta_dswa_fwd_lse(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  int(taps), int(dilation_frames), float(scale), _stream(stream)),
+           "hta_dswa_fwd_lse")
+
+
+def _bwd_ws(s: Shape, workspace, device):
+    need = hta_workspace_bytes(HTA_OP_ATTN_BWD, s, None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def hta_swa_bwd(q, k, v, o, lse, dout, dq, dk, dv, P: int, window_frames: int,
+                scale: float = 0.0, workspace=None, stream=None):
+    s = make_shape(q, v, P, o)
+    workspace = _bwd_ws(s, workspace, q.device)
+    _check(lib().hta_swa_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), int(window_frames),
+                             float(scale), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "hta_swa_bwd")
+
+
+def hta_dswa_bwd(q, k, v, o, lse, dout, dq, dk, dv, P: int, taps: int, dilation_frames: int,
+                 scale: float = 0.0, workspace=None, stream=None):
+    s = make_shape(q, v, P, o)
+    workspace = _bwd_ws(s, workspace, q.device)
+    _check(lib().hta_dswa_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), int(taps),
+                              int(dilation_frames), float(scale), _ptr(workspace),
+                              workspace.numel(), _stream(stream)), "hta_dswa_bwd")
 
 
 def hta_swa_dswa_fwd(q, k, v, o, P: int, params: Params, add=None, stream=None):

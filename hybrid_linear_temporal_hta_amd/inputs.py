@@ -112,3 +112,16 @@ def make_inputs(w: Workload, device="cpu", frames: int | None = None) -> dict:
         "beta": beta.contiguous(),
         "frames": F,
     }
+
+
+def make_output_grad(w: Workload, device="cpu", frames: int | None = None,
+                     std: float = 1.0) -> torch.Tensor:
+    """A seeded output gradient dL/do [B,H,F*P,dv] ~ N(0, std^2), drawn in fp32
+    from its own generator (seed + 1000) and rounded once to the storage dtype:
+    the input of a backward pass, standing in for the gradient a loss would send."""
+    F = w.T if frames is None else int(frames)
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(w.seed) + 1000)
+    d = torch.randn((w.B, w.H, F * w.P, w.dv), generator=g, device=dev, dtype=torch.float32)
+    return (d * std).to(w.dtype).contiguous()

@@ -105,6 +105,7 @@ typedef struct {
 #define HTA_OP_GLA          1
 #define HTA_OP_HYBRID       2
 #define HTA_OP_STREAM_STEP  3
+#define HTA_OP_ATTN_BWD     4   /* hta_swa_bwd / hta_dswa_bwd (params may be NULL) */
 
 /*
  * hta_workspace_bytes -- device workspace (bytes, 256-byte aligned start
@@ -129,6 +130,42 @@ int hta_swa_fwd(const hta_shape* shape, const void* q, const void* k, const void
  */
 int hta_dswa_fwd(const hta_shape* shape, const void* q, const void* k, const void* v,
                  void* o, int taps, int dilation_frames, float scale, void* stream);
+
+/*
+ * hta_swa_fwd_lse / hta_dswa_fwd_lse -- hta_swa_fwd / hta_dswa_fwd that also
+ * write, for the backward pass, lse: fp32 [B][H][L] with
+ *   lse[t] = log sum_s exp(scale * q_t . k_s)   (natural log)
+ * over the keys s of row t's window. lse must not overlap q, k, v or o.
+ */
+int hta_swa_fwd_lse(const hta_shape* shape, const void* q, const void* k, const void* v,
+                    void* o, float* lse, int window_frames, float scale, void* stream);
+int hta_dswa_fwd_lse(const hta_shape* shape, const void* q, const void* k, const void* v,
+                     void* o, float* lse, int taps, int dilation_frames, float scale,
+                     void* stream);
+
+/*
+ * hta_swa_bwd / hta_dswa_bwd -- gradient of one attention branch (the SWA or
+ * DSWA paragraph's forward), by the chain rule through softmax:
+ *   p_ts = exp(scale q_t.k_s - lse_t),  D_t = dout_t . o_t,
+ *   ds_ts = p_ts (dout_t . v_s - D_t),
+ *   dq_t = scale sum_s ds_ts k_s,  dk_s = scale sum_t ds_ts q_t,  dv_s = sum_t p_ts dout_t.
+ * Inputs: q, k, v as in the forward (dtype); o and lse from hta_*_fwd_lse with
+ * the same window and scale; dout = dL/do, [B][H][L][dv] in out_dtype (the
+ * dtype of o). Outputs dq, dk ([B][H][L][dk]) and dv ([B][H][L][dv]) in dtype,
+ * each written once (not accumulated). With bf16 inputs the products run on
+ * bf16 MFMA with fp32 accumulation: p and ds are rounded to bf16 as operands,
+ * dout is rounded to bf16 (and D taken from the rounded values).
+ * workspace: >= hta_workspace_bytes(HTA_OP_ATTN_BWD, shape, NULL). Outputs
+ * must not overlap the inputs, each other or the workspace.
+ */
+int hta_swa_bwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                void* dv, int window_frames, float scale, void* workspace,
+                size_t workspace_bytes, void* stream);
+int hta_dswa_bwd(const hta_shape* shape, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, const void* dout, void* dq, void* dk,
+                 void* dv, int taps, int dilation_frames, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /*
  * hta_swa_dswa_fwd -- SWA and DSWA summed: o = o_swa + o_dswa (+ add). The
