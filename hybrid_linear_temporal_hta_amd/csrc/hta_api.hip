@@ -341,6 +341,35 @@ hipError_t run_window_bwd(const hta_shape* s, hta::BwdLaunch b, const void* o, c
     return hta::launch_win_bwd(b, st);
 }
 
+size_t gla_bwd_ws(const hta_shape* s) {
+    return align_up(hta::gla_bwd_workspace_bytes(s->dtype, s->B * s->H, (long long)s->T * s->P,
+                                                 s->dk));
+}
+
+hta::GlaBwdLaunch gla_bwd_base(const hta_shape* s, const hta_params* p, const void* q,
+                               const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* state0, const void* dout,
+                               float* dstate, void* dq, void* dk, void* dv, float* dalpha,
+                               float* dbeta, void* ws, size_t ws_bytes) {
+    hta::GlaBwdLaunch b;
+    memset(&b, 0, sizeof(b));
+    b.q = q; b.k = k; b.v = v; b.alpha = alpha; b.beta = beta; b.state0 = state0;
+    b.dout = dout;
+    b.do_f32 = s->out_dtype == HTA_F32 ? 1 : 0;
+    b.dstate = dstate;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.dbeta = dbeta;
+    b.L = (long long)s->T * s->P;
+    b.BH = s->B * s->H;
+    b.d = s->dk;
+    b.chunk = p->gla_chunk;
+    b.scale = gla_scale_of(p->gla_scale);
+    b.dtype = s->dtype;
+    b.form = p->gla_form;
+    b.ws = ws;
+    b.ws_bytes = ws_bytes;
+    return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,6 +401,10 @@ size_t hta_workspace_bytes(int op, const hta_shape* shape, const hta_params* par
         return gla_ws(shape, params->gla_chunk);
     }
     if (op == HTA_OP_ATTN_BWD) return attn_bwd_ws(shape);
+    if (op == HTA_OP_GLA_BWD) {
+        if (!params || check_chunk(shape->dtype, params->gla_chunk) != HTA_OK) return 0;
+        return gla_bwd_ws(shape);
+    }
     if (op == HTA_OP_HYBRID || op == HTA_OP_STREAM_STEP) {
         if (check_params(shape, params) != HTA_OK) return 0;
         if (op == HTA_OP_STREAM_STEP && shape->T != 1) return 0;
@@ -568,6 +601,41 @@ int hta_gla_fwd_ex(const hta_shape* shape, const hta_params* params, const void*
     hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, o, params->gla_chunk,
                                 params->gla_scale, workspace, need, params->gla_form);
     hipError_t e = run_gla(g, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+int hta_gla_bwd(const hta_shape* shape, const hta_params* params, const void* q, const void* k,
+                const void* v, const float* alpha, const float* beta, const float* state0,
+                const void* dout, float* dstate, void* dq, void* dk, void* dv, float* dalpha,
+                float* dbeta, void* workspace, size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_shape(shape)) != HTA_OK) return st;
+    if (!params) return HTA_ERR_NULL;
+    if ((st = check_chunk(shape->dtype, params->gla_chunk)) != HTA_OK) return st;
+    if (!isfinite(params->gla_scale)) return HTA_ERR_UNSUPPORTED;
+    if (params->gla_form != HTA_GLA_GATED_DELTA && params->gla_form != HTA_GLA_PRINTED)
+        return HTA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !alpha || !beta || !state0 || !dout || !dstate || !dq || !dk || !dv ||
+        !dalpha || !dbeta)
+        return HTA_ERR_NULL;
+    const size_t need = gla_bwd_ws(shape);
+    if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    const size_t nq = seq_bytes(shape, shape->dk), nv = seq_bytes(shape, shape->dv);
+    const Range in[7] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                         range_of(alpha, gate_bytes(shape)), range_of(beta, gate_bytes(shape)),
+                         range_of(state0, state_bytes(shape)), range_of(dout, out_bytes(shape))};
+    const Range outs[7] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv),
+                           range_of(dalpha, gate_bytes(shape)), range_of(dbeta, gate_bytes(shape)),
+                           range_of(dstate, state_bytes(shape)), range_of(workspace, need)};
+    for (int i = 0; i < 7; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlap(outs[i], in[j])) return HTA_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(outs[i], outs[j])) return HTA_ERR_ALIAS;
+    }
+    hta::GlaBwdLaunch b = gla_bwd_base(shape, params, q, k, v, alpha, beta, state0, dout, dstate,
+                                       dq, dk, dv, dalpha, dbeta, workspace, need);
+    hipError_t e = hta::launch_gla_bwd(b, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HTA_OK : hip_fail(e);
 }
 

@@ -106,6 +106,35 @@ struct GlaLaunch {
     size_t ws_bytes;
 };
 
+// Backward of the GLA branch over one sequence per (b,h): given dL/do and
+// dL/dM_L (in dstate), the gradients of q, k, v, alpha, beta and dL/dM_0 (out
+// in dstate). The forward is recomputed from the inputs and the initial state.
+struct GlaBwdLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const float* state0;    // [BH][d][d] initial state M_0 = S_0^T
+    const void* dout;       // [BH][L][d], fp32 (do_f32) or bf16
+    int do_f32;
+    float* dstate;          // [BH][d][d]: in dL/dM_L, out dL/dM_0
+    void* dq;               // dtype of q
+    void* dk;
+    void* dv;
+    float* dalpha;          // [BH][L]
+    float* dbeta;
+    long long L;
+    int BH, d, chunk;
+    float scale;            // output scale of the forward
+    int dtype;
+    int form;               // 0: GatedDeltaNet reading, 1: the printed update
+    void* ws;
+    size_t ws_bytes;
+};
+size_t gla_bwd_workspace_bytes(int dtype, int BH, long long L, int d);
+hipError_t launch_gla_bwd(const GlaBwdLaunch& b, hipStream_t stream);
+
 // Per-token projections and gates (bf16 MFMA GEMM + fused epilogue).
 struct ProjLaunch {
     const void* x;          // [M][Dm] bf16, M = B * L tokens

@@ -106,6 +106,7 @@ typedef struct {
 #define HTA_OP_HYBRID       2
 #define HTA_OP_STREAM_STEP  3
 #define HTA_OP_ATTN_BWD     4   /* hta_swa_bwd / hta_dswa_bwd (params may be NULL) */
+#define HTA_OP_GLA_BWD      5   /* hta_gla_bwd (params: gla_chunk)                 */
 
 /*
  * hta_workspace_bytes -- device workspace (bytes, 256-byte aligned start
@@ -202,6 +203,30 @@ int hta_gla_fwd_ex(const hta_shape* shape, const hta_params* params,
                    const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, float* state, void* o,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hta_gla_bwd -- gradient of the GLA branch (GLA paragraph and update equations;
+ * form, chunk and output scale from params as in hta_gla_fwd_ex). With the
+ * state M = S^T, the forward maps (q, k, v, alpha, beta, M_0) to (o, M_L); this
+ * call returns the vector-Jacobian product for dL/do and dL/dM_L:
+ *   state0: fp32 [B][H][dk][dv], the initial state M_0 the forward started from
+ *           (zeros for S_0 = 0); not modified.
+ *   dout:   dL/do, [B][H][L][dv] in out_dtype.
+ *   dstate: fp32 [B][H][dk][dv], in: dL/dM_L (zero it when the loss does not
+ *           read the final state), out: dL/dM_0.
+ *   dq, dk ([B][H][L][dk]), dv ([B][H][L][dv]) in dtype; dalpha, dbeta fp32
+ *           [B][H][L]; each written once.
+ * The forward is recomputed inside the call from the inputs and state0. The
+ * gradient with respect to alpha goes through log(alpha): alpha must be > 0.
+ * workspace: >= hta_workspace_bytes(HTA_OP_GLA_BWD, shape, params). Outputs must
+ * not overlap the inputs, each other or the workspace.
+ */
+int hta_gla_bwd(const hta_shape* shape, const hta_params* params,
+                const void* q, const void* k, const void* v,
+                const float* alpha, const float* beta, const float* state0,
+                const void* dout, float* dstate, void* dq, void* dk, void* dv,
+                float* dalpha, float* dbeta, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /*
  * hta_hybrid_fwd -- the whole layer (three-branch figure): o = o_swa + o_dswa + o_gla
