@@ -42,45 +42,14 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "gla_tiles.h"
 #include "hta_internal.h"
 
 namespace hta {
 
 namespace {
 
-constexpr int kC = 64;                 // chunk
-constexpr int kD = 128;                // head dim
-constexpr float kLogFloor = -1.0e4f;   // log(alpha) floor: alpha = 0 decays to exactly 0
-
-// Operand block of one chunk (workspace and LDS stage share this layout).
-constexpr int kOffK = 0;               // K fp16 [64][128], 16-byte chunks swizzled by swz64
-constexpr int kOffQ = 16384;           // Q fp16, same layout
-constexpr int kOffT = 32768;           // T fp16 [64][64], chunks swizzled by swz32
-constexpr int kOffP = 40960;           // Pm fp16, same layout
-constexpr int kOffE = 49152;           // e^{g_t} fp32 [64]
-constexpr int kOffD = 49408;           // e^{g_C - g_t} fp32 [64]
-constexpr int kOffB = 49664;           // beta fp32 [64] (0 past the end of the sequence)
-constexpr int kOffX = 49920;           // e^{gp_t} fp32 [64]: scale of K M0 in X (gp = g, or
-                                       // g_{t-1} for the printed form)
-constexpr int kBlockMain = 49152;      // K, Q, T, Pm: 48 KiB = 12 x 4 KiB
-constexpr int kTailChunks = 64;        // eg, ed, beta, egp: 1 KiB = 64 x 16
-constexpr size_t kChunkBytes = 50176;  // + eg, ed, beta, egp
-constexpr int kOffV = 50176;           // LDS only: V tile bf16 [64 tokens][64 columns]
-constexpr int kStageBytes = kOffV + 64 * 64 * 2;   // 58368
-
-// 256-byte rows (K, Q): chunk c of row r in slot c ^ swz64(r).
-__device__ __forceinline__ int swz64(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-// 128-byte rows (T, Pm): chunk c of row r in slot c ^ swz32(r).
-__device__ __forceinline__ int swz32(int r) { return (r >> 1) & 7; }
-// 128-byte rows of the V tile.
-__device__ __forceinline__ int swzv(int r) { return 2 * ((r >> 2) & 3); }
-
-__device__ __forceinline__ int offK(int row, int col) {   // byte offset of element (row, col)
-    return row * 256 + 16 * ((col >> 3) ^ swz64(row)) + 2 * (col & 7);
-}
-__device__ __forceinline__ int offT(int row, int col) {
-    return row * 128 + 16 * ((col >> 3) ^ swz32(row)) + 2 * (col & 7);
-}
+using namespace glat;
 
 // ------------------------------------------------------------------ prep
 
@@ -204,18 +173,6 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
 
 // ------------------------------------------------------------------ scan
 
-// One global_load_lds_dwordx4 (16 bytes per lane into LDS at base + 16 * lane,
-// base wave-uniform). Written as asm so the compiler does not serialise it
-// against LDS reads of the other stage; completion is tracked by wait_vmcnt0.
-// It has no register outputs.
-__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
-    typedef __attribute__((address_space(3))) const char lds_char;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(gptr) : "m0");
-}
-
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
-
 // Enqueue chunk c's operand block and the 64-column V tile into an LDS stage.
 __device__ __forceinline__ void issue_chunk(char* stage, const GlaLaunch& g, int bh, int tile,
                                             long long c, long long nch, int wave, int lane) {
@@ -236,43 +193,6 @@ __device__ __forceinline__ void issue_chunk(char* stage, const GlaLaunch& g, int
         const int cc = (p & 7) ^ swzv(tok);
         dma16(vb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * wave + i));
     }
-}
-
-// A fragment of a 16-row block from a swizzled fp16 tile: row `row`, k-step
-// columns 32*ks + 4G + j (j < 4) and 32*ks + 16 + 4G + (j - 4).
-__device__ __forceinline__ f16x8 afragK(const char* base, int row, int ks, int G) {
-    const int c0 = 32 * ks + 4 * G;
-    return cat(*reinterpret_cast<const f16x4*>(base + offK(row, c0)),
-               *reinterpret_cast<const f16x4*>(base + offK(row, c0 + 16)));
-}
-__device__ __forceinline__ f16x8 afragT(const char* base, int row, int ks, int G) {
-    const int c0 = 32 * ks + 4 * G;
-    return cat(*reinterpret_cast<const f16x4*>(base + offT(row, c0)),
-               *reinterpret_cast<const f16x4*>(base + offT(row, c0 + 16)));
-}
-// K^T fragment for d-block kb, k-step kt (tokens 32kt + 4G + j, + 16) by two
-// transposed reads: source lane 4j + a addresses token row 32kt + 4G + j,
-// columns 16kb + 4a .. +3; lane 4a + b receives column b of rows j = 0..3.
-__device__ __forceinline__ f16x8 afragKt(const char* Kbase, int kb, int kt, int lane) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const int G = lane >> 4, s = lane & 15, j = s >> 2, a = s & 3;
-    const int t0 = 32 * kt + 4 * G + j;
-    const int col = 16 * kb + 4 * a;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Kbase + offK(t0, col)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Kbase + offK(t0 + 16, col)));
-    return cat(__builtin_bit_cast(f16x4, lo), __builtin_bit_cast(f16x4, hi));
-}
-
-// B fragment from two 16x16 accumulator tiles (rows 32ks..+15 and 32ks+16..+31).
-__device__ __forceinline__ f16x8 bfrag(const f32x4& lo, const f32x4& hi) {
-    f16x8 b;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        b[i] = (f16)lo[i];
-        b[4 + i] = (f16)hi[i];
-    }
-    return b;
 }
 
 template <bool OUT_F32>
@@ -310,6 +230,13 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
         const float* dsm = reinterpret_cast<const float*>(S + kOffD);
         const float* bsm = reinterpret_cast<const float*>(S + kOffB);
         const float* xsm = reinterpret_cast<const float*>(S + kOffX);
+        if (g.save_m) {   // the state entering this chunk, for a backward pass
+            f16* sm = static_cast<f16*>(g.save_m) + ((long long)bh * nch + c) * kD * kD + col;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm[(16 * kb + 4 * G + i) * kD] = (f16)Mr[kb][i];
+        }
 
         // K M0 and Q M0 (fragments of the critical path read ahead of their use)
         f16x8 kf[4][4];
@@ -374,6 +301,13 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
             U[rb] = mfma16h(tf[rb][0], xb[0], zero4);
             if (rb >= 2) U[rb] = mfma16h(tf[rb][1], xb[1], U[rb]);
         }
+        if (g.save_u) {
+            f16* su = static_cast<f16*>(g.save_u) + ((long long)bh * nch + c) * kC * kD + col;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) su[(16 * rb + 4 * G + i) * kD] = (f16)U[rb][i];
+        }
         f32x4 Us[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
@@ -431,6 +365,8 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
 }
 
 }  // namespace
+
+size_t gla_bf16_chunk_bytes() { return kChunkBytes; }
 
 size_t gla_bf16_workspace_bytes(int BH, long long L, int chunk) {
     (void)chunk;

@@ -104,6 +104,8 @@ struct GlaLaunch {
     long long ring_off;     // element offset of the slot inside a (b,h) slice
     void* ws;               // workspace
     size_t ws_bytes;
+    void* save_m;           // optional fp16 [BH][nch][d][d]: the state entering each chunk
+    void* save_u;           // optional fp16 [BH][nch][64][d]: each chunk's U (bf16 path)
 };
 
 // Backward of the GLA branch over one sequence per (b,h): given dL/do and
@@ -158,6 +160,8 @@ hipError_t launch_gla_f32(const GlaLaunch& g, hipStream_t stream);
 constexpr int kGlaPrep = 1, kGlaScan = 2;
 hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream, int parts = kGlaPrep | kGlaScan);
 size_t gla_bf16_workspace_bytes(int BH, long long L, int chunk);
+// Chunk operand block of the bf16 path (bytes per 64-token chunk).
+size_t gla_bf16_chunk_bytes();
 
 // Per-(b,h) strided copy of `elems` elements (16-byte multiples) from
 // src[bh*src_bh + src_off] to dst[bh*dst_bh + dst_off] (strides/offsets in elements).

@@ -56,3 +56,19 @@ def test_gla_bwd_fp32_tiny(form):
 def test_gla_bwd_fp32_d128_ragged(form):
     w = WORKLOADS["tiny_fp32"].replace(dk=128, dv=128, T=3, P=50, seed=7)   # L = 150
     _case(w, form)
+
+
+@pytest.mark.parametrize("form", [0, 1])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gla_bwd_bf16_ragged(form, out_dtype):
+    """bf16 chunked path: L = 200 (three full chunks and a ragged fourth)."""
+    w = WORKLOADS["gla_bf16"].replace(B=1, H=2, T=4, P=50, seed=8)
+    _case(w, form, out_dtype)
+
+
+@pytest.mark.parametrize("form", [0, 1])
+def test_gla_bwd_bf16_long(form):
+    """bf16 chunked path over 31 chunks with a ragged tail and gates as in the
+    GLA workload (alpha = sigmoid(N(4, 1)))."""
+    w = WORKLOADS["gla_bf16"].replace(B=2, H=4, T=13, P=151, seed=9)   # L = 1963
+    _case(w, form, torch.float32)
