@@ -789,9 +789,15 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
             if (row < n) {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const int col = 32 * wave + 16 * q + m;
-                    static_cast<bf16*>(b.dq)[(tok0 + row) * kD + col] = f2bf(accQ[2 * mt + q][i] * inv);
-                    static_cast<bf16*>(b.dk)[(tok0 + row) * kD + col] = f2bf(accK[2 * mt + q][i] * inv);
+                    const long long o = (tok0 + row) * kD + 32 * wave + 16 * q + m;
+                    const float xq = accQ[2 * mt + q][i] * inv, xk = accK[2 * mt + q][i] * inv;
+                    if (b.grad_f32) {
+                        static_cast<float*>(b.dq)[o] = xq;
+                        static_cast<float*>(b.dk)[o] = xk;
+                    } else {
+                        static_cast<bf16*>(b.dq)[o] = f2bf(xq);
+                        static_cast<bf16*>(b.dk)[o] = f2bf(xk);
+                    }
                 }
             }
         }
@@ -801,14 +807,24 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
         float s = 0.f;
         if (row < n) {
             const bf16x8 vv = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.v) + (tok0 + row) * kD + c8);
-            bf16x8 ov;
+            float ov[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float r = (float)Rr[row * kLd + c8 + i];
                 s += r * bf2f(vv[i]);
-                ov[i] = f2bf(bs[row] * r * inv);
+                ov[i] = bs[row] * r * inv;
             }
-            *reinterpret_cast<bf16x8*>(static_cast<bf16*>(b.dv) + (tok0 + row) * kD + c8) = ov;
+            const long long o = (tok0 + row) * kD + c8;
+            if (b.grad_f32) {
+                f32x4* d = reinterpret_cast<f32x4*>(static_cast<float*>(b.dv) + o);
+                d[0] = f32x4{ov[0], ov[1], ov[2], ov[3]};
+                d[1] = f32x4{ov[4], ov[5], ov[6], ov[7]};
+            } else {
+                bf16x8 ob;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ob[i] = f2bf(ov[i]);
+                *reinterpret_cast<bf16x8*>(static_cast<bf16*>(b.dv) + o) = ob;
+            }
         }
         s = group16_sum(s);
         if ((e & 15) == 0 && row < n) atomicAdd(&dbt[row], s);

@@ -260,8 +260,46 @@ hipError_t run_gla(const hta::GlaLaunch& g, hipStream_t st) {
 // ends, so its few workgroups take their CUs before the attention workgroups
 // (which can never share a CU with a scan workgroup: LDS) fill the chip. The
 // DSWA pass waits for the SWA pass and adds both partials, writing w.o.
+size_t gla_bwd_ws(const hta_shape* s) {
+    return align_up(hta::gla_bwd_workspace_bytes(s->dtype, s->B * s->H, (long long)s->T * s->P,
+                                                 s->dk));
+}
+
+hta::GlaBwdLaunch gla_bwd_base(const hta_shape* s, const hta_params* p, const void* q,
+                               const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* state0, const void* dout,
+                               float* dstate, void* dq, void* dk, void* dv, float* dalpha,
+                               float* dbeta, void* ws, size_t ws_bytes) {
+    hta::GlaBwdLaunch b;
+    memset(&b, 0, sizeof(b));
+    b.q = q; b.k = k; b.v = v; b.alpha = alpha; b.beta = beta; b.state0 = state0;
+    b.dout = dout;
+    b.do_f32 = s->out_dtype == HTA_F32 ? 1 : 0;
+    b.dstate = dstate;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.dbeta = dbeta;
+    b.L = (long long)s->T * s->P;
+    b.BH = s->B * s->H;
+    b.d = s->dk;
+    b.chunk = p->gla_chunk;
+    b.scale = gla_scale_of(p->gla_scale);
+    b.dtype = s->dtype;
+    b.form = p->gla_form;
+    b.ws = ws;
+    b.ws_bytes = ws_bytes;
+    return b;
+}
+
+// Training outputs of the attention passes (all optional): each branch's
+// log-sum-exp, and the DSWA branch's own output (the SWA one is `mid`).
+struct TrainOut {
+    float* lse_a = nullptr;
+    float* lse_b = nullptr;
+    float* obr_b = nullptr;
+};
+
 hipError_t run_hybrid_overlapped(const hta::GlaLaunch& g, const hta::WinLaunch& w, float* mid,
-                                 const hta_params* p, hipStream_t sm) {
+                                 const hta_params* p, hipStream_t sm,
+                                 const TrainOut& tr = TrainOut()) {
     std::lock_guard<std::mutex> lock(g_aux_mu);
     Aux* a = nullptr;
     hipError_t e = aux_for_current_device(&a);
@@ -277,6 +315,7 @@ hipError_t run_hybrid_overlapped(const hta::GlaLaunch& g, const hta::WinLaunch& 
     sw.out_f32 = 1;
     sw.add = nullptr;
     sw.add2 = nullptr;
+    sw.lse = tr.lse_a;
     if ((e = hta::launch_win_attn(sw, a->s)) != hipSuccess) return e;
     if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return e;
@@ -285,8 +324,34 @@ hipError_t run_hybrid_overlapped(const hta::GlaLaunch& g, const hta::WinLaunch& 
     taps_dswa(dw.taps, p->dswa_taps, p->dswa_dilation);
     dw.add = mid;
     dw.add2 = static_cast<const float*>(g.o);
+    dw.lse = tr.lse_b;
+    dw.obr = tr.obr_b;
     return hta::launch_win_attn(dw, sm);
 }
+
+// What a training forward keeps for hta_hybrid_bwd (caller-owned `saved`).
+struct Saved {
+    float* o_swa;      // [BH][L][dv] the SWA branch's output
+    float* o_dswa;     // [BH][L][dv] the DSWA branch's output
+    float* lse_swa;    // [BH][L]
+    float* lse_dswa;   // [BH][L]
+    float* state0;     // [BH][dk][dv] the initial GLA state
+};
+size_t saved_bytes(const hta_shape* s) {
+    return 2 * fp32_seq_bytes(s) + 2 * align_up(gate_bytes(s)) + align_up(state_bytes(s));
+}
+Saved saved_of(const hta_shape* s, void* p) {
+    char* c = static_cast<char*>(p);
+    Saved v;
+    v.o_swa = reinterpret_cast<float*>(c); c += fp32_seq_bytes(s);
+    v.o_dswa = reinterpret_cast<float*>(c); c += fp32_seq_bytes(s);
+    v.lse_swa = reinterpret_cast<float*>(c); c += align_up(gate_bytes(s));
+    v.lse_dswa = reinterpret_cast<float*>(c); c += align_up(gate_bytes(s));
+    v.state0 = reinterpret_cast<float*>(c);
+    return v;
+}
+
+
 
 // Backward of one attention branch. Workspace: per-row stats {lse log2(e), D}
 // with 64 rows of padding (the key pass stages 64-row tiles of it), then, for
@@ -341,33 +406,13 @@ hipError_t run_window_bwd(const hta_shape* s, hta::BwdLaunch b, const void* o, c
     return hta::launch_win_bwd(b, st);
 }
 
-size_t gla_bwd_ws(const hta_shape* s) {
-    return align_up(hta::gla_bwd_workspace_bytes(s->dtype, s->B * s->H, (long long)s->T * s->P,
-                                                 s->dk));
-}
-
-hta::GlaBwdLaunch gla_bwd_base(const hta_shape* s, const hta_params* p, const void* q,
-                               const void* k, const void* v, const float* alpha,
-                               const float* beta, const float* state0, const void* dout,
-                               float* dstate, void* dq, void* dk, void* dv, float* dalpha,
-                               float* dbeta, void* ws, size_t ws_bytes) {
-    hta::GlaBwdLaunch b;
-    memset(&b, 0, sizeof(b));
-    b.q = q; b.k = k; b.v = v; b.alpha = alpha; b.beta = beta; b.state0 = state0;
-    b.dout = dout;
-    b.do_f32 = s->out_dtype == HTA_F32 ? 1 : 0;
-    b.dstate = dstate;
-    b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.dbeta = dbeta;
-    b.L = (long long)s->T * s->P;
-    b.BH = s->B * s->H;
-    b.d = s->dk;
-    b.chunk = p->gla_chunk;
-    b.scale = gla_scale_of(p->gla_scale);
-    b.dtype = s->dtype;
-    b.form = p->gla_form;
-    b.ws = ws;
-    b.ws_bytes = ws_bytes;
-    return b;
+// Hybrid backward workspace: [GLA backward][stats SWA][stats DSWA][dout bf16]
+// [fp32 partials dq, dk, dv].
+size_t hybrid_bwd_ws(const hta_shape* s) {
+    size_t n = gla_bwd_ws(s) + 2 * attn_bwd_stats_bytes(s);
+    if (s->dtype == HTA_BF16 && s->out_dtype == HTA_F32)
+        n += align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 2);
+    return n + 3 * fp32_seq_bytes(s);
 }
 
 }  // namespace
@@ -401,6 +446,10 @@ size_t hta_workspace_bytes(int op, const hta_shape* shape, const hta_params* par
         return gla_ws(shape, params->gla_chunk);
     }
     if (op == HTA_OP_ATTN_BWD) return attn_bwd_ws(shape);
+    if (op == HTA_OP_HYBRID_BWD) {
+        if (check_params(shape, params) != HTA_OK) return 0;
+        return hybrid_bwd_ws(shape);
+    }
     if (op == HTA_OP_GLA_BWD) {
         if (!params || check_chunk(shape->dtype, params->gla_chunk) != HTA_OK) return 0;
         return gla_bwd_ws(shape);
@@ -636,6 +685,149 @@ int hta_gla_bwd(const hta_shape* shape, const hta_params* params, const void* q,
     hta::GlaBwdLaunch b = gla_bwd_base(shape, params, q, k, v, alpha, beta, state0, dout, dstate,
                                        dq, dk, dv, dalpha, dbeta, workspace, need);
     hipError_t e = hta::launch_gla_bwd(b, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+size_t hta_hybrid_saved_bytes(const hta_shape* shape) {
+    if (check_shape(shape) != HTA_OK) return 0;
+    return saved_bytes(shape);
+}
+
+int hta_hybrid_fwd_train(const hta_shape* shape, const hta_params* params, const void* q,
+                         const void* k, const void* v, const float* alpha, const float* beta,
+                         float* state, void* o, void* saved, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_shape(shape)) != HTA_OK) return st;
+    if ((st = check_params(shape, params)) != HTA_OK) return st;
+    if (!saved) return HTA_ERR_NULL;
+    const size_t need_gla = gla_ws(shape, params->gla_chunk);
+    const size_t need = need_gla + partial_ws(shape);
+    if ((st = check_gla_buffers(shape, q, k, v, alpha, beta, state, o, workspace, workspace_bytes,
+                                need)) != HTA_OK)
+        return st;
+    const size_t nq = seq_bytes(shape, shape->dk), nv = seq_bytes(shape, shape->dv);
+    const Range rs = range_of(saved, saved_bytes(shape));
+    const Range others[8] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                             range_of(alpha, gate_bytes(shape)), range_of(beta, gate_bytes(shape)),
+                             range_of(state, state_bytes(shape)), range_of(o, out_bytes(shape)),
+                             range_of(workspace, need)};
+    for (int j = 0; j < 8; ++j)
+        if (overlap(rs, others[j])) return HTA_ERR_ALIAS;
+    hipStream_t sm = static_cast<hipStream_t>(stream);
+    const Saved sv = saved_of(shape, saved);
+    const long long BH = (long long)shape->B * shape->H;
+    hipError_t e = hta::launch_fill_f32(sv.state0, state, BH * shape->dk * shape->dv, sm);
+    if (e != hipSuccess) return hip_fail(e);
+    hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
+    if (shape->dtype == HTA_BF16) {
+        char* wsb = static_cast<char*>(workspace);
+        float* gpart = reinterpret_cast<float*>(wsb + need_gla);
+        hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, gpart, params->gla_chunk,
+                                    params->gla_scale, workspace, need_gla, params->gla_form);
+        g.out_f32 = 1;
+        TrainOut tr;
+        tr.lse_a = sv.lse_swa;
+        tr.lse_b = sv.lse_dswa;
+        tr.obr_b = sv.o_dswa;
+        e = run_hybrid_overlapped(g, w, sv.o_swa, params, sm, tr);
+        return e == hipSuccess ? HTA_OK : hip_fail(e);
+    }
+    // fp32: GLA into o, the SWA pass into saved, the DSWA pass adding both into o
+    hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, o, params->gla_chunk,
+                                params->gla_scale, workspace, need_gla, params->gla_form);
+    if ((e = run_gla(g, sm)) != hipSuccess) return hip_fail(e);
+    hta::WinLaunch a = w;
+    a.nbr = 1;
+    taps_swa(a.taps, params->swa_window);
+    a.o = sv.o_swa;
+    a.lse = sv.lse_swa;
+    if ((e = hta::launch_win_attn(a, sm)) != hipSuccess) return hip_fail(e);
+    hta::WinLaunch d = w;
+    d.nbr = 1;
+    taps_dswa(d.taps, params->dswa_taps, params->dswa_dilation);
+    d.add = static_cast<const float*>(o);
+    d.add2 = sv.o_swa;
+    d.lse = sv.lse_dswa;
+    d.obr = sv.o_dswa;
+    e = hta::launch_win_attn(d, sm);
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+int hta_hybrid_bwd(const hta_shape* shape, const hta_params* params, const void* q, const void* k,
+                   const void* v, const float* alpha, const float* beta, const void* saved,
+                   const void* dout, float* dstate, void* dq, void* dk, void* dv, float* dalpha,
+                   float* dbeta, void* workspace, size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_shape(shape)) != HTA_OK) return st;
+    if ((st = check_params(shape, params)) != HTA_OK) return st;
+    if (!q || !k || !v || !alpha || !beta || !saved || !dout || !dstate || !dq || !dk || !dv ||
+        !dalpha || !dbeta)
+        return HTA_ERR_NULL;
+    const size_t need = hybrid_bwd_ws(shape);
+    if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    const size_t nq = seq_bytes(shape, shape->dk), nv = seq_bytes(shape, shape->dv);
+    const Range in[7] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
+                         range_of(alpha, gate_bytes(shape)), range_of(beta, gate_bytes(shape)),
+                         range_of(saved, saved_bytes(shape)), range_of(dout, out_bytes(shape))};
+    const Range outs[7] = {range_of(dq, nq), range_of(dk, nq), range_of(dv, nv),
+                           range_of(dalpha, gate_bytes(shape)), range_of(dbeta, gate_bytes(shape)),
+                           range_of(dstate, state_bytes(shape)), range_of(workspace, need)};
+    for (int i = 0; i < 7; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlap(outs[i], in[j])) return HTA_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(outs[i], outs[j])) return HTA_ERR_ALIAS;
+    }
+    hipStream_t sm = static_cast<hipStream_t>(stream);
+    const Saved sv = saved_of(shape, const_cast<void*>(saved));
+    char* w = static_cast<char*>(workspace);
+    const size_t gws = gla_bwd_ws(shape);
+    float* stats_a = reinterpret_cast<float*>(w + gws);
+    float* stats_b = reinterpret_cast<float*>(w + gws + attn_bwd_stats_bytes(shape));
+    char* p = w + gws + 2 * attn_bwd_stats_bytes(shape);
+    void* do_bf16 = nullptr;
+    if (shape->dtype == HTA_BF16 && shape->out_dtype == HTA_F32) {
+        do_bf16 = p;
+        p += align_up((size_t)shape->B * shape->H * (size_t)shape->T * shape->P * shape->dv * 2);
+    }
+    float* pq = reinterpret_cast<float*>(p);
+    float* pk = reinterpret_cast<float*>(p + fp32_seq_bytes(shape));
+    float* pv = reinterpret_cast<float*>(p + 2 * fp32_seq_bytes(shape));
+    // 1. GLA branch: fp32 partials of dq, dk, dv; dalpha, dbeta, dstate final
+    hta::GlaBwdLaunch gb = gla_bwd_base(shape, params, q, k, v, alpha, beta, sv.state0, dout,
+                                        dstate, pq, pk, pv, dalpha, dbeta, w, gws);
+    gb.grad_f32 = 1;
+    hipError_t e = hta::launch_gla_bwd(gb, sm);
+    if (e != hipSuccess) return hip_fail(e);
+    // 2. per-branch statistics (and dout in bf16 once)
+    hta::BwdPrep pr;
+    memset(&pr, 0, sizeof(pr));
+    pr.dout = dout;
+    pr.rows = (long long)shape->B * shape->H * shape->T * shape->P;
+    pr.d = shape->dv;
+    pr.o_f32 = 1;
+    pr.do_f32 = shape->out_dtype == HTA_F32 ? 1 : 0;
+    pr.round_do = shape->dtype == HTA_BF16 ? 1 : 0;
+    pr.o = sv.o_swa; pr.lse = sv.lse_swa; pr.stats = stats_a; pr.dout_bf16 = do_bf16;
+    if ((e = hta::launch_win_bwd_prep(pr, sm)) != hipSuccess) return hip_fail(e);
+    pr.o = sv.o_dswa; pr.lse = sv.lse_dswa; pr.stats = stats_b; pr.dout_bf16 = nullptr;
+    if ((e = hta::launch_win_bwd_prep(pr, sm)) != hipSuccess) return hip_fail(e);
+    // 3. SWA: partials in place; 4. DSWA: adds the partials, writes the outputs
+    hta::WinTaps ts, td;
+    taps_swa(ts, params->swa_window);
+    taps_dswa(td, params->dswa_taps, params->dswa_dilation);
+    hta::BwdLaunch bs = bwd_base(shape, q, k, v, pq, pk, pv, params->attn_scale, ts);
+    bs.dout = do_bf16 ? do_bf16 : dout;
+    bs.stats = stats_a;
+    bs.add_q = pq; bs.add_k = pk; bs.add_v = pv;
+    bs.out_f32 = 1;
+    if ((e = hta::launch_win_bwd(bs, sm)) != hipSuccess) return hip_fail(e);
+    hta::BwdLaunch bd = bwd_base(shape, q, k, v, dq, dk, dv, params->attn_scale, td);
+    bd.dout = do_bf16 ? do_bf16 : dout;
+    bd.stats = stats_b;
+    bd.add_q = pq; bd.add_k = pk; bd.add_v = pv;
+    e = hta::launch_win_bwd(bd, sm);
     return e == hipSuccess ? HTA_OK : hip_fail(e);
 }
 

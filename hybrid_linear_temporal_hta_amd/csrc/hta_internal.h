@@ -41,6 +41,7 @@ struct WinLaunch {
     int nbr;                // 1 or 2 branches
     WinTaps taps;
     float* lse;             // optional [BH][Tq*P]: log-sum-exp of the scaled logits (one branch)
+    float* obr;             // optional fp32 [BH][Tq*P][dv]: this branch's own output (one branch)
 };
 
 hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream);
@@ -131,6 +132,7 @@ struct GlaBwdLaunch {
     float scale;            // output scale of the forward
     int dtype;
     int form;               // 0: GatedDeltaNet reading, 1: the printed update
+    int grad_f32;           // bf16 inputs: write dq, dk, dv as fp32 (partials of a sum)
     void* ws;
     size_t ws_bytes;
 };

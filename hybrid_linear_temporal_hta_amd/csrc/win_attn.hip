@@ -277,6 +277,8 @@ void win_attn_bf16_kernel(WinLaunch w) {
                 r[i] = A.o[db][4 * g + i] * invA;
                 if (NBR == 2) r[i] += Bacc.o[db][4 * g + i] * invB;
             }
+            if (NBR == 1 && w.obr)
+                *reinterpret_cast<f32x4*>(w.obr + orow + d0) = f32x4{r[0], r[1], r[2], r[3]};
             if (ap) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(ap + d0);
 #pragma unroll
@@ -385,6 +387,7 @@ __global__ __launch_bounds__(256) void win_attn_f32_kernel(WinLaunch w) {
     for (int i = 0; i < D / 4; ++i) {
         float r = accA[i] * iA;
         if (NBR == 2) r += accB[i] * iB;
+        if (NBR == 1 && w.obr) w.obr[qoff + 4 * i + sub] = r;
         if (ap) r += ap[4 * i + sub];
         if (ap2) r += ap2[4 * i + sub];
         op[4 * i + sub] = r;

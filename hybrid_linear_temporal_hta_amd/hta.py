@@ -36,6 +36,7 @@ HTA_OP_HYBRID = 2
 HTA_OP_STREAM_STEP = 3
 HTA_OP_ATTN_BWD = 4
 HTA_OP_GLA_BWD = 5
+HTA_OP_HYBRID_BWD = 6
 
 HTA_NORM_Q = 1
 HTA_NORM_K = 2
@@ -46,7 +47,8 @@ HTA_GLA_PRINTED = 1       # S = alpha S - beta (S k) k^T + beta v k^T
 EXPORTED = (
     "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_swa_fwd_lse", "hta_dswa_fwd_lse",
     "hta_swa_bwd", "hta_dswa_bwd", "hta_swa_dswa_fwd", "hta_gla_fwd",
-    "hta_gla_fwd_ex", "hta_gla_bwd", "hta_hybrid_fwd", "hta_project_fwd",
+    "hta_gla_fwd_ex", "hta_gla_bwd", "hta_hybrid_fwd", "hta_hybrid_saved_bytes",
+    "hta_hybrid_fwd_train", "hta_hybrid_bwd", "hta_project_fwd",
     "hta_stream_init", "hta_stream_step", "hta_status_string", "hta_last_hip_error",
     "hta_version",
 )
@@ -116,6 +118,12 @@ def lib() -> ctypes.CDLL:
     L.hta_gla_fwd_ex.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.hta_gla_bwd.restype = i
     L.hta_gla_bwd.argtypes = [sp, pp] + [vp] * 14 + [sz, vp]
+    L.hta_hybrid_saved_bytes.restype = sz
+    L.hta_hybrid_saved_bytes.argtypes = [sp]
+    L.hta_hybrid_fwd_train.restype = i
+    L.hta_hybrid_fwd_train.argtypes = [sp, pp] + [vp] * 9 + [sz, vp]
+    L.hta_hybrid_bwd.restype = i
+    L.hta_hybrid_bwd.argtypes = [sp, pp] + [vp] * 14 + [sz, vp]
     L.hta_hybrid_fwd.restype = i
     L.hta_hybrid_fwd.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.hta_project_fwd.restype = i
@@ -306,6 +314,37 @@ def hta_hybrid_fwd(q, k, v, alpha, beta, state, o, P: int, params: Params, works
     _check(lib().hta_hybrid_fwd(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
                                 _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o), _ptr(workspace),
                                 workspace.numel(), _stream(stream)), "hta_hybrid_fwd")
+
+
+def hta_hybrid_saved_bytes(shape: Shape) -> int:
+    return int(lib().hta_hybrid_saved_bytes(ctypes.byref(shape)))
+
+
+def hta_hybrid_fwd_train(q, k, v, alpha, beta, state, o, saved, P: int, params: Params,
+                         workspace=None, stream=None):
+    """hta_hybrid_fwd that also fills `saved` (uint8, hta_hybrid_saved_bytes bytes)."""
+    s = make_shape(q, v, P, o)
+    need = hta_workspace_bytes(HTA_OP_HYBRID, s, params)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().hta_hybrid_fwd_train(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
+                                      _ptr(saved), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)), "hta_hybrid_fwd_train")
+
+
+def hta_hybrid_bwd(q, k, v, alpha, beta, saved, dout, dstate, dq, dk, dv, dalpha, dbeta,
+                   P: int, params: Params, workspace=None, stream=None):
+    """Gradients of the hybrid layer; dstate is dL/dM_L on entry and dL/dM_0 on exit."""
+    s = make_shape(q, v, P, dout)
+    need = hta_workspace_bytes(HTA_OP_HYBRID_BWD, s, params)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().hta_hybrid_bwd(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(alpha), _ptr(beta), _ptr(saved), _ptr(dout), _ptr(dstate),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(dbeta),
+                                _ptr(workspace), workspace.numel(), _stream(stream)),
+           "hta_hybrid_bwd")
 
 
 class Stream:

@@ -107,6 +107,7 @@ typedef struct {
 #define HTA_OP_STREAM_STEP  3
 #define HTA_OP_ATTN_BWD     4   /* hta_swa_bwd / hta_dswa_bwd (params may be NULL) */
 #define HTA_OP_GLA_BWD      5   /* hta_gla_bwd (params: gla_chunk)                 */
+#define HTA_OP_HYBRID_BWD   6   /* hta_hybrid_bwd                                  */
 
 /*
  * hta_workspace_bytes -- device workspace (bytes, 256-byte aligned start
@@ -245,6 +246,36 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params,
                    const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, float* state, void* o,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Training: hta_hybrid_fwd_train is hta_hybrid_fwd (same arguments, workspace
+ * of HTA_OP_HYBRID, same stream behaviour) that also fills `saved`, a caller
+ * buffer of hta_hybrid_saved_bytes(shape) bytes (0 on an invalid shape), with
+ * what the backward pass needs: the initial GLA state (copied before the call
+ * advances `state`), each attention branch's own output (fp32) and per-row
+ * log-sum-exp. `saved` must not overlap any other argument.
+ *
+ * hta_hybrid_bwd -- gradient of the whole layer, o = o_swa + o_dswa + o_gla, for
+ * dout = dL/do ([B][H][L][dv], out_dtype) and dstate = dL/dM_L (in; zero it if
+ * the loss does not read the final state), from the inputs of the forward and
+ * its `saved` buffer. Writes dq, dk, dv (dtype; the three branches' gradients
+ * summed in fp32 and rounded once), dalpha, dbeta (fp32 [B][H][L]) and dstate
+ * (out: dL/dM_0). The GLA branch's forward is recomputed inside the call. The
+ * same numerics as hta_swa_bwd / hta_dswa_bwd and hta_gla_bwd apply.
+ * workspace: >= hta_workspace_bytes(HTA_OP_HYBRID_BWD, shape, params). Outputs
+ * must not overlap the inputs, each other or the workspace.
+ */
+size_t hta_hybrid_saved_bytes(const hta_shape* shape);
+int hta_hybrid_fwd_train(const hta_shape* shape, const hta_params* params,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta, float* state, void* o,
+                         void* saved, void* workspace, size_t workspace_bytes, void* stream);
+int hta_hybrid_bwd(const hta_shape* shape, const hta_params* params,
+                   const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const void* saved,
+                   const void* dout, float* dstate, void* dq, void* dk, void* dv,
+                   float* dalpha, float* dbeta, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /*
  * Streaming context: the complete resumable memory of the layer after

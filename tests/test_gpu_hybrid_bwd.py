@@ -1,0 +1,129 @@
+"""GPU parity of the hybrid layer's training pair (hta_hybrid_fwd_train,
+hta_hybrid_bwd) against the oracle: the forward output equals hta_hybrid_fwd's,
+and the gradients of o = o_swa + o_dswa + o_gla (dq, dk, dv summed over the
+branches, dalpha, dbeta, dL/dM_0) match the oracle's exact gradients.
+
+Inputs: the hybrid workload's distributions (q, v ~ N(0,1)/sqrt(d), unit-norm
+k, alpha = sigmoid(N(4, 1)), beta = sigmoid(N(0, 1))), a seeded output
+gradient ~ N(0, 1), a non-zero initial state and final-state gradient.
+Tolerance: max |gpu - oracle| <= tol * RMS(oracle) (1e-4 fp32, 2e-2 bf16 plus
+the half-ulp of bf16 outputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, assert_parity, assert_parity_rounded, f64
+from hybrid_linear_temporal_hta_amd import hta
+from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, make_inputs, make_output_grad
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, x, dout, s0, dsf, prm, out_dtype):
+    q, k, v, a, b = x["q"], x["k"], x["v"], x["alpha"], x["beta"]
+    B, H, L, d = q.shape
+    st = s0.clone()
+    o = torch.empty(B, H, L, d, dtype=out_dtype, device="cuda")
+    shape = hta.make_shape(q, v, w.P, o)
+    saved = torch.empty(hta.hta_hybrid_saved_bytes(shape), dtype=torch.uint8, device="cuda")
+    hta.hta_hybrid_fwd_train(q, k, v, a, b, st, o, saved, w.P, prm)
+    st2 = s0.clone()
+    o2 = torch.empty_like(o)
+    hta.hta_hybrid_fwd(q, k, v, a, b, st2, o2, w.P, prm)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    da, db = torch.empty_like(a), torch.empty_like(b)
+    dst = dsf.clone()
+    hta.hta_hybrid_bwd(q, k, v, a, b, saved, dout, dst, dq, dk, dv, da, db, w.P, prm)
+    torch.cuda.synchronize()
+    if w.dtype == torch.bfloat16:   # the same kernels in the same order: identical bits
+        assert torch.equal(o, o2), "hta_hybrid_fwd_train output differs from hta_hybrid_fwd"
+    else:   # fp32 inference sums both attention branches in one pass: rounding order differs
+        assert_parity(o, f64(o2), w.dtype, "fwd_train vs fwd output")
+    assert torch.equal(st, st2), "final states differ"
+    return dict(dq=dq, dk=dk, dv=dv, dalpha=da, dbeta=db, dstate0=dst)
+
+
+def _inputs(w, out_dtype):
+    x = make_inputs(w, device="cuda", frames=w.T)
+    dout = make_output_grad(w, device="cuda").to(out_dtype)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 77)
+    s0 = 0.3 * torch.randn(w.B, w.H, w.dk, w.dv, generator=g, device="cuda")
+    dsf = torch.randn(w.B, w.H, w.dk, w.dv, generator=g, device="cuda")
+    return x, dout, s0, dsf
+
+
+def _check(got, ref, dtype, what):
+    for name in ("dq", "dk", "dv"):
+        if dtype == torch.bfloat16:
+            assert_parity_rounded(got[name], ref[name], TOL[dtype], f"{what} {name}")
+        else:
+            assert_parity(got[name], ref[name], dtype, f"{what} {name}")
+    for name in ("dalpha", "dbeta", "dstate0"):
+        assert_parity(got[name], ref[name], dtype, f"{what} {name}")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("form", [0, 1])
+def test_hybrid_bwd_bf16(out_dtype, form):
+    w = WORKLOADS["hybrid_stream"].replace(B=1, H=2, T=9, P=70, stream_frames=0, dilation=2,
+                                           seed=41)
+    print(f"[case] hybrid bwd B{w.B} H{w.H} T{w.T} P{w.P} form{form} out {out_dtype}", flush=True)
+    x, dout, s0, dsf = _inputs(w, out_dtype)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, gla_form=form)
+    got = _run(w, x, dout, s0, dsf, prm, out_dtype)
+    do = f64(dout.to(torch.bfloat16))
+    ref = oracle.hybrid_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["alpha"]),
+                            f64(x["beta"]), do, w.T, w.P, w.window, w.taps, w.dilation,
+                            f64(s0), f64(dsf), form=form)
+    _check(got, ref, w.dtype, "hybrid")
+
+
+def test_hybrid_bwd_fp32():
+    w = WORKLOADS["tiny_fp32"]
+    print(f"[case] hybrid bwd {w.name}", flush=True)
+    x, dout, s0, dsf = _inputs(w, torch.float32)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    got = _run(w, x, dout, s0, dsf, prm, torch.float32)
+    ref = oracle.hybrid_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["alpha"]),
+                            f64(x["beta"]), f64(dout), w.T, w.P, w.window, w.taps, w.dilation,
+                            f64(s0), f64(dsf))
+    _check(got, ref, w.dtype, "hybrid fp32")
+
+
+@pytest.mark.slow
+def test_hybrid_bwd_full_size_sampled():
+    """The hybrid workload (B2 H16 T21 P1560, bf16 in, fp32 out) in the launch
+    configuration the benchmark times. For two (b, h) slices: the GLA
+    gradients over the whole sequence, and dq / dk / dv on sampled rows (the
+    attention part from the oracle's row routines plus the GLA part)."""
+    w = WORKLOADS["hybrid_stream"].replace(stream_frames=0)
+    print(f"[case] hybrid bwd full size B{w.B} H{w.H} T{w.T} P{w.P}", flush=True)
+    x, dout, s0, dsf = _inputs(w, torch.float32)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    got = _run(w, x, dout, s0, dsf, prm, torch.float32)
+    q, k, v = x["q"].cpu(), x["k"].cpu(), x["v"].cpu()
+    do = f64(dout.to(torch.bfloat16))
+    L = w.L
+    rng = np.random.default_rng(3)
+    for b_, h_ in ((0, 3), (1, 14)):
+        bh = b_ * w.H + h_
+        sl = (slice(b_, b_ + 1), slice(h_, h_ + 1))
+        print(f"[case] oracle GLA backward of (b, h) = ({b_}, {h_})", flush=True)
+        g = oracle.gla_bwd(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(x["alpha"][sl]),
+                           f64(x["beta"][sl]), do[sl], f64(s0[sl]), f64(dsf[sl]))
+        for name in ("dalpha", "dbeta", "dstate0"):
+            assert_parity(got[name][sl], g[name], w.dtype, f"full-size {name} (b,h)=({b_},{h_})")
+        pos = np.unique(np.concatenate([[0, 1559, 1560, L - 1], rng.integers(0, L, 24)]))
+        rows = bh * L + pos
+        att_dq = sum(oracle.window_dq_rows(kind, q, k, v, do, w.T, w.P, a, dd, rows)
+                     for kind, a, dd in (("swa", w.window, 0), ("dswa", w.taps, w.dilation)))
+        kv = [oracle.window_dkv_rows(kind, q, k, v, do, w.T, w.P, a, dd, rows)
+              for kind, a, dd in (("swa", w.window, 0), ("dswa", w.taps, w.dilation))]
+        att_dk, att_dv = kv[0][0] + kv[1][0], kv[0][1] + kv[1][1]
+        for name, att in (("dq", att_dq), ("dk", att_dk), ("dv", att_dv)):
+            ref = att + g[name][0, 0, pos]
+            assert_parity_rounded(got[name][b_, h_, torch.from_numpy(pos).cuda()], ref,
+                                  TOL[w.dtype], f"full-size {name} sampled rows (b,h)=({b_},{h_})")
