@@ -7,7 +7,9 @@ library's auxiliary stream beside the SWA pass; the DSWA pass then adds both
 partials. The dominant kernel's roofline is timed on the same attention
 launches run alone; the GLA branch is timed alone as well. After the forward
 steps the 64-frame streaming continuation of the same workload is timed
-(reported under "stream"), then the 336-frame long-horizon workload.
+(reported under "stream"), then the training pair on the same batch (forward
+that saves activations + backward, under "train"), the 336-frame long-horizon
+workload and the input-side projection.
 
 Prints ONE JSON line. With --gpus above 1 it exits: this build runs on a single
 GPU (sharding is described in the design notes, not measured).
@@ -209,6 +211,95 @@ def projection(hta, dev, steps):
             "frac_mfma": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)}
 
 
+def train(hta, w, x, dev, steps, warmup, cpu_heads):
+    """The training pair on the same batch (NEXT to the forward hot path): one
+    step = hta_hybrid_fwd_train + hta_hybrid_bwd (dL/do ~ N(0, 1), fp32), wall
+    time; the backward alone and each attention branch's backward alone
+    (HIP events), with the attention backward's MFMA roofline: its algorithmic
+    work is 2.5x the branch's forward (recompute S, then dP, dV, dK, dQ: five
+    products of 2 d P^2 per (query frame, tap frame) pair against two)."""
+    import torch
+    from hybrid_linear_temporal_hta_amd.inputs import make_output_grad
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    q, k, v, a, b = x["q"], x["k"], x["v"], x["alpha"], x["beta"]
+    o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device=dev)
+    st = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
+    shape = hta.make_shape(q, v, w.P, o)
+    saved = torch.empty(hta.hta_hybrid_saved_bytes(shape), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape, prm), dtype=torch.uint8,
+                      device=dev)
+    wsb = torch.empty(hta.hta_workspace_bytes(hta.HTA_OP_HYBRID_BWD, shape, prm),
+                      dtype=torch.uint8, device=dev)
+    wsa = torch.empty(hta.hta_workspace_bytes(hta.HTA_OP_ATTN_BWD, shape, None),
+                      dtype=torch.uint8, device=dev)
+    dout = make_output_grad(w.replace(stream_frames=0), device=dev).to(torch.float32)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    da, db = torch.empty_like(a), torch.empty_like(b)
+    dst = torch.zeros_like(st)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        hta.hta_hybrid_fwd_train(q, k, v, a, b, st, o, saved, w.P, prm, workspace=wsf,
+                                 stream=stream)
+        hta.hta_hybrid_bwd(q, k, v, a, b, saved, dout, dst, dq, dk, dv, da, db, w.P, prm,
+                           workspace=wsb, stream=stream)
+    step_ms = timed_wall(step, steps, warmup)
+    bwd_ms = timed_events(lambda: hta.hta_hybrid_bwd(q, k, v, a, b, saved, dout, dst, dq, dk, dv,
+                                                     da, db, w.P, prm, workspace=wsb,
+                                                     stream=stream), steps, 1, stream)
+    lse = torch.empty(w.B, w.H, w.L, device=dev)
+    ob = torch.empty_like(o)
+    hta.hta_swa_fwd_lse(q, k, v, ob, lse, w.P, w.window, stream=stream)
+    swa_ms = timed_events(lambda: hta.hta_swa_bwd(q, k, v, ob, lse, dout, dq, dk, dv, w.P,
+                                                  w.window, workspace=wsa, stream=stream),
+                          steps, 1, stream)
+    hta.hta_dswa_fwd_lse(q, k, v, ob, lse, w.P, w.taps, w.dilation, stream=stream)
+    dswa_ms = timed_events(lambda: hta.hta_dswa_bwd(q, k, v, ob, lse, dout, dq, dk, dv, w.P,
+                                                    w.taps, w.dilation, workspace=wsa,
+                                                    stream=stream), steps, 1, stream)
+    fl_branch = attn_flops(w) / 2          # SWA and DSWA have equal tap-frame counts here
+    fl_bwd = 2.5 * fl_branch
+    att_ms = (swa_ms + dswa_ms) / 2
+    achieved = fl_bwd / (att_ms / 1e3) / 1e12
+    res = {"workload": "B2 H16 T21 P1560 d128 (L=32760) bf16 in, fp32 out and dL/do",
+           "steps": steps, "ms_per_step": round(step_ms, 3),
+           "tokens_per_s": round(w.B * w.L / (step_ms / 1e3), 1),
+           "bwd_ms": round(bwd_ms, 3),
+           "attn_bwd_roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                                 "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
+                                 "calls": "hta_swa_bwd, hta_dswa_bwd (prep + query pass + key pass)",
+                                 "flop_per_call": fl_bwd, "avg_call_ms": round(att_ms, 4)}}
+    if cpu_heads > 0:
+        res["cpu_baseline"] = cpu_baseline_bwd(w, x, dout, cpu_heads)
+    del saved, wsf, wsb, wsa
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_bwd(w, x, dout, heads: int, frames: int = 2):
+    """The fp64 oracle's hybrid backward, untuned, on a bounded sample: `heads`
+    heads of batch 0 over the first `frames` frames (the attention windows are
+    shorter there than in the full sequence, so this over-states the oracle's
+    rate on the workload). A token carries H heads: the sample is worth
+    frames * P * heads / H tokens."""
+    import oracle
+    n = frames * w.P
+    sl = (slice(0, 1), slice(0, heads), slice(0, n))
+    f = lambda t: t[sl].double().cpu().numpy()
+    q, k, v, a, b = f(x["q"]), f(x["k"]), f(x["v"]), f(x["alpha"]), f(x["beta"])
+    do = f(dout.to(w.dtype))
+    t0 = time.perf_counter()
+    oracle.hybrid_bwd(q, k, v, a, b, do, frames, w.P, w.window, w.taps, w.dilation)
+    dt = time.perf_counter() - t0
+    tokens = n * heads / w.H
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"hybrid backward of {heads} of {w.H} heads of batch 0 over the first "
+                      f"{frames} frames ({n} tokens each; = {tokens:.0f} tokens of {w.H} heads), "
+                      f"{dt:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,6 +308,7 @@ def main():
     ap.add_argument("--stream-steps", type=int, default=64)
     ap.add_argument("--long-horizon-steps", type=int, default=2)
     ap.add_argument("--project-steps", type=int, default=10)
+    ap.add_argument("--train-steps", type=int, default=10)
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU oracle baseline runs (0: skip it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="CALLS",
@@ -307,6 +399,7 @@ def main():
     del full
     torch.cuda.empty_cache()
 
+    tr = train(hta, w, x, dev, args.train_steps, 2, args.cpu_heads) if args.train_steps > 0 else None
     lh = long_horizon(hta, dev, args.long_horizon_steps) if args.long_horizon_steps > 0 else None
     proj = projection(hta, dev, args.project_steps) if args.project_steps > 0 else None
     cpu = cpu_baseline(w, x, args.cpu_heads) if args.cpu_heads > 0 else None
@@ -320,7 +413,7 @@ def main():
                       "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.dk,
                       "parallelism": "single GPU"},
            "roofline": roofline, "gla": gla, "stream": sres, "long_horizon": lh, "project": proj,
-           "cpu_baseline": cpu}
+           "train": tr, "cpu_baseline": cpu}
     print(json.dumps(out))
 
 

@@ -359,11 +359,34 @@ Saved saved_of(const hta_shape* s, void* p) {
 size_t attn_bwd_stats_bytes(const hta_shape* s) {
     return align_up(((size_t)s->B * s->H * (size_t)s->T * s->P + 64) * 8);
 }
-size_t attn_bwd_ws(const hta_shape* s) {
-    size_t n = attn_bwd_stats_bytes(s);
+// bf16 inputs: the maxima that scale dS (256 bytes) and fp16 copies of q and k.
+size_t attn_bwd_aux_bytes(const hta_shape* s) {
+    if (s->dtype != HTA_BF16) return 0;
+    return kAlign + 2 * align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dk * 2);
+}
+size_t do_copy_bytes(const hta_shape* s) {
     if (s->dtype == HTA_BF16 && s->out_dtype == HTA_F32)
-        n += align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 2);
-    return n;
+        return align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 2);
+    return 0;
+}
+size_t attn_bwd_ws(const hta_shape* s) {
+    return attn_bwd_stats_bytes(s) + attn_bwd_aux_bytes(s) + do_copy_bytes(s);
+}
+
+// Points the prep and the passes at the aux region (bf16): maxima, q16, k16;
+// zeroes the maxima (a kernel, not a memset).
+hipError_t bind_bwd_aux(const hta_shape* s, char* aux, hta::BwdPrep& p, hipStream_t st) {
+    if (s->dtype != HTA_BF16) return hipSuccess;
+    const size_t nqk = align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dk * 2);
+    p.gmax = reinterpret_cast<unsigned*>(aux);
+    p.q16 = aux + kAlign;
+    p.k16 = aux + kAlign + nqk;
+    return hta::launch_fill_f32(reinterpret_cast<float*>(aux), nullptr, 2, st);
+}
+void use_bwd_aux(const hta::BwdPrep& p, hta::BwdLaunch& b) {
+    b.gmax = p.gmax;
+    b.q16 = p.q16;
+    b.k16 = p.k16;
 }
 
 hta::BwdLaunch bwd_base(const hta_shape* s, const void* q, const void* k, const void* v, void* dq,
@@ -398,21 +421,24 @@ hipError_t run_window_bwd(const hta_shape* s, hta::BwdLaunch b, const void* o, c
     p.d = s->dv;
     p.o_f32 = p.do_f32 = s->out_dtype == HTA_F32 ? 1 : 0;
     p.round_do = s->dtype == HTA_BF16 ? 1 : 0;
-    if (s->dtype == HTA_BF16 && s->out_dtype == HTA_F32) p.dout_bf16 = w + attn_bwd_stats_bytes(s);
-    hipError_t e = hta::launch_win_bwd_prep(p, st);
+    p.q = b.q; p.k = b.k; p.v = b.v;
+    char* aux = w + attn_bwd_stats_bytes(s);
+    if (do_copy_bytes(s)) p.dout_bf16 = aux + attn_bwd_aux_bytes(s);
+    hipError_t e = bind_bwd_aux(s, aux, p, st);
     if (e != hipSuccess) return e;
+    if ((e = hta::launch_win_bwd_prep(p, st)) != hipSuccess) return e;
     b.stats = p.stats;
     b.dout = p.dout_bf16 ? p.dout_bf16 : dout;
+    use_bwd_aux(p, b);
     return hta::launch_win_bwd(b, st);
 }
 
-// Hybrid backward workspace: [GLA backward][stats SWA][stats DSWA][dout bf16]
-// [fp32 partials dq, dk, dv].
+// Hybrid backward workspace: [GLA backward][stats SWA][stats DSWA][maxima, fp16
+// q and k][dout bf16][fp32 partials dq, dk, dv of the GLA branch][the same of
+// the SWA branch].
 size_t hybrid_bwd_ws(const hta_shape* s) {
-    size_t n = gla_bwd_ws(s) + 2 * attn_bwd_stats_bytes(s);
-    if (s->dtype == HTA_BF16 && s->out_dtype == HTA_F32)
-        n += align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 2);
-    return n + 3 * fp32_seq_bytes(s);
+    return gla_bwd_ws(s) + 2 * attn_bwd_stats_bytes(s) + attn_bwd_aux_bytes(s) +
+           do_copy_bytes(s) + 6 * fp32_seq_bytes(s);
 }
 
 }  // namespace
@@ -785,22 +811,20 @@ int hta_hybrid_bwd(const hta_shape* shape, const hta_params* params, const void*
     const size_t gws = gla_bwd_ws(shape);
     float* stats_a = reinterpret_cast<float*>(w + gws);
     float* stats_b = reinterpret_cast<float*>(w + gws + attn_bwd_stats_bytes(shape));
-    char* p = w + gws + 2 * attn_bwd_stats_bytes(shape);
+    char* aux = w + gws + 2 * attn_bwd_stats_bytes(shape);
+    char* p = aux + attn_bwd_aux_bytes(shape);
     void* do_bf16 = nullptr;
-    if (shape->dtype == HTA_BF16 && shape->out_dtype == HTA_F32) {
+    if (do_copy_bytes(shape)) {
         do_bf16 = p;
-        p += align_up((size_t)shape->B * shape->H * (size_t)shape->T * shape->P * shape->dv * 2);
+        p += do_copy_bytes(shape);
     }
-    float* pq = reinterpret_cast<float*>(p);
-    float* pk = reinterpret_cast<float*>(p + fp32_seq_bytes(shape));
-    float* pv = reinterpret_cast<float*>(p + 2 * fp32_seq_bytes(shape));
-    // 1. GLA branch: fp32 partials of dq, dk, dv; dalpha, dbeta, dstate final
-    hta::GlaBwdLaunch gb = gla_bwd_base(shape, params, q, k, v, alpha, beta, sv.state0, dout,
-                                        dstate, pq, pk, pv, dalpha, dbeta, w, gws);
-    gb.grad_f32 = 1;
-    hipError_t e = hta::launch_gla_bwd(gb, sm);
-    if (e != hipSuccess) return hip_fail(e);
-    // 2. per-branch statistics (and dout in bf16 once)
+    const size_t fs = fp32_seq_bytes(shape);
+    float* gq = reinterpret_cast<float*>(p);            // GLA partials
+    float* gk = reinterpret_cast<float*>(p + fs);
+    float* gv = reinterpret_cast<float*>(p + 2 * fs);
+    float* sq = reinterpret_cast<float*>(p + 3 * fs);   // SWA partials
+    float* sk = reinterpret_cast<float*>(p + 4 * fs);
+    float* sv_ = reinterpret_cast<float*>(p + 5 * fs);
     hta::BwdPrep pr;
     memset(&pr, 0, sizeof(pr));
     pr.dout = dout;
@@ -809,24 +833,55 @@ int hta_hybrid_bwd(const hta_shape* shape, const hta_params* params, const void*
     pr.o_f32 = 1;
     pr.do_f32 = shape->out_dtype == HTA_F32 ? 1 : 0;
     pr.round_do = shape->dtype == HTA_BF16 ? 1 : 0;
-    pr.o = sv.o_swa; pr.lse = sv.lse_swa; pr.stats = stats_a; pr.dout_bf16 = do_bf16;
-    if ((e = hta::launch_win_bwd_prep(pr, sm)) != hipSuccess) return hip_fail(e);
-    pr.o = sv.o_dswa; pr.lse = sv.lse_dswa; pr.stats = stats_b; pr.dout_bf16 = nullptr;
-    if ((e = hta::launch_win_bwd_prep(pr, sm)) != hipSuccess) return hip_fail(e);
-    // 3. SWA: partials in place; 4. DSWA: adds the partials, writes the outputs
+    pr.q = q; pr.k = k; pr.v = v;
+    hipError_t e;
+    if ((e = bind_bwd_aux(shape, aux, pr, sm)) != hipSuccess) return hip_fail(e);
     hta::WinTaps ts, td;
     taps_swa(ts, params->swa_window);
     taps_dswa(td, params->dswa_taps, params->dswa_dilation);
-    hta::BwdLaunch bs = bwd_base(shape, q, k, v, pq, pk, pv, params->attn_scale, ts);
+    hta::GlaBwdLaunch gb = gla_bwd_base(shape, params, q, k, v, alpha, beta, sv.state0, dout,
+                                        dstate, gq, gk, gv, dalpha, dbeta, w, gws);
+    gb.grad_f32 = 1;
+    hta::BwdLaunch bs = bwd_base(shape, q, k, v, sq, sk, sv_, params->attn_scale, ts);
     bs.dout = do_bf16 ? do_bf16 : dout;
     bs.stats = stats_a;
-    bs.add_q = pq; bs.add_k = pk; bs.add_v = pv;
     bs.out_f32 = 1;
-    if ((e = hta::launch_win_bwd(bs, sm)) != hipSuccess) return hip_fail(e);
     hta::BwdLaunch bd = bwd_base(shape, q, k, v, dq, dk, dv, params->attn_scale, td);
     bd.dout = do_bf16 ? do_bf16 : dout;
     bd.stats = stats_b;
-    bd.add_q = pq; bd.add_k = pk; bd.add_v = pv;
+    bd.add_q = sq; bd.add_k = sk; bd.add_v = sv_;
+    bd.add2_q = gq; bd.add2_k = gk; bd.add2_v = gv;
+    use_bwd_aux(pr, bs);
+    use_bwd_aux(pr, bd);
+    // the first prep (SWA) also makes the fp16 copies and the maxima; the second
+    // only its own statistics
+    hta::BwdPrep pr2 = pr;
+    pr2.q16 = nullptr; pr2.k16 = nullptr; pr2.gmax = nullptr; pr2.dout_bf16 = nullptr;
+    pr2.o = sv.o_dswa; pr2.lse = sv.lse_dswa; pr2.stats = stats_b;
+    if (shape->dtype == HTA_BF16) {
+        // The GLA backward (two latency-bound chunk scans with few workgroups, and a
+        // chunk-parallel gradient kernel) on `sm`, beside the SWA backward on the
+        // auxiliary stream; the DSWA backward then adds both sets of partials.
+        std::lock_guard<std::mutex> lock(g_aux_mu);
+        Aux* a = nullptr;
+        if ((e = aux_for_current_device(&a)) != hipSuccess) return hip_fail(e);
+        if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return hip_fail(e);
+        if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return hip_fail(e);
+        if ((e = hta::launch_gla_bwd(gb, sm)) != hipSuccess) return hip_fail(e);
+        pr.o = sv.o_swa; pr.lse = sv.lse_swa; pr.stats = stats_a; pr.dout_bf16 = do_bf16;
+        if ((e = hta::launch_win_bwd_prep(pr, a->s)) != hipSuccess) return hip_fail(e);
+        if ((e = hta::launch_win_bwd(bs, a->s)) != hipSuccess) return hip_fail(e);
+        if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return hip_fail(e);
+        if ((e = hta::launch_win_bwd_prep(pr2, sm)) != hipSuccess) return hip_fail(e);
+        if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return hip_fail(e);
+        e = hta::launch_win_bwd(bd, sm);
+        return e == hipSuccess ? HTA_OK : hip_fail(e);
+    }
+    if ((e = hta::launch_gla_bwd(gb, sm)) != hipSuccess) return hip_fail(e);
+    pr.o = sv.o_swa; pr.lse = sv.lse_swa; pr.stats = stats_a; pr.dout_bf16 = do_bf16;
+    if ((e = hta::launch_win_bwd_prep(pr, sm)) != hipSuccess) return hip_fail(e);
+    if ((e = hta::launch_win_bwd(bs, sm)) != hipSuccess) return hip_fail(e);
+    if ((e = hta::launch_win_bwd_prep(pr2, sm)) != hipSuccess) return hip_fail(e);
     e = hta::launch_win_bwd(bd, sm);
     return e == hipSuccess ? HTA_OK : hip_fail(e);
 }

@@ -59,6 +59,13 @@ struct BwdPrep {
     int d;
     int o_f32, do_f32;
     int round_do;           // D from the bf16-rounded dout (what the bf16 kernels multiply)
+    // bf16 inputs only (optional):
+    const void* q;          // q, k [rows][d] bf16: copied to fp16 into q16, k16
+    const void* k;
+    void* q16;
+    void* k16;
+    const void* v;          // v [rows][d] bf16: max |v| into gmax[1]
+    unsigned* gmax;         // max |dout| (as rounded) and max |v|, float bits, zeroed before
 };
 hipError_t launch_win_bwd_prep(const BwdPrep& p, hipStream_t stream);
 
@@ -74,12 +81,20 @@ struct BwdLaunch {
     const float* add_q;     // optional fp32 partials [BH][L][d] added before the store
     const float* add_k;
     const float* add_v;
+    const float* add2_q;    // optional second set of partials (never equal to the outputs)
+    const float* add2_k;
+    const float* add2_v;
     int out_f32;            // gradients written as fp32 (1) or bf16 (0)
     long long bh_elems;     // elements between (b,h) slices (L*d)
     int BH, P, T, d, dtype;
     float scale;
     int ntaps;
     int off[kMaxTaps];      // ascending frame offsets: query frame f reads key frames f - off[j]
+    // bf16 path: fp16 copies of q and k (exact for |x| < 65504) and the maxima
+    // that fix the power-of-two scale of dS in its fp16 products
+    const void* q16;
+    const void* k16;
+    const unsigned* gmax;
 };
 constexpr int kBwdQuery = 1, kBwdKey = 2;
 hipError_t launch_win_bwd(const BwdLaunch& b, hipStream_t stream, int parts = kBwdQuery | kBwdKey);

@@ -7,7 +7,7 @@
 // per-row log-sum-exp lse_t and D_t = dO_t . o_t,
 //   p_ts = exp(scale q_t.k_s - lse_t),  dp_ts = dO_t . v_s,  ds_ts = p_ts (dp_ts - D_t),
 //   dq_t = scale sum_s ds_ts k_s,  dk_s = scale sum_t ds_ts q_t,  dv_s = sum_t p_ts dO_t.
-// Three launches, no atomics:
+// Four launches, no atomics:
 //   prep       per row: stats = {lse log2(e), D} (and dO rounded to bf16 when it
 //              arrives in fp32 for bf16 inputs) -- HBM-bound, one pass;
 //   query pass per 128 queries (a query frame's tile): walks the key tiles of its
@@ -16,10 +16,13 @@
 //   key pass   per 128 keys of one key frame: walks the query tiles of every frame
 //              whose window holds that key frame (f_k + off[j] < T), recomputing
 //              S = Q K^T and dP = dO V^T, and accumulates dV^T += dO^T P and
-//              dK^T += Q^T dS (dK and dV in separate waves, S computed by both).
-// dS enters its products as the sum of two bf16 values (hi + lo): a single bf16
-// rounding of dS costs about 1 % of RMS in dq and dk, because sum_s ds_s = 0
-// makes those sums cancel; the split keeps about 16 significant bits.
+//              dK^T += Q^T dS (dK and dV in two launches, S computed by both).
+// dS enters its products (dQ = K^T dS, dK = Q^T dS) in fp16, against fp16
+// copies of K and Q (exact for |x| < 65504) made by the prep: a bf16 dS costs
+// about 1 % of RMS in dq and dk, because sum_s ds_s = 0 makes those sums
+// cancel; fp16 keeps 11 significant bits. dS is scaled by a power of two sigma
+// from max |dO| max |v| (found by the prep) so that it sits in fp16's normal
+// range whatever the gradient's magnitude; the results are scaled back exactly.
 // The bf16 kernels (d = 128) keep their own 32 rows (queries or keys) as MFMA B
 // fragments in registers and stream the other side through a two-stage LDS
 // ring with direct global->LDS loads, as the forward does; the logits' register
@@ -44,12 +47,13 @@ constexpr int kRows = 128;   // queries (query pass) or keys (key pass) per work
 
 template <int D>
 __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
+    __shared__ float mx[2][4];
     const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int sub = threadIdx.x & 15;
-    if (row >= p.rows) return;   // whole 16-lane groups leave together
-    constexpr int E = D / 16;    // elements per lane
+    const int sub = threadIdx.x & 15, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool ok = row < p.rows;   // whole 16-lane groups alike
+    constexpr int E = D / 16;       // elements per lane
     float dov[E], ov[E];
-    const long long base = row * D + sub * E;
+    const long long base = (ok ? row : 0) * D + sub * E;
     if (p.do_f32) {
         const float* s = static_cast<const float*>(p.dout) + base;
 #pragma unroll
@@ -72,20 +76,60 @@ __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
 #pragma unroll
         for (int i = 0; i < E; ++i) dov[i] = bf2f(f2bf(dov[i]));
     }
-    if (p.dout_bf16) {
+    if (p.dout_bf16 && ok) {
         bf16* dst = static_cast<bf16*>(p.dout_bf16) + base;
 #pragma unroll
         for (int i = 0; i < E; ++i) dst[i] = f2bf(dov[i]);
+    }
+    if (p.q16 && ok) {   // exact fp16 copies of q and k (D == 128 here: 8 per lane)
+        const bf16* qs = static_cast<const bf16*>(p.q) + base;
+        const bf16* ks = static_cast<const bf16*>(p.k) + base;
+        f16* qd = static_cast<f16*>(p.q16) + base;
+        f16* kd = static_cast<f16*>(p.k16) + base;
+#pragma unroll
+        for (int i = 0; i < E; ++i) { qd[i] = (f16)bf2f(qs[i]); kd[i] = (f16)bf2f(ks[i]); }
     }
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < E; ++i) acc = __builtin_fmaf(dov[i], ov[i], acc);
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (sub == 0) {
+    if (sub == 0 && ok) {
         p.stats[2 * row] = p.lse[row] * kLog2e;
         p.stats[2 * row + 1] = acc;
     }
+    if (p.gmax) {   // block maxima of |dout| and |v|, one atomic each per block
+        float md = 0.f, mv = 0.f;
+        if (ok) {
+            const bf16* vs = static_cast<const bf16*>(p.v) + base;
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                md = fmaxf(md, fabsf(dov[i]));
+                mv = fmaxf(mv, fabsf(bf2f(vs[i])));
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            md = fmaxf(md, __shfl_xor(md, m, 64));
+            mv = fmaxf(mv, __shfl_xor(mv, m, 64));
+        }
+        if (lane == 0) { mx[0][wave] = md; mx[1][wave] = mv; }
+        __syncthreads();
+        if (threadIdx.x < 2) {
+            const float* m4 = mx[threadIdx.x];
+            atomicMax(p.gmax + threadIdx.x, __float_as_uint(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))));
+        }
+    }
+}
+
+// Power-of-two scale of dS for its fp16 products: with m = max|dO| max|v|,
+// |dS| <= |dO . v| + |D| <= 2 d m, so sigma = 2^-floor(log2 m) keeps sigma |dS|
+// below 2 d while typical values stay in fp16's normal range (1 when m = 0).
+__device__ __forceinline__ float ds_sigma(const unsigned* gmax) {
+    const float m = __uint_as_float(gmax[0]) * __uint_as_float(gmax[1]);
+    if (!(m > 0.f)) return 1.f;
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
+    return ldexpf(1.f, -max(-100, min(e, 100)));
 }
 
 // ---------------------------------------------------------------------------------
@@ -94,7 +138,8 @@ __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
 // Writes mul * X (+ add) to dst row `row` (fp32 or bf16).
 
 __device__ __forceinline__ void store_rows(const f32x16 (&acc)[4], float mul, const float* add,
-                                           void* dst, int out_f32, long long rowoff, int h) {
+                                           const float* add2, void* dst, int out_f32,
+                                           long long rowoff, int h) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -105,6 +150,11 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[4], float mul, co
             for (int i = 0; i < 4; ++i) r[i] = acc[db][4 * g + i] * mul;
             if (add) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(add + rowoff + d0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] += x[i];
+            }
+            if (add2) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(add2 + rowoff + d0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) r[i] += x[i];
             }
@@ -132,6 +182,16 @@ __device__ __forceinline__ void load_rows(bf16x8 (&f)[8], const bf16* p, bool va
     }
 }
 
+__device__ __forceinline__ void load_rows_h(f16x8 (&f)[8], const f16* p, bool valid, int h) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        if (valid) f[ks] = *reinterpret_cast<const f16x8*>(p + 16 * ks + 8 * h);
+        else
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[ks][j] = (f16)0.f;
+    }
+}
+
 // ---------------------------------------------------------------------------------
 // bf16 query pass: dq. One workgroup = 4 waves = 128 query rows of one frame.
 
@@ -156,7 +216,8 @@ void win_bwd_dq_bf16_kernel(BwdLaunch w) {
     LaneOffs L;
     lane_offsets(L, wave, lane);
 
-    const bf16* kbh = static_cast<const bf16*>(w.k) + (long long)bh * w.bh_elems;
+    // K staged in fp16 (for S and for dQ = K^T dS), V in bf16
+    const bf16* kbh = static_cast<const bf16*>(w.k16) + (long long)bh * w.bh_elems;
     const bf16* vbh = static_cast<const bf16*>(w.v) + (long long)bh * w.bh_elems;
     const long long kv_frame = (long long)w.P * kD;
 
@@ -177,13 +238,15 @@ void win_bwd_dq_bf16_kernel(BwdLaunch w) {
     const bool valid = qrow < w.P;
     const bool wave_rows = qt * kRows + wave * 32 < w.P;
     const long long rowoff = (long long)bh * w.bh_elems + ((long long)fq * w.P + qrow) * kD;
-    bf16x8 qf[8], df[8];
-    load_rows(qf, static_cast<const bf16*>(w.q) + rowoff, valid, h);
+    f16x8 qf[8];
+    bf16x8 df[8];
+    load_rows_h(qf, static_cast<const f16*>(w.q16) + rowoff, valid, h);
     load_rows(df, static_cast<const bf16*>(w.dout) + rowoff, valid, h);
     const long long srow = (long long)bh * w.T * w.P + (long long)fq * w.P + qrow;
     const float lse2 = valid ? w.stats[2 * srow] : 0.f;
     const float Dq = valid ? w.stats[2 * srow + 1] : 0.f;
     const float c = w.scale * kLog2e;
+    const float sig = ds_sigma(w.gmax);
 
     f32x16 acc[4];
 #pragma unroll
@@ -201,7 +264,6 @@ void win_bwd_dq_bf16_kernel(BwdLaunch w) {
         if (wave_rows) {
             const char* Ks = Kst[ST];
             const char* Vs = Vst[ST];
-            typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
             // one 32-key block at a time keeps the live logits to 32 registers
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -209,32 +271,28 @@ void win_bwd_dq_bf16_kernel(BwdLaunch w) {
                 const f32x16 zero = {};
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + kb * 32 * kRowB + L.k[ks]);
-                    s = mfma32(kf, qf[ks], ks == 0 ? zero : s);
+                    const f16x8 kf = *reinterpret_cast<const f16x8*>(Ks + kb * 32 * kRowB + L.k[ks]);
+                    s = mfma32h(kf, qf[ks], ks == 0 ? zero : s);
                     const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vs + kb * 32 * kRowB + L.k[ks]);
                     dp = mfma32(vf, df[ks], ks == 0 ? zero : dp);
                 }
-                // ds = hi + lo, both bf16: the product keeps ~16 significant bits of ds
-                bf16x8 dhi[2], dlo[2];
+                // sigma ds in fp16 (11 significant bits)
+                f16x8 dsf[2];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
                     const float p = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
-                    const float ds = key < nvalid ? p * (dp[i] - Dq) : 0.f;
-                    const bf16 hi = f2bf(ds);
-                    dhi[i >> 3][i & 7] = hi;
-                    dlo[i >> 3][i & 7] = f2bf(ds - bf2f(hi));
+                    const float ds = key < nvalid ? (p * sig) * (dp[i] - Dq) : 0.f;
+                    dsf[i >> 3][i & 7] = (f16)ds;
                 }
 #pragma unroll
                 for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
                     for (int db = 0; db < 4; ++db) {
                         const char* kb_ = Ks + (kb * 32 + 16 * gg) * kRowB;
-                        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(kb_ + L.v[db]));
-                        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(kb_ + L.vh[db]));
-                        const bf16x8 kt = cat(lo, hi);
-                        acc[db] = mfma32(kt, dhi[gg], acc[db]);
-                        acc[db] = mfma32(kt, dlo[gg], acc[db]);
+                        const f16x4 lo = tr_f16(kb_ + L.v[db]);
+                        const f16x4 hi = tr_f16(kb_ + L.vh[db]);
+                        acc[db] = mfma32h(cat(lo, hi), dsf[gg], acc[db]);
                     }
             }
         }
@@ -245,18 +303,20 @@ void win_bwd_dq_bf16_kernel(BwdLaunch w) {
         if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     }
     if (!valid) return;
-    store_rows(acc, w.scale, w.add_q, w.dq, w.out_f32, rowoff, h);
+    store_rows(acc, w.scale / sig, w.add_q, w.add2_q, w.dq, w.out_f32, rowoff, h);
 }
 
 // ---------------------------------------------------------------------------------
-// bf16 key pass: dk, dv. One workgroup = 8 waves over 128 keys of one key frame:
-// waves 0..3 accumulate dK for keys 32w..32w+31 (they need S, dP and dS), waves
-// 4..7 accumulate dV for the same keys (they need S and P only) and stage the
-// query tiles (Q, dO and their stats) of every attending frame through LDS.
-// Splitting the two accumulators over two waves recomputes S once more but keeps
-// each wave within 256 registers at two waves per SIMD.
+// bf16 key pass: one workgroup = 4 waves = 128 keys of one key frame, walking the
+// query tiles (Q, dO and their stats, staged in LDS) of every frame whose window
+// holds that key frame. Two launches of the same kernel: DK accumulates dK^T
+// (needs S, dP and dS), the other dV^T (needs S and P); keeping one accumulator
+// set per launch keeps each within 256 registers at two waves per SIMD, at the
+// price of computing S twice.
 
-__global__ __launch_bounds__(512) void win_bwd_dkdv_bf16_kernel(BwdLaunch w) {
+template <bool DK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void win_bwd_key_bf16_kernel(BwdLaunch w) {
     __shared__ __attribute__((aligned(1024))) char Qst[2][kTileB];
     __shared__ __attribute__((aligned(1024))) char Ost[2][kTileB];
     __shared__ __attribute__((aligned(16))) float Sst[2][2 * kBK];   // {lse2, D} per query
@@ -273,14 +333,13 @@ __global__ __launch_bounds__(512) void win_bwd_dkdv_bf16_kernel(BwdLaunch w) {
     const int bh = wid / (nkt * w.T);
 
     const int lane = threadIdx.x & 63;
-    const int wave8 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool kwave = wave8 < 4;       // dK wave (else dV wave)
-    const int wave = wave8 & 3;         // key block, and staging slot of a dV wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, h = lane >> 5;
     LaneOffs L;
     lane_offsets(L, wave, lane);
 
-    const bf16* qbh = static_cast<const bf16*>(w.q) + (long long)bh * w.bh_elems;
+    // Q staged in fp16 (for S and for dK = Q^T dS), dO in bf16
+    const bf16* qbh = static_cast<const bf16*>(w.q16) + (long long)bh * w.bh_elems;
     const bf16* obh = static_cast<const bf16*>(w.dout) + (long long)bh * w.bh_elems;
     const float* sbh = w.stats + 2 * (long long)bh * w.T * w.P;
 
@@ -290,18 +349,16 @@ __global__ __launch_bounds__(512) void win_bwd_dkdv_bf16_kernel(BwdLaunch w) {
     const int ntq = (w.P + kBK - 1) / kBK;
     const int nit = nseg * ntq;
 
-    int isg = 0, itq = 0;   // next tile to stage (advanced by every wave alike)
+    int isg = 0, itq = 0;   // next tile to stage
     auto issue = [&](uint32_t stage) {
         const long long r0 = (long long)(fk + w.off[isg]) * w.P + (long long)itq * kBK;
-        if (!kwave) {
-            issue_tile(ldsQ + stage * kTileB, ldsO + stage * kTileB, qbh + r0 * kD, obh + r0 * kD,
-                       min(kBK, w.P - itq * kBK), wave, lane, L);
-            // stats of the tile's 64 queries (512 bytes, two dword loads); rows past the
-            // frame read on into the next rows or the 64-row padding, never used
-            if (wave == 0) {
-                dma4((uint32_t)lane * 4u, sbh + 2 * r0, ldsS + stage * 512u);
-                dma4((uint32_t)lane * 4u + 256u, sbh + 2 * r0, ldsS + stage * 512u + 256u);
-            }
+        issue_tile(ldsQ + stage * kTileB, ldsO + stage * kTileB, qbh + r0 * kD, obh + r0 * kD,
+                   min(kBK, w.P - itq * kBK), wave, lane, L);
+        // stats of the tile's 64 queries (512 bytes, two dword loads); rows past the
+        // frame read on into the next rows or the 64-row padding, never used
+        if (wave == 0) {
+            dma4((uint32_t)lane * 4u, sbh + 2 * r0, ldsS + stage * 512u);
+            dma4((uint32_t)lane * 4u + 256u, sbh + 2 * r0, ldsS + stage * 512u + 256u);
         }
         if (++itq == ntq) { itq = 0; ++isg; }
     };
@@ -311,12 +368,14 @@ __global__ __launch_bounds__(512) void win_bwd_dkdv_bf16_kernel(BwdLaunch w) {
     const bool valid = krow < w.P;
     const bool wave_rows = kt * kRows + wave * 32 < w.P;
     const long long rowoff = (long long)bh * w.bh_elems + ((long long)fk * w.P + krow) * kD;
-    bf16x8 kf[8], vf[8];
-    load_rows(kf, static_cast<const bf16*>(w.k) + rowoff, valid, h);
-    load_rows(vf, static_cast<const bf16*>(w.v) + rowoff, valid && kwave, h);
+    f16x8 kf[8];
+    bf16x8 vf[DK ? 8 : 1];
+    load_rows_h(kf, static_cast<const f16*>(w.k16) + rowoff, valid, h);
+    if (DK) load_rows(reinterpret_cast<bf16x8(&)[8]>(vf), static_cast<const bf16*>(w.v) + rowoff, valid, h);
     const float c = w.scale * kLog2e;
+    const float sig = ds_sigma(w.gmax);
 
-    f32x16 acc[4];   // dK^T (dK waves) or dV^T (dV waves)
+    f32x16 acc[4];   // dK^T or dV^T
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -333,25 +392,22 @@ __global__ __launch_bounds__(512) void win_bwd_dkdv_bf16_kernel(BwdLaunch w) {
             const char* Qs = Qst[ST];
             const char* Os = Ost[ST];
             const float* Ss = Sst[ST];
-            typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 f32x16 s, dp;
                 const f32x16 zero = {};
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + qb * 32 * kRowB + L.k[ks]);
-                    s = mfma32(qa, kf[ks], ks == 0 ? zero : s);
-                }
-                if (kwave) {
-#pragma unroll
-                    for (int ks = 0; ks < 8; ++ks) {
+                    const f16x8 qa = *reinterpret_cast<const f16x8*>(Qs + qb * 32 * kRowB + L.k[ks]);
+                    s = mfma32h(qa, kf[ks], ks == 0 ? zero : s);
+                    if (DK) {
                         const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Os + qb * 32 * kRowB + L.k[ks]);
-                        dp = mfma32(oa, vf[ks], ks == 0 ? zero : dp);
+                        dp = mfma32(oa, vf[DK ? ks : 0], ks == 0 ? zero : dp);
                     }
                 }
                 // element i: query qb*32 + 8(i/4) + 4h + i%4 of the tile, key n
-                bf16x8 xhi[2], xlo[2];   // dV waves: P (hi only); dK waves: dS = hi + lo
+                f16x8 dsf[2];   // DK: sigma dS in fp16
+                bf16x8 pf[2];   // dV: P in bf16
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int q0 = qb * 32 + 8 * g + 4 * h;
@@ -364,24 +420,23 @@ __global__ __launch_bounds__(512) void win_bwd_dkdv_bf16_kernel(BwdLaunch w) {
                         const int i = 4 * g + r;
                         const bool ok = q0 + r < nvalid;
                         const float p = fast_exp2(__builtin_fmaf(s[i], c, -l2[r]));
-                        const float x = !ok ? 0.f : (kwave ? p * (dp[i] - dd[r]) : p);
-                        const bf16 hi = f2bf(x);
-                        xhi[i >> 3][i & 7] = hi;
-                        if (kwave) xlo[i >> 3][i & 7] = f2bf(x - bf2f(hi));
+                        if (DK) dsf[i >> 3][i & 7] = (f16)(ok ? (p * sig) * (dp[i] - dd[r]) : 0.f);
+                        else pf[i >> 3][i & 7] = f2bf(ok ? p : 0.f);
                     }
                 }
-                // dV^T += dO^T P (dV waves), dK^T += Q^T dS (dK waves)
-                const char* src = kwave ? Qs : Os;
 #pragma unroll
                 for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
                     for (int db = 0; db < 4; ++db) {
-                        const char* b_ = src + (qb * 32 + 16 * gg) * kRowB;
-                        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b_ + L.v[db]));
-                        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(b_ + L.vh[db]));
-                        const bf16x8 at = cat(lo, hi);
-                        acc[db] = mfma32(at, xhi[gg], acc[db]);
-                        if (kwave) acc[db] = mfma32(at, xlo[gg], acc[db]);
+                        if (DK) {   // dK^T += Q^T dS
+                            const char* b_ = Qs + (qb * 32 + 16 * gg) * kRowB;
+                            acc[db] = mfma32h(cat(tr_f16(b_ + L.v[db]), tr_f16(b_ + L.vh[db])),
+                                              dsf[gg], acc[db]);
+                        } else {    // dV^T += dO^T P
+                            const char* b_ = Os + (qb * 32 + 16 * gg) * kRowB;
+                            acc[db] = mfma32(cat(tr_bf16(b_ + L.v[db]), tr_bf16(b_ + L.vh[db])),
+                                             pf[gg], acc[db]);
+                        }
                     }
             }
         }
@@ -392,8 +447,8 @@ __global__ __launch_bounds__(512) void win_bwd_dkdv_bf16_kernel(BwdLaunch w) {
         if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     }
     if (!valid) return;
-    if (kwave) store_rows(acc, w.scale, w.add_k, w.dk, w.out_f32, rowoff, h);
-    else store_rows(acc, 1.f, w.add_v, w.dv, w.out_f32, rowoff, h);
+    if (DK) store_rows(acc, w.scale / sig, w.add_k, w.add2_k, w.dk, w.out_f32, rowoff, h);
+    else store_rows(acc, 1.f, w.add_v, w.add2_v, w.dv, w.out_f32, rowoff, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -452,6 +507,7 @@ __global__ __launch_bounds__(256) void win_bwd_dq_f32_kernel(BwdLaunch w) {
     for (int i = 0; i < D / 4; ++i) {
         float r = acc[i] * w.scale;
         if (w.add_q) r += w.add_q[rowoff + 4 * i + sub];
+        if (w.add2_q) r += w.add2_q[rowoff + 4 * i + sub];
         static_cast<float*>(w.dq)[rowoff + 4 * i + sub] = r;
     }
 }
@@ -504,6 +560,8 @@ __global__ __launch_bounds__(256) void win_bwd_dkdv_f32_kernel(BwdLaunch w) {
         float a = dk[i] * w.scale, b = dv[i];
         if (w.add_k) a += w.add_k[rowoff + 4 * i + sub];
         if (w.add_v) b += w.add_v[rowoff + 4 * i + sub];
+        if (w.add2_k) a += w.add2_k[rowoff + 4 * i + sub];
+        if (w.add2_v) b += w.add2_v[rowoff + 4 * i + sub];
         static_cast<float*>(w.dk)[rowoff + 4 * i + sub] = a;
         static_cast<float*>(w.dv)[rowoff + 4 * i + sub] = b;
     }
@@ -531,8 +589,10 @@ hipError_t launch_win_bwd(const BwdLaunch& b, hipStream_t stream, int parts) {
         if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
         if (parts & kBwdQuery)
             hipLaunchKernelGGL(win_bwd_dq_bf16_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, b);
-        if (parts & kBwdKey)
-            hipLaunchKernelGGL(win_bwd_dkdv_bf16_kernel, dim3((unsigned)nwg), dim3(512), 0, stream, b);
+        if (parts & kBwdKey) {
+            hipLaunchKernelGGL(win_bwd_key_bf16_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, stream, b);
+            hipLaunchKernelGGL(win_bwd_key_bf16_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, stream, b);
+        }
         return hipGetLastError();
     }
     const long long nwg = (long long)b.BH * b.T * ((b.P + 63) / 64);

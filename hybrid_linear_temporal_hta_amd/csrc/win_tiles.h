@@ -73,6 +73,17 @@ __device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t 
                  : "m0");
 }
 
+// Transposed LDS reads (ds_read_b64_tr_b16) of 16-bit elements, as bf16 or fp16.
+__device__ __forceinline__ bf16x4 tr_bf16(const char* p) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+__device__ __forceinline__ f16x4 tr_f16(const char* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+
 // Per-lane byte offsets that stay fixed for the whole kernel.
 struct LaneOffs {
     uint32_t k[8];     // row fragment ks of row n (32-row block 0, stage 0)
