@@ -185,3 +185,92 @@ def test_project_argument_checks():
     assert call(ok, q=K) == hta.HTA_ERR_ALIAS                               # q overlaps k
     assert call(ok, q=X) == hta.HTA_ERR_ALIAS                               # output on input
 
+
+
+# ---- backward entry points: argument checks before any launch
+
+Z1 = ctypes.c_void_p(0x90000000)
+Z2 = ctypes.c_void_p(0xa0000000)
+Z3 = ctypes.c_void_p(0xb0000000)
+L1 = ctypes.c_void_p(0xc0000000)
+D1 = ctypes.c_void_p(0xd0000000)
+
+
+def test_attention_backward_argument_checks():
+    lib = hta.lib()
+    s = shape()
+    need = hta.hta_workspace_bytes(hta.HTA_OP_ATTN_BWD, s, None)
+    assert need > 0
+    # bf16 inputs with an fp32 dout need room for its bf16 copy as well
+    assert hta.hta_workspace_bytes(hta.HTA_OP_ATTN_BWD, shape(out=hta.HTA_F32), None) > need
+
+    def call(fn="hta_swa_bwd", ws=W, wsb=need, a=3, **kw):
+        args = [ctypes.byref(s), kw.get("q", F), G, Hh, kw.get("o", O), kw.get("lse", L1),
+                kw.get("dout", D1), kw.get("dq", Z1), Z2, Z3]
+        tail = [a] if fn == "hta_swa_bwd" else [4, kw.get("dil", 2)]
+        return getattr(lib, fn)(*args, *tail, 0.0, ws, wsb, None)
+
+    assert call(q=None) == hta.HTA_ERR_NULL
+    assert call(lse=None) == hta.HTA_ERR_NULL
+    assert call(dout=None) == hta.HTA_ERR_NULL
+    assert call(ws=None) == hta.HTA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == hta.HTA_ERR_WORKSPACE
+    assert call(a=0) == hta.HTA_ERR_WINDOW
+    assert call(fn="hta_dswa_bwd", dil=0) == hta.HTA_ERR_WINDOW
+    assert call(dq=F) == hta.HTA_ERR_ALIAS            # a gradient over an input
+    assert call(dq=D1) == hta.HTA_ERR_ALIAS           # over dout
+    assert call(dq=W) == hta.HTA_ERR_ALIAS            # over the workspace
+    # the forward with log-sum-exp: lse must not overlap q, k, v or o
+    assert lib.hta_swa_fwd_lse(ctypes.byref(s), F, G, Hh, O, None, 3, 0.0, None) == hta.HTA_ERR_NULL
+    assert lib.hta_swa_fwd_lse(ctypes.byref(s), F, G, Hh, O, O, 3, 0.0, None) == hta.HTA_ERR_ALIAS
+    assert lib.hta_dswa_fwd_lse(ctypes.byref(s), F, G, Hh, O, L1, 0, 2, 0.0, None) == \
+        hta.HTA_ERR_WINDOW
+
+
+def test_gla_backward_argument_checks():
+    lib = hta.lib()
+    s = shape()
+    prm = hta.make_params(chunk=64)
+    need = hta.hta_workspace_bytes(hta.HTA_OP_GLA_BWD, s, prm)
+    assert need > hta.hta_workspace_bytes(hta.HTA_OP_GLA, s, prm)
+    assert hta.hta_workspace_bytes(hta.HTA_OP_GLA_BWD, s, hta.make_params(chunk=32)) == 0
+
+    def call(p=prm, ws=W, wsb=need, **kw):
+        return lib.hta_gla_bwd(ctypes.byref(s), ctypes.byref(p), F, G, Hh, A, Bt,
+                               kw.get("s0", S), kw.get("dout", D1), kw.get("dst", L1),
+                               kw.get("dq", Z1), Z2, Z3, kw.get("da", O),
+                               ctypes.c_void_p(0xe0000000), ws, wsb, None)
+
+    assert call(s0=None) == hta.HTA_ERR_NULL
+    assert call(dst=None) == hta.HTA_ERR_NULL
+    assert call(wsb=need - 1) == hta.HTA_ERR_WORKSPACE
+    assert call(p=hta.make_params(chunk=64, gla_form=2)) == hta.HTA_ERR_UNSUPPORTED
+    assert call(dq=S) == hta.HTA_ERR_ALIAS            # a gradient over the initial state
+    assert call(da=A) == hta.HTA_ERR_ALIAS            # dalpha over alpha
+    assert call(dst=S) == hta.HTA_ERR_ALIAS           # dstate over the initial state
+
+
+def test_hybrid_training_argument_checks():
+    lib = hta.lib()
+    s = shape()
+    prm = hta.make_params()
+    saved = hta.hta_hybrid_saved_bytes(s)
+    # two fp32 branch outputs, two log-sum-exp rows, the initial state
+    L = s.B * s.H * s.T * s.P
+    al = lambda n: (n + 255) // 256 * 256
+    assert saved == 2 * al(L * s.dv * 4) + 2 * al(L * 4) + al(s.B * s.H * s.dk * s.dv * 4)
+    assert hta.hta_hybrid_saved_bytes(shape(B=0)) == 0
+    need_f = hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, s, prm)
+    need_b = hta.hta_workspace_bytes(hta.HTA_OP_HYBRID_BWD, s, prm)
+    assert need_b > hta.hta_workspace_bytes(hta.HTA_OP_GLA_BWD, s, prm)
+    SV = ctypes.c_void_p(0xf0000000)
+    fwd = lambda sv=SV, o=O: lib.hta_hybrid_fwd_train(ctypes.byref(s), ctypes.byref(prm), F, G, Hh,
+                                                      A, Bt, S, o, sv, W, need_f, None)
+    assert fwd(sv=None) == hta.HTA_ERR_NULL
+    assert fwd(sv=O) == hta.HTA_ERR_ALIAS             # saved over o
+    bwd = lambda wsb=need_b, dq=Z1, sv=SV: lib.hta_hybrid_bwd(
+        ctypes.byref(s), ctypes.byref(prm), F, G, Hh, A, Bt, sv, D1, L1, dq, Z2, Z3, O,
+        ctypes.c_void_p(0xe0000000), W, wsb, None)
+    assert bwd(sv=None) == hta.HTA_ERR_NULL
+    assert bwd(wsb=need_b - 1) == hta.HTA_ERR_WORKSPACE
+    assert bwd(dq=SV) == hta.HTA_ERR_ALIAS            # a gradient over the saved activations
