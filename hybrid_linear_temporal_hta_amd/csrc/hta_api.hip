@@ -116,9 +116,16 @@ size_t gla_ws(const hta_shape* s, int chunk) {
 size_t fp32_seq_bytes(const hta_shape* s) {
     return align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 4);
 }
+size_t park_ws(const hta_shape* s) {
+    return align_up(hta::win_attn_park_bytes(s->B * s->H, s->T, s->P));
+}
 size_t partial_ws(const hta_shape* s) {
     if (s->dtype == HTA_F32) return 0;
-    return fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2);
+    return fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2) + park_ws(s);
+}
+// Layout of partial_ws: [GLA partial][attention partial (bf16 o only)][park].
+float* park_of(const hta_shape* s, char* partials) {
+    return reinterpret_cast<float*>(partials + fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2));
 }
 
 // One auxiliary stream and two events per device, created on first use and
@@ -329,6 +336,44 @@ hipError_t run_hybrid_overlapped(const hta::GlaLaunch& g, const hta::WinLaunch& 
     return hta::launch_win_attn(dw, sm);
 }
 
+// hta_swa_dswa_fwd_ex workspace: [park][fp32 branch-A output]; fp32 inputs need none.
+size_t swa_dswa_ws(const hta_shape* s) {
+    if (s->dtype != HTA_BF16) return kAlign;
+    return park_ws(s) + fp32_seq_bytes(s);
+}
+
+// bf16 hybrid (inference): the GLA prep, then the GLA scan on `sm`, beside ONE
+// attention pass on the auxiliary stream that runs both windows with one
+// accumulator set (the query's own frame, common to both, attended once: its
+// softmax state is parked in memory while the SWA taps finish, then resumed for
+// the DSWA taps) into `att` (fp32: o itself, or a partial for a bf16 o); then
+// o = att + the GLA partial, rounded once.
+hipError_t run_hybrid_fused(const hta::GlaLaunch& g, const hta::WinLaunch& w, float* att,
+                            float* park, const hta_params* p, hipStream_t sm) {
+    std::lock_guard<std::mutex> lock(g_aux_mu);
+    Aux* a = nullptr;
+    hipError_t e = aux_for_current_device(&a);
+    if (e != hipSuccess) return e;
+    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
+    if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return e;
+    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaScan)) != hipSuccess) return e;
+    hta::WinLaunch f = w;
+    f.nbr = 3;
+    taps_hybrid(f.taps, p->swa_window, p->dswa_taps, p->dswa_dilation);
+    f.o = att;
+    f.out_f32 = 1;
+    f.oa = att;
+    f.park = park;
+    f.add = nullptr;
+    f.add2 = nullptr;
+    if ((e = hta::launch_win_attn(f, a->s)) != hipSuccess) return e;
+    if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return e;
+    const long long n = (long long)w.BH * w.Tq * w.P * w.d;
+    return hta::launch_add_f32(w.o, w.out_f32 ? 0 : 1, att, static_cast<const float*>(g.o), n, sm);
+}
+
 // What a training forward keeps for hta_hybrid_bwd (caller-owned `saved`).
 struct Saved {
     float* o_swa;      // [BH][L][dv] the SWA branch's output
@@ -472,6 +517,7 @@ size_t hta_workspace_bytes(int op, const hta_shape* shape, const hta_params* par
         return gla_ws(shape, params->gla_chunk);
     }
     if (op == HTA_OP_ATTN_BWD) return attn_bwd_ws(shape);
+    if (op == HTA_OP_SWA_DSWA) return swa_dswa_ws(shape);
     if (op == HTA_OP_HYBRID_BWD) {
         if (check_params(shape, params) != HTA_OK) return 0;
         return hybrid_bwd_ws(shape);
@@ -621,6 +667,45 @@ int hta_swa_dswa_fwd(const hta_shape* s, const hta_params* p, const void* q, con
     w.add = add;
     hipError_t e = run_swa_dswa(w, p->swa_window, p->dswa_taps, p->dswa_dilation,
                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? HTA_OK : hip_fail(e);
+}
+
+int hta_swa_dswa_fwd_ex(const hta_shape* s, const hta_params* p, const void* q, const void* k,
+                        const void* v, const float* add, void* o, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_shape(s)) != HTA_OK) return st;
+    if (!p) return HTA_ERR_NULL;
+    if ((st = check_window(p->swa_window)) != HTA_OK) return st;
+    if ((st = check_dilated(p->dswa_taps, p->dswa_dilation)) != HTA_OK) return st;
+    if ((st = check_scale(p->attn_scale)) != HTA_OK) return st;
+    if (s->dtype != HTA_BF16)   // fp32 inputs: the two-accumulator pass needs no workspace
+        return hta_swa_dswa_fwd(s, p, q, k, v, add, o, stream);
+    if (!q || !k || !v || !o) return HTA_ERR_NULL;
+    const size_t need = swa_dswa_ws(s);
+    if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
+    const Range rq = range_of(q, nq), rk = range_of(k, nq), rv = range_of(v, nv);
+    const Range ro = range_of(o, out_bytes(s)), rw = range_of(workspace, need);
+    if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rw, ro) ||
+        overlap(rw, rq) || overlap(rw, rk) || overlap(rw, rv))
+        return HTA_ERR_ALIAS;
+    if (add) {
+        const Range ra = range_of(add, (size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 4);
+        if (overlap(ra, rq) || overlap(ra, rk) || overlap(ra, rv) || overlap(ra, rw)) return HTA_ERR_ALIAS;
+        const bool in_place = static_cast<const void*>(add) == o && s->out_dtype == HTA_F32;
+        if (!in_place && overlap(ra, ro)) return HTA_ERR_ALIAS;
+    }
+    char* w = static_cast<char*>(workspace);
+    hta::WinLaunch f = win_base(s, q, k, v, o, p->attn_scale);
+    f.nbr = 3;
+    taps_hybrid(f.taps, p->swa_window, p->dswa_taps, p->dswa_dilation);
+    f.park = reinterpret_cast<float*>(w);
+    // branch A's output: o itself when o is fp32 and nothing is added in place
+    f.oa = (s->out_dtype == HTA_F32 && static_cast<const void*>(add) != o)
+               ? static_cast<float*>(o) : reinterpret_cast<float*>(w + park_ws(s));
+    f.add = add;
+    hipError_t e = hta::launch_win_attn(f, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? HTA_OK : hip_fail(e);
 }
 
@@ -908,7 +993,7 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void*
                                     params->gla_scale, workspace, need_gla, params->gla_form);
         g.out_f32 = 1;
         hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
-        hipError_t e = run_hybrid_overlapped(g, w, mid, params, sm);
+        hipError_t e = run_hybrid_fused(g, w, mid, park_of(shape, wsb + need_gla), params, sm);
         return e == hipSuccess ? HTA_OK : hip_fail(e);
     }
     // fp32 inputs: GLA into o, then SWA + DSWA adding it in place.
@@ -1082,7 +1167,8 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, gpart, ctx->p.gla_chunk,
                                     ctx->p.gla_scale, workspace, need_gla, ctx->p.gla_form);
         g.out_f32 = 1;
-        e = run_hybrid_overlapped(g, ring_launch(ctx, s, q, o, n), mid, &ctx->p, sm);
+        e = run_hybrid_fused(g, ring_launch(ctx, s, q, o, n), mid, park_of(&s, wsb + need_gla),
+                             &ctx->p, sm);
         if (e != hipSuccess) return hip_fail(e);
     } else {
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, o, ctx->p.gla_chunk,

@@ -38,11 +38,21 @@ struct WinLaunch {
     int d;                  // dk == dv
     int dtype;              // HTA_F32 / HTA_BF16 (inputs)
     int out_f32;            // 1: o is fp32, 0: o is bf16
-    int nbr;                // 1 or 2 branches
+    int nbr;                // 1 or 2 branches, or 3: both branches with one accumulator
+                            //   set (bf16): the own frame's state is parked in `park`
+                            //   and resumed for branch B after branch A is written to `oa`
     WinTaps taps;
     float* lse;             // optional [BH][Tq*P]: log-sum-exp of the scaled logits (one branch)
     float* obr;             // optional fp32 [BH][Tq*P][dv]: this branch's own output (one branch)
+    float* park;            // nbr 3: scratch, win_attn_park_bytes(BH, Tq, P) bytes
+    float* oa;              // nbr 3: fp32 [BH][Tq*P][dv] for branch A's output (may be o when
+                            //   o is fp32 and no partial is added)
 };
+size_t win_attn_park_bytes(int BH, int Tq, int P);
+
+// dst = a + b elementwise (fp32), written as fp32 or rounded to bf16; n a multiple of 4.
+hipError_t launch_add_f32(void* dst, int dst_bf16, const float* a, const float* b, long long n,
+                          hipStream_t stream);
 
 hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream);
 

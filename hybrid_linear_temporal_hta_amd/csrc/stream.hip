@@ -29,6 +29,38 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ dst,
         dst[i] = src ? src[i] : 0.f;
 }
 
+// dst = a + b over n4 groups of 4 floats; each thread takes 4 groups 256 apart
+// per pass, all loads issued before the stores (more bytes in flight per lane).
+__global__ __launch_bounds__(256) void add_f32_kernel(void* __restrict__ dst, int dst_bf16,
+                                                      const float* a, const float* b, long long n4) {
+    const long long step = (long long)gridDim.x * 1024;
+    for (long long base = (long long)blockIdx.x * 1024 + threadIdx.x; base < n4; base += step) {
+        f32x4 r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const long long i = base + 256 * u;
+            if (i < n4) {
+                const f32x4 x = reinterpret_cast<const f32x4*>(a)[i];
+                const f32x4 y = reinterpret_cast<const f32x4*>(b)[i];
+                r[u] = f32x4{x[0] + y[0], x[1] + y[1], x[2] + y[2], x[3] + y[3]};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const long long i = base + 256 * u;
+            if (i >= n4) break;
+            if (dst_bf16) {
+                bf16x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = f2bf(r[u][j]);
+                reinterpret_cast<bf16x4*>(dst)[i] = o;
+            } else {
+                reinterpret_cast<f32x4*>(dst)[i] = r[u];
+            }
+        }
+    }
+}
+
 unsigned grid_for(long long work) {
     long long g = (work + 255) / 256;
     if (g > 8192) g = 8192;
@@ -51,6 +83,17 @@ hipError_t launch_copy_frames(const void* src, void* dst, int BH, long long src_
                        static_cast<const char*>(src) + src_off * elem_bytes,
                        static_cast<char*>(dst) + dst_off * elem_bytes, BH, src_bh * elem_bytes,
                        dst_bh * elem_bytes, n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_f32(void* dst, int dst_bf16, const float* a, const float* b, long long n,
+                          hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    if (n & 3) return hipErrorInvalidValue;
+    long long g = (n / 4 + 1023) / 1024;
+    if (g > 16384) g = 16384;
+    hipLaunchKernelGGL(add_f32_kernel, dim3((unsigned)(g < 1 ? 1 : g)), dim3(256), 0, stream, dst,
+                       dst_bf16, a, b, n / 4);
     return hipGetLastError();
 }
 

@@ -154,10 +154,43 @@ struct TileCursor {
     const bf16* vf;
 };
 
-// Two waves per SIMD for the single-branch kernel (fits 256 registers without
-// spilling); the fused two-branch kernel keeps two accumulator sets and runs at one.
+// Parked softmax state of one wave (nbr 3): per lane 64 accumulator values, m
+// and l, contiguous (68 floats, 16-byte aligned), so one address per lane plus
+// immediate offsets reaches all of it.
+constexpr int kParkPerLane = 68;
+
+__device__ __forceinline__ void park_store(const Acc& a, float* p) {
+    f32x4* q = reinterpret_cast<f32x4*>(p);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            q[4 * db + g] = f32x4{a.o[db][4 * g], a.o[db][4 * g + 1], a.o[db][4 * g + 2],
+                                  a.o[db][4 * g + 3]};
+    q[16] = f32x4{a.m, a.l, 0.f, 0.f};
+}
+
+__device__ __forceinline__ void park_load(Acc& a, const float* p) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 x = q[4 * db + g];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.o[db][4 * g + i] = x[i];
+        }
+    const f32x4 ml = q[16];
+    a.m = ml[0];
+    a.l = ml[1];
+}
+
+// Two waves per SIMD for the single-accumulator kernels (NBR 1, and NBR 3 which
+// parks the shared own-frame state in memory instead of keeping a second set);
+// the two-set kernel (NBR 2) runs at one.
 template <int NBR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3 - NBR, 3 - NBR)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(NBR == 2 ? 1 : 2, NBR == 2 ? 1 : 2)))
 void win_attn_bf16_kernel(WinLaunch w) {
     __shared__ __attribute__((aligned(1024))) char Kst[2][kTileB];
     __shared__ __attribute__((aligned(1024))) char Vst[2][kTileB];
@@ -184,9 +217,10 @@ void win_attn_bf16_kernel(WinLaunch w) {
 
     // Segments: present taps of branch A, then of branch B.
     const int nSegA = taps_present(w.taps.offA, w.taps.nA, fa);
-    const int nseg = nSegA + (NBR == 2 ? taps_present(w.taps.offB, w.taps.nB, fa) : 0);
+    const int nseg = nSegA + (NBR >= 2 ? taps_present(w.taps.offB, w.taps.nB, fa) : 0);
     const int ntk = (w.P + kBK - 1) / kBK;
     const int nit = nseg * ntk;
+    float* park = NBR == 3 ? w.park + (((size_t)wid * 4 + wave) * 64 + lane) * kParkPerLane : nullptr;
 
     auto seg_base = [&](TileCursor& t) {
         const long long ofs = seg_frame(w, fa, t.sg, nSegA) * w.kv_frame;
@@ -242,8 +276,29 @@ void win_attn_bf16_kernel(WinLaunch w) {
         }
         const int nvalid = min(kBK, w.P - tk * kBK);
         if (wave_rows) {   // waves whose 32 query rows all lie past the frame only stage tiles
-            Acc& acc = (NBR == 1 || sg < nSegA) ? A : Bacc;
+            Acc& acc = (NBR != 2 || sg < nSegA) ? A : Bacc;
             attend_tile(acc, qf, Kst[ST], Vst[ST], L, nvalid, c, lane);
+            if (NBR == 3 && tk == ntk - 1) {
+                // own frame done: park the state branch B resumes from
+                if (sg == 0) park_store(A, park);
+                // branch A done: write its output, resume from the parked state
+                if (sg == nSegA - 1) {
+                    const float inv = 1.f / halves_sum(A.l);
+                    float* oa = w.oa + (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
+                    if (qrow < w.P) {
+#pragma unroll
+                        for (int db = 0; db < 4; ++db)
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const int d0 = db * 32 + 8 * g + 4 * h;
+                                *reinterpret_cast<f32x4*>(oa + d0) =
+                                    f32x4{A.o[db][4 * g] * inv, A.o[db][4 * g + 1] * inv,
+                                          A.o[db][4 * g + 2] * inv, A.o[db][4 * g + 3] * inv};
+                            }
+                    }
+                    park_load(A, park);
+                }
+            }
         }
         if (NBR == 2 && sg == 0 && tk == ntk - 1) Bacc = A;   // own frame seeds branch B
         if (++tk == ntk) { tk = 0; ++sg; }
@@ -266,6 +321,7 @@ void win_attn_bf16_kernel(WinLaunch w) {
     const long long orow = (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
     const float* ap = w.add ? w.add + orow : nullptr;
     const float* ap2 = w.add2 ? w.add2 + orow : nullptr;
+    const float* apa = NBR == 3 ? w.oa + orow : nullptr;   // branch A's output
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -279,6 +335,11 @@ void win_attn_bf16_kernel(WinLaunch w) {
             }
             if (NBR == 1 && w.obr)
                 *reinterpret_cast<f32x4*>(w.obr + orow + d0) = f32x4{r[0], r[1], r[2], r[3]};
+            if (NBR == 3) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(apa + d0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] += x[i];
+            }
             if (ap) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(ap + d0);
 #pragma unroll
@@ -396,13 +457,21 @@ __global__ __launch_bounds__(256) void win_attn_f32_kernel(WinLaunch w) {
 
 }  // namespace
 
+size_t win_attn_park_bytes(int BH, int Tq, int P) {
+    const long long nwg = (long long)BH * Tq * ((P + kBQ - 1) / kBQ);
+    return (size_t)nwg * 4 * kParkPerLane * 64 * sizeof(float);
+}
+
 hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream) {
     if (w.BH == 0 || w.Tq == 0 || w.P == 0) return hipSuccess;
     if (w.dtype == 1) {  // bf16, d == 128
         const int nqt = (w.P + kBQ - 1) / kBQ;
         const long long nwg = (long long)w.BH * w.Tq * nqt;
         if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-        if (w.nbr == 2)
+        if (w.nbr == 3) {
+            if (!w.park || !w.oa) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((win_attn_bf16_kernel<3>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
+        } else if (w.nbr == 2)
             hipLaunchKernelGGL((win_attn_bf16_kernel<2>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
         else
             hipLaunchKernelGGL((win_attn_bf16_kernel<1>), dim3((unsigned)nwg), dim3(256), 0, stream, w);

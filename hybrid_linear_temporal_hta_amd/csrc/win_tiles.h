@@ -89,7 +89,6 @@ struct LaneOffs {
     uint32_t k[8];     // row fragment ks of row n (32-row block 0, stage 0)
     uint32_t v[4];     // transposed fragment of d-block db, rows 4(g/2) + j (block 0, stage 0)
     uint32_t vh[4];    // ... and rows 8 + 4(g/2) + j (swz differs in row bit 3)
-    uint32_t dma[4];   // source offset within a tile of DMA instruction i (row r, slot c)
 };
 
 // Row and column of the chunk that DMA instruction i of `wave` fills for `lane`:
@@ -117,10 +116,6 @@ __device__ __forceinline__ void lane_offsets(LaneOffs& L, int wave, int lane) {
         L.v[db] = r0 * kRowB + 16 * ((col >> 3) ^ swz(r0)) + 8 * ((col >> 2) & 1);
         L.vh[db] = r1 * kRowB + 16 * ((col >> 3) ^ swz(r1)) + 8 * ((col >> 2) & 1);
     }
-    // DMA: wave w, instruction i fills LDS chunks [64 (4w + i), +64) of a tile.
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        L.dma[i] = (uint32_t)(dma_row(wave, i, lane) * kD + dma_col(wave, i, lane)) * 2;
 }
 
 // Enqueue one 64-row tile of each of two tensors straight into LDS (K and V in
@@ -131,11 +126,14 @@ __device__ __forceinline__ void issue_tile(uint32_t ldsK, uint32_t ldsV, const b
                                            const bf16* vb, int nvalid, int wave, int lane,
                                            const LaneOffs& L) {
     if (nvalid == kBK) {
+        // wave w, instruction i fills LDS chunks [64 (4w + i), +64) of a tile (source
+        // offsets recomputed here rather than held in registers)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t off = 1024u * (4 * wave + i);
-            dma16(L.dma[i], kb, ldsK + off);
-            dma16(L.dma[i], vb, ldsV + off);
+            const uint32_t src = (uint32_t)(dma_row(wave, i, lane) * kD + dma_col(wave, i, lane)) * 2;
+            dma16(src, kb, ldsK + off);
+            dma16(src, vb, ldsV + off);
         }
     } else {
 #pragma unroll

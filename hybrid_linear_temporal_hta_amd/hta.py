@@ -37,6 +37,7 @@ HTA_OP_STREAM_STEP = 3
 HTA_OP_ATTN_BWD = 4
 HTA_OP_GLA_BWD = 5
 HTA_OP_HYBRID_BWD = 6
+HTA_OP_SWA_DSWA = 7
 
 HTA_NORM_Q = 1
 HTA_NORM_K = 2
@@ -46,7 +47,7 @@ HTA_GLA_PRINTED = 1       # S = alpha S - beta (S k) k^T + beta v k^T
 
 EXPORTED = (
     "hta_workspace_bytes", "hta_swa_fwd", "hta_dswa_fwd", "hta_swa_fwd_lse", "hta_dswa_fwd_lse",
-    "hta_swa_bwd", "hta_dswa_bwd", "hta_swa_dswa_fwd", "hta_gla_fwd",
+    "hta_swa_bwd", "hta_dswa_bwd", "hta_swa_dswa_fwd", "hta_swa_dswa_fwd_ex", "hta_gla_fwd",
     "hta_gla_fwd_ex", "hta_gla_bwd", "hta_hybrid_fwd", "hta_hybrid_saved_bytes",
     "hta_hybrid_fwd_train", "hta_hybrid_bwd", "hta_project_fwd",
     "hta_stream_init", "hta_stream_step", "hta_status_string", "hta_last_hip_error",
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
     L.hta_swa_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, f, vp, sz, vp]
     L.hta_dswa_bwd.restype = i
     L.hta_dswa_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, f, vp, sz, vp]
+    L.hta_swa_dswa_fwd_ex.restype = i
+    L.hta_swa_dswa_fwd_ex.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.hta_swa_dswa_fwd.restype = i
     L.hta_swa_dswa_fwd.argtypes = [sp, pp, vp, vp, vp, vp, vp, vp]
     L.hta_gla_fwd.restype = i
@@ -256,6 +259,17 @@ def hta_swa_dswa_fwd(q, k, v, o, P: int, params: Params, add=None, stream=None):
     _check(lib().hta_swa_dswa_fwd(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k),
                                   _ptr(v), _ptr(add), _ptr(o), _stream(stream)),
            "hta_swa_dswa_fwd")
+
+
+def hta_swa_dswa_fwd_ex(q, k, v, o, P: int, params: Params, add=None, workspace=None,
+                        stream=None):
+    s = make_shape(q, v, P, o)
+    need = hta_workspace_bytes(HTA_OP_SWA_DSWA, s, params)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().hta_swa_dswa_fwd_ex(ctypes.byref(s), ctypes.byref(params), _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(add), _ptr(o), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)), "hta_swa_dswa_fwd_ex")
 
 
 def hta_gla_fwd(q, k, v, alpha, beta, state, o, P: int, chunk: int = 64, scale: float = 0.0,

@@ -108,6 +108,7 @@ typedef struct {
 #define HTA_OP_ATTN_BWD     4   /* hta_swa_bwd / hta_dswa_bwd (params may be NULL) */
 #define HTA_OP_GLA_BWD      5   /* hta_gla_bwd (params: gla_chunk)                 */
 #define HTA_OP_HYBRID_BWD   6   /* hta_hybrid_bwd                                  */
+#define HTA_OP_SWA_DSWA     7   /* hta_swa_dswa_fwd_ex (params may be NULL)         */
 
 /*
  * hta_workspace_bytes -- device workspace (bytes, 256-byte aligned start
@@ -184,6 +185,20 @@ int hta_swa_dswa_fwd(const hta_shape* shape, const hta_params* params,
                      void* o, void* stream);
 
 /*
+ * hta_swa_dswa_fwd_ex -- hta_swa_dswa_fwd computed in ONE pass over the tap
+ * frames with bf16 inputs: the query's own frame, common to both windows, is
+ * attended once; its softmax state is kept in the workspace while the SWA taps
+ * finish (that branch's output goes to o, or to the workspace), then resumed for
+ * the DSWA taps, and the epilogue adds the two branches (and `add`). Same
+ * arguments, results and aliasing rules as hta_swa_dswa_fwd, plus
+ * workspace >= hta_workspace_bytes(HTA_OP_SWA_DSWA, shape, NULL) not overlapping
+ * any other argument. fp32 inputs behave exactly as hta_swa_dswa_fwd.
+ */
+int hta_swa_dswa_fwd_ex(const hta_shape* shape, const hta_params* params,
+                        const void* q, const void* k, const void* v, const float* add,
+                        void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * hta_gla_fwd -- GLA branch alone (GLA paragraph and update equations), chunked.
  * state: fp32 [B][H][dk][dv] = S^T; in: initial state (zero it for S_0 = 0),
  * out: state after the last token. o: [B][H][L][dv] (o_t = scale * S_t q_t).
@@ -233,13 +248,14 @@ int hta_gla_bwd(const hta_shape* shape, const hta_params* params,
  * hta_hybrid_fwd -- the whole layer (three-branch figure): o = o_swa + o_dswa + o_gla
  * with shared q, k, v; the GLA branch in params->gla_form. state as in hta_gla_fwd. workspace: >=
  * hta_workspace_bytes(HTA_OP_HYBRID, shape, params).
- * bf16 inputs: the GLA branch (into an fp32 partial in the workspace) runs on
- * the library's auxiliary stream, forked from `stream` by an event, beside the
- * SWA pass on `stream` (into o when out_dtype is HTA_F32, else into a second
- * fp32 workspace partial); `stream` then waits for the GLA branch and the
- * DSWA pass adds both partials, rounding once. Everything the call enqueues is
- * ordered after the work already on `stream`, and later work on `stream` is
- * ordered after all of it. The fork/join is serialised across host threads.
+ * bf16 inputs: the GLA chunk scan (into an fp32 partial in the workspace) runs
+ * on `stream` beside the attention, which runs on the library's auxiliary stream
+ * (forked from `stream` by an event) as one pass over both windows (as in
+ * hta_swa_dswa_fwd_ex; into o when out_dtype is HTA_F32, else into a second
+ * fp32 workspace partial); `stream` then waits for it and one elementwise pass
+ * adds the GLA partial, rounding once. Everything the call enqueues is ordered
+ * after the work already on `stream`, and later work on `stream` is ordered
+ * after all of it. The fork/join is serialised across host threads.
  * fp32 inputs: GLA into o, then SWA + DSWA adding it, all on `stream`.
  */
 int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params,

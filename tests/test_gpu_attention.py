@@ -161,3 +161,39 @@ def test_tiny_fp32_workload_all_branches():
     torch.cuda.synchronize()
     assert_parity(o, ref_o, w.dtype, "hybrid")
     assert_parity(st, ref_state, w.dtype, "hybrid state")
+
+
+@pytest.mark.parametrize("B,H,T,P,d,dtype,window,taps,dil", CASES)
+@pytest.mark.parametrize("mode", ["fp32", "bf16", "add", "add_in_place"])
+def test_swa_dswa_one_pass(B, H, T, P, d, dtype, window, taps, dil, mode):
+    """hta_swa_dswa_fwd_ex: both windows in one pass (the shared own frame's
+    softmax state parked and resumed), to fp32 or bf16 outputs, with an added
+    fp32 partial (also in place), against the oracle's SWA + DSWA (+ partial)."""
+    if dtype == torch.float32 and mode == "bf16":
+        pytest.skip("fp32 inputs give fp32 outputs")
+    print(f"[case] one-pass swa+dswa B{B} H{H} T{T} P{P} {dtype} W{window} taps{taps} dil{dil} "
+          f"{mode}", flush=True)
+    w = _workload(B, H, T, P, d, dtype, seed=300 + T * 7 + P, qv_std=1.0, k_std=1.0)
+    x = _gpu(make_inputs(w, frames=T))
+    prm = hta.make_params(window, taps, dil)
+    ref = oracle.swa(x["q"], x["k"], x["v"], T, P, window) + \
+        oracle.dswa(x["q"], x["k"], x["v"], T, P, taps, dil)
+    out_dtype = torch.bfloat16 if mode == "bf16" else torch.float32
+    o = _out(x, out_dtype)
+    add = None
+    if mode.startswith("add"):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(5)
+        part = torch.randn(x["v"].shape, generator=g, device="cuda")
+        ref = ref + f64(part)
+        if mode == "add_in_place":
+            o.copy_(part)
+            add = o
+        else:
+            add = part
+    hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, P, prm, add=add)
+    torch.cuda.synchronize()
+    if mode == "bf16":
+        assert_parity_rounded(o, ref, TOL[dtype], "one-pass bf16-out")
+    else:
+        assert_parity(o, ref, dtype, f"one-pass {mode}")

@@ -37,9 +37,11 @@ def _run(w, x, dout, s0, dsf, prm, out_dtype):
     dst = dsf.clone()
     hta.hta_hybrid_bwd(q, k, v, a, b, saved, dout, dst, dq, dk, dv, da, db, w.P, prm)
     torch.cuda.synchronize()
-    if w.dtype == torch.bfloat16:   # the same kernels in the same order: identical bits
-        assert torch.equal(o, o2), "hta_hybrid_fwd_train output differs from hta_hybrid_fwd"
-    else:   # fp32 inference sums both attention branches in one pass: rounding order differs
+    # inference sums both attention branches in one pass (the training forward keeps
+    # them apart to save each): same results up to rounding order
+    if o.dtype == torch.bfloat16:
+        assert_parity_rounded(o, f64(o2), TOL[w.dtype], "fwd_train vs fwd output")
+    else:
         assert_parity(o, f64(o2), w.dtype, "fwd_train vs fwd output")
     assert torch.equal(st, st2), "final states differ"
     return dict(dq=dq, dk=dk, dv=dv, dalpha=da, dbeta=db, dstate0=dst)
