@@ -2,10 +2,11 @@
 
 One step = one hta_hybrid_fwd call over one batch of the workload B=2, H=16,
 d=128, T=21 frames x P=1560 tokens (L=32760), bf16 q/k/v, fp32 accumulation
-and output, inputs resident in HBM. Inside the call the GLA branch runs on the
-library's auxiliary stream beside the SWA pass; the DSWA pass then adds both
-partials. The dominant kernel's roofline is timed on the same attention
-launches run alone; the GLA branch is timed alone as well. After the forward
+and output, inputs resident in HBM. Inside the call the GLA chunk scan runs
+beside one attention pass over both windows (on the library's auxiliary
+stream); an elementwise pass then adds the GLA partial. The dominant kernel's
+roofline is timed on that attention pass run alone (hta_swa_dswa_fwd_ex); the
+GLA branch is timed alone as well. After the forward
 steps the 64-frame streaming continuation of the same workload is timed
 (reported under "stream"), then the training pair on the same batch (forward
 that saves activations + backward, under "train"), the 336-frame long-horizon
@@ -30,17 +31,24 @@ if ROOT not in sys.path:
 METRIC = "hybrid temporal-attn fwd tokens/s at L=32760,H=16,d=128; % MFMA peak"
 PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0              # MI355X HBM3E
-ATTN_KERNEL = "win_attn_bf16_kernel<1>"   # one branch per pass
-PMC_FILE = os.path.join(ROOT, "profiles", "win_attn_bf16_hybrid_fwd_B2H16L32760_traffic.json")
+ATTN_KERNEL = "win_attn_bf16_kernel<3>"   # both windows in one pass (own frame shared)
+PMC_FILE = os.path.join(ROOT, "profiles", "win_attn_bf16_onepass_hybrid_fwd_B2H16L32760_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "hybrid_linear_temporal_hta_amd", "csrc", "win_attn.hip")
-ATTN_LAUNCHES = 2                   # SWA pass, then DSWA pass (adds the SWA+GLA partial)
+ATTN_LAUNCHES = 1                   # one SWA+DSWA pass per step
 
 
 def attn_flops(w) -> float:
-    """Algorithmic FLOPs of SWA + DSWA: 4 d P^2 per (query frame, tap frame) pair."""
+    """Algorithmic FLOPs of SWA + DSWA: 4 d P^2 per (query frame, tap frame) pair,
+    each branch counted in full (its own frame included)."""
     n_swa = sum(min(w.window, f + 1) for f in range(w.T))
     n_dswa = sum(sum(1 for j in range(w.taps) if f - j * w.dilation >= 0) for f in range(w.T))
     return 4.0 * w.dk * w.P * w.P * (n_swa + n_dswa) * w.B * w.H
+
+
+def attn_flops_executed(w) -> float:
+    """MFMA work the one-pass kernel executes: the query's own frame, common to
+    both windows, is attended once."""
+    return attn_flops(w) - 4.0 * w.dk * w.P * w.P * w.T * w.B * w.H
 
 
 def gla_flops(w) -> float:
@@ -126,6 +134,12 @@ def setup(hta, w, x, dev):
     return prm, state, o, ws
 
 
+def attn_ws(hta, w, x, o, prm, dev):
+    import torch
+    n = hta.hta_workspace_bytes(hta.HTA_OP_SWA_DSWA, hta.make_shape(x["q"], x["v"], w.P, o), prm)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+
+
 def timed_wall(fn, steps, warmup):
     """Wall time (ms) per call of `steps` calls after `warmup`, bracketed by
     device synchronisation."""
@@ -172,8 +186,10 @@ def long_horizon(hta, dev, steps):
     prm, state, o, ws = setup(hta, w, x, dev)
     stream = torch.cuda.current_stream()
     ms = timed_wall(hybrid_call(hta, w, x, state, o, ws, prm, stream), steps, 1)
-    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd(x["q"], x["k"], x["v"], o, w.P, prm,
-                                                        add=o, stream=stream), steps, 0, stream)
+    wsa = attn_ws(hta, w, x, o, prm, dev)
+    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, w.P, prm,
+                                                           workspace=wsa, stream=stream),
+                           steps, 0, stream)
     gla_ms = timed_events(lambda: hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"],
                                                   state, o, w.P, w.chunk, 0.0, ws, stream),
                           steps, 0, stream)
@@ -340,10 +356,11 @@ def main():
                              args.warmup)
     tokens = w.B * w.L
     value = tokens / (ms_per_step / 1e3)
-    # Roofline of the dominant kernel: the same two attention launches, alone on
-    # the stream, timed with HIP events on that stream.
-    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd(x["q"], x["k"], x["v"], o, w.P, prm,
-                                                        add=o, stream=stream),
+    # Roofline of the dominant kernel: the hybrid's attention pass (both windows in
+    # one launch), alone on the stream, timed with HIP events on that stream.
+    wsa = attn_ws(hta, w, x, o, prm, dev)
+    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, w.P, prm,
+                                                           workspace=wsa, stream=stream),
                            args.steps, 1, stream)
     # The GLA branch alone (prep + scan), for its own HBM fraction.
     gla_ms = timed_events(lambda: hta.hta_gla_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"],
@@ -352,13 +369,16 @@ def main():
 
     fl = attn_flops(w)
     launch_ms = attn_ms / ATTN_LAUNCHES
-    fl_launch = fl / ATTN_LAUNCHES       # SWA and DSWA have equal tap-frame counts here
+    fl_launch = fl / ATTN_LAUNCHES
     achieved = fl_launch / (launch_ms / 1e3) / 1e12
+    executed = attn_flops_executed(w) / ATTN_LAUNCHES / (launch_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
                 "traffic": pmc_traffic(), "kernel": ATTN_KERNEL,
                 "launches_per_step": ATTN_LAUNCHES, "flop_per_launch": fl_launch,
-                "avg_launch_ms": round(launch_ms, 4)}
+                "avg_launch_ms": round(launch_ms, 4),
+                "executed_mfma_TFLOPs": round(executed, 2),
+                "executed_frac": round(executed / PEAK_MFMA_BF16_TFLOPS, 4)}
     gb = gla_bytes(w)
     gla = {"kernels": "gla_prep_bf16_kernel + gla_scan_bf16_kernel", "avg_ms": round(gla_ms, 4),
            "algorithmic_bytes": gb, "achieved_GBps": round(gb / (gla_ms / 1e3) / 1e9, 1),
