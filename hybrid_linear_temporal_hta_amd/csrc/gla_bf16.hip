@@ -173,30 +173,52 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
 
 // ------------------------------------------------------------------ scan
 
-// Enqueue chunk c's operand block and the 64-column V tile into an LDS stage.
+// LDS of the scan: two operand stages, then the hand-over from the state waves
+// to the output waves: M0 (the state entering the chunk) and U, both already
+// rounded to the fp16 B fragments the products consume. Fragment k of lane l of
+// column group w sits at ((w * nfrag + k) * 64 + l) * 16: consecutive lanes,
+// consecutive 16-byte slots.
+constexpr int kXchM = 2 * kStageBytes;
+constexpr int kXchU = kXchM + 4 * 4 * 64 * 16;
+constexpr int kScanLds = kXchU + 4 * 2 * 64 * 16;
+static_assert(kScanLds <= 160 * 1024, "scan LDS exceeds one CU");
+
+// Enqueue chunk c's operand block and 64-column V tile into an LDS stage; ow is
+// the issuing wave among the four output waves.
 __device__ __forceinline__ void issue_chunk(char* stage, const GlaLaunch& g, int bh, int tile,
-                                            long long c, long long nch, int wave, int lane) {
+                                            long long c, long long nch, int ow, int lane) {
     const char* blk = static_cast<const char*>(g.ws) + (size_t)((long long)bh * nch + c) * kChunkBytes;
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
-        const int q = 12 * wave + i;
+        const int q = 12 * ow + i;
         dma16(blk + 1024 * q + 16 * lane, stage + 1024 * q);
     }
-    if (wave == 0 && lane < kTailChunks) dma16(blk + kBlockMain + 16 * lane, stage + kBlockMain);
+    if (ow == 0 && lane < kTailChunks) dma16(blk + kBlockMain + 16 * lane, stage + kBlockMain);
     const long long t0 = c * kC;
     const int n = (int)min((long long)kC, g.L - t0);
     const bf16* vb = static_cast<const bf16*>(g.v) + ((long long)bh * g.L + t0) * kD + tile * 64;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int p = 64 * (2 * wave + i) + lane;
+        const int p = 64 * (2 * ow + i) + lane;
         const int tok = p >> 3;
         const int cc = (p & 7) ^ swzv(tok);
-        dma16(vb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * wave + i));
+        dma16(vb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * ow + i));
     }
 }
 
+// One workgroup per (batch, head, 64 value columns), eight waves in two roles
+// that share the column group cg = wave & 3 (16 columns each):
+//   state waves (0..3) carry the recurrence: K M0, X, U = T X and the update of
+//     M; they publish M0 and U to LDS and never touch global memory inside the
+//     loop;
+//   output waves (4..7) issue the next chunk's DMA, store the saved M0 / U when
+//     asked, and form the output O = diag(e^g) Q M0 + Pm U and store it, 16 bytes
+//     per lane.
+// Two barriers per chunk: B1 (chunk c staged, M0 published) and B2 (U published).
+// The arithmetic and its rounding are those of a single wave doing both.
 template <bool OUT_F32>
-__global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gla_scan_bf16_kernel(GlaLaunch g) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
     const int BH = g.BH;
@@ -206,162 +228,199 @@ __global__ __launch_bounds__(256) void gla_scan_bf16_kernel(GlaLaunch g) {
     else { bh = b >> 1; tile = b & 1; }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool state_wave = wave < 4;
+    const int cg = wave & 3;
     const int m = lane & 15, G = lane >> 4;
-    const int colw = wave * 16 + m;             // column inside the workgroup's 64-column tile
-    const int col = tile * 64 + colw;
+    const int col = tile * 64 + cg * 16 + m;
     const long long nch = (g.L + kC - 1) / kC;
-
+    f16x8* xm = reinterpret_cast<f16x8*>(smem + kXchM) + cg * 4 * 64 + lane;   // + 64 k
+    f16x8* xu = reinterpret_cast<f16x8*>(smem + kXchU) + cg * 2 * 64 + lane;
     float* st = g.state + (long long)bh * kD * kD;
-    f32x4 Mr[8];                                   // M[16kb + 4G + i][col]
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Mr[kb][i] = st[(16 * kb + 4 * G + i) * kD + col];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    issue_chunk(smem, g, bh, tile, 0, nch, wave, lane);
-
-    const float scale = g.scale;
-    for (long long c = 0; c < nch; ++c) {
-        wait_vmcnt0();
-        __syncthreads();   // chunk c landed for every wave; the other stage is free
-        if (c + 1 < nch) issue_chunk(smem + ((c + 1) & 1) * kStageBytes, g, bh, tile, c + 1, nch, wave, lane);
-        const char* S = smem + (c & 1) * kStageBytes;
-        const float* esm = reinterpret_cast<const float*>(S + kOffE);
-        const float* dsm = reinterpret_cast<const float*>(S + kOffD);
-        const float* bsm = reinterpret_cast<const float*>(S + kOffB);
-        const float* xsm = reinterpret_cast<const float*>(S + kOffX);
-        if (g.save_m) {   // the state entering this chunk, for a backward pass
-            f16* sm = static_cast<f16*>(g.save_m) + ((long long)bh * nch + c) * kD * kD + col;
+    if (state_wave) {
+        f32x4 Mr[8];                                   // M[16kb + 4G + i][col]
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm[(16 * kb + 4 * G + i) * kD] = (f16)Mr[kb][i];
-        }
-
-        // K M0 and Q M0 (fragments of the critical path read ahead of their use)
-        f16x8 kf[4][4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) kf[rb][ks] = afragK(S + kOffK, 16 * rb + m, ks, G);
+            for (int i = 0; i < 4; ++i) Mr[kb][i] = st[(16 * kb + 4 * G + i) * kD + col];
         f16x8 bM[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) bM[ks] = bfrag(Mr[2 * ks], Mr[2 * ks + 1]);
-        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 KM[4], QM[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            KM[rb] = zero4;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) KM[rb] = mfma16h(kf[rb][ks], bM[ks], KM[rb]);
+        for (int ks = 0; ks < 4; ++ks) {
+            bM[ks] = bfrag(Mr[2 * ks], Mr[2 * ks + 1]);
+            xm[64 * ks] = bM[ks];
         }
-        f16x8 tf[4][2];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-                if (kt == 0 || rb >= 2) tf[rb][kt] = afragT(S + kOffT, 16 * rb + m, kt, G);
-        // Per-token factors of this lane's rows 16rb + 4G + i, four at a time.
-        f32x4 e4[4], d4[4], b4[4], x4[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            e4[rb] = *reinterpret_cast<const f32x4*>(esm + 16 * rb + 4 * G);
-            x4[rb] = *reinterpret_cast<const f32x4*>(xsm + 16 * rb + 4 * G);
-            d4[rb] = *reinterpret_cast<const f32x4*>(dsm + 16 * rb + 4 * G);
-            b4[rb] = *reinterpret_cast<const f32x4*>(bsm + 16 * rb + 4 * G);
-        }
-        // V[16rb + 4G + i][colw], i = 0..3, by one transposed read per row block:
-        // source lane 4j + a addresses token 16rb + 4G + j, columns 16w + 4a .. +3.
-        bf16x4 v4[4];
-        {
-            typedef short s16x4 __attribute__((ext_vector_type(4)));
-            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-            const int j = m >> 2, a = m & 3;
-            const int vc = 16 * wave + 4 * a;
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                const int t = 16 * rb + 4 * G + j;
-                const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(
-                    S + kOffV + t * 128 + 16 * ((vc >> 3) ^ swzv(t)) + 2 * (vc & 7)));
-                v4[rb] = __builtin_bit_cast(bf16x4, r);
-            }
-        }
-        // X = diag(beta) (V - diag(e^g) K M0)
-        f32x4 X[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                X[rb][i] = b4[rb][i] * (bf2f(v4[rb][i]) - x4[rb][i] * KM[rb][i]);
-        const f16x8 xb[2] = {bfrag(X[0], X[1]), bfrag(X[2], X[3])};
-        // U = T X (T lower triangular: row blocks 0,1 only see k-step 0)
-        f32x4 U[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            U[rb] = mfma16h(tf[rb][0], xb[0], zero4);
-            if (rb >= 2) U[rb] = mfma16h(tf[rb][1], xb[1], U[rb]);
-        }
-        if (g.save_u) {
-            f16* su = static_cast<f16*>(g.save_u) + ((long long)bh * nch + c) * kC * kD + col;
+        for (long long c = 0; c < nch; ++c) {
+            __syncthreads();   // B1: chunk c staged; the output waves have M0
+            const char* S = smem + (c & 1) * kStageBytes;
+            const float* esm = reinterpret_cast<const float*>(S + kOffE);
+            const float* dsm = reinterpret_cast<const float*>(S + kOffD);
+            const float* bsm = reinterpret_cast<const float*>(S + kOffB);
+            const float* xsm = reinterpret_cast<const float*>(S + kOffX);
+            // K M0
+            f16x8 kf[4][4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) su[(16 * rb + 4 * G + i) * kD] = (f16)U[rb][i];
-        }
-        f32x4 Us[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Us[rb][i] = U[rb][i] * d4[rb][i];
-        const f16x8 usb[2] = {bfrag(Us[0], Us[1]), bfrag(Us[2], Us[3])};
-        // M = e^{g_C} M0 + K^T diag(e^{g_C - g}) U
-        const float egC = esm[kC - 1];
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            const f16x8 k0 = afragKt(S + kOffK, kb, 0, lane);
-            const f16x8 k1 = afragKt(S + kOffK, kb, 1, lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Mr[kb][i] *= egC;
-            Mr[kb] = mfma16h(k0, usb[0], Mr[kb]);
-            Mr[kb] = mfma16h(k1, usb[1], Mr[kb]);
-        }
-        // O = diag(e^g) Q M0 + Pm U (off the state's dependency chain)
-        if (g.o) {
+                for (int ks = 0; ks < 4; ++ks) kf[rb][ks] = afragK(S + kOffK, 16 * rb + m, ks, G);
+            f32x4 KM[4];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
-                QM[rb] = zero4;
+                KM[rb] = zero4;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) KM[rb] = mfma16h(kf[rb][ks], bM[ks], KM[rb]);
+            }
+            f16x8 tf[4][2];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    if (kt == 0 || rb >= 2) tf[rb][kt] = afragT(S + kOffT, 16 * rb + m, kt, G);
+            // Per-token factors of this lane's rows 16rb + 4G + i, four at a time.
+            f32x4 d4[4], b4[4], x4[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                x4[rb] = *reinterpret_cast<const f32x4*>(xsm + 16 * rb + 4 * G);
+                d4[rb] = *reinterpret_cast<const f32x4*>(dsm + 16 * rb + 4 * G);
+                b4[rb] = *reinterpret_cast<const f32x4*>(bsm + 16 * rb + 4 * G);
+            }
+            // V[16rb + 4G + i][col], i = 0..3, by one transposed read per row block:
+            // source lane 4j + a addresses token 16rb + 4G + j, columns 16cg + 4a .. +3.
+            bf16x4 v4[4];
+            {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                const int j = m >> 2, a = m & 3;
+                const int vc = 16 * cg + 4 * a;
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    const int t = 16 * rb + 4 * G + j;
+                    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(
+                        S + kOffV + t * 128 + 16 * ((vc >> 3) ^ swzv(t)) + 2 * (vc & 7)));
+                    v4[rb] = __builtin_bit_cast(bf16x4, r);
+                }
+            }
+            // X = diag(beta) (V - diag(e^gp) K M0)
+            f32x4 X[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    X[rb][i] = b4[rb][i] * (bf2f(v4[rb][i]) - x4[rb][i] * KM[rb][i]);
+            const f16x8 xb[2] = {bfrag(X[0], X[1]), bfrag(X[2], X[3])};
+            // U = T X (T lower triangular: row blocks 0,1 only see k-step 0)
+            f32x4 U[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                U[rb] = mfma16h(tf[rb][0], xb[0], zero4);
+                if (rb >= 2) U[rb] = mfma16h(tf[rb][1], xb[1], U[rb]);
+            }
+            xu[0] = bfrag(U[0], U[1]);
+            xu[64] = bfrag(U[2], U[3]);
+            f32x4 Us[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Us[rb][i] = U[rb][i] * d4[rb][i];
+            const f16x8 usb[2] = {bfrag(Us[0], Us[1]), bfrag(Us[2], Us[3])};
+            const float egC = esm[kC - 1];
+            __syncthreads();   // B2: U published; the output waves are done with M0
+            // M = e^{g_C} M0 + K^T diag(e^{g_C - g}) U
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                const f16x8 k0 = afragKt(S + kOffK, kb, 0, lane);
+                const f16x8 k1 = afragKt(S + kOffK, kb, 1, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Mr[kb][i] *= egC;
+                Mr[kb] = mfma16h(k0, usb[0], Mr[kb]);
+                Mr[kb] = mfma16h(k1, usb[1], Mr[kb]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                bM[ks] = bfrag(Mr[2 * ks], Mr[2 * ks + 1]);
+                xm[64 * ks] = bM[ks];
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[(16 * kb + 4 * G + i) * kD + col] = Mr[kb][i];
+    } else {
+        const float scale = g.scale;
+        issue_chunk(smem, g, bh, tile, 0, nch, cg, lane);
+        for (long long c = 0; c < nch; ++c) {
+            wait_vmcnt0();     // this wave's part of chunk c has landed
+            __syncthreads();   // B1
+            if (c + 1 < nch) issue_chunk(smem + ((c + 1) & 1) * kStageBytes, g, bh, tile, c + 1, nch, cg, lane);
+            const char* S = smem + (c & 1) * kStageBytes;
+            f16x8 bM[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) bM[ks] = xm[64 * ks];
+            if (g.save_m) {   // the state entering this chunk, for a backward pass
+                f16* sm = static_cast<f16*>(g.save_m) + ((long long)bh * nch + c) * kD * kD + col;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    QM[rb] = mfma16h(afragK(S + kOffQ, 16 * rb + m, ks, G), bM[ks], QM[rb]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sm[(32 * ks + 4 * G + i) * kD] = bM[ks][i];
+                        sm[(32 * ks + 16 + 4 * G + i) * kD] = bM[ks][4 + i];
+                    }
             }
-            const f16x8 ub[2] = {bfrag(U[0], U[1]), bfrag(U[2], U[3])};
-            const long long t0 = c * kC;
-            const bool full = t0 + kC <= g.L;
-            typedef typename std::conditional<OUT_F32, float, bf16>::type OT;
-            OT* obase = static_cast<OT*>(g.o) + ((long long)bh * g.L + t0 + 4 * G) * kD + col;
+            // The output is formed transposed, O^T = M0^T Q^T + U^T Pm^T: an A fragment
+            // and a B fragment of the 16x16x32 product have the same lane layout, so the
+            // same registers serve with the operands swapped, and lane (m, G) ends up
+            // holding O[16 rb + m][16 cg + 4G + i], four adjacent columns of one token.
+            f32x4 QM[4];
+            if (g.o) {
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                f32x4 PU = mfma16h(afragT(S + kOffP, 16 * rb + m, 0, G), ub[0], zero4);
-                if (rb >= 2) PU = mfma16h(afragT(S + kOffP, 16 * rb + m, 1, G), ub[1], PU);
-                OT* orow = obase + 16 * rb * kD;
-                float ov[4];
+                for (int rb = 0; rb < 4; ++rb) {
+                    QM[rb] = zero4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = scale * (e4[rb][i] * QM[rb][i] + PU[i]);
-                if (full) {
+                    for (int ks = 0; ks < 4; ++ks)
+                        QM[rb] = mfma16h(bM[ks], afragK(S + kOffQ, 16 * rb + m, ks, G), QM[rb]);
+                }
+            }
+            __syncthreads();   // B2
+            const f16x8 ub[2] = {xu[0], xu[64]};
+            if (g.save_u) {
+                f16* su = static_cast<f16*>(g.save_u) + ((long long)bh * nch + c) * kC * kD + col;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) orow[i * kD] = (OT)ov[i];
-                } else {
+                for (int k = 0; k < 2; ++k)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (t0 + 16 * rb + 4 * G + i < g.L) orow[i * kD] = (OT)ov[i];
+                    for (int i = 0; i < 4; ++i) {
+                        su[(32 * k + 4 * G + i) * kD] = ub[k][i];
+                        su[(32 * k + 16 + 4 * G + i) * kD] = ub[k][4 + i];
+                    }
+            }
+            if (g.o) {
+                const float* esm = reinterpret_cast<const float*>(S + kOffE);
+                const long long t0 = c * kC;
+                const int c0 = tile * 64 + cg * 16 + 4 * G;
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    f32x4 PU = mfma16h(ub[0], afragT(S + kOffP, 16 * rb + m, 0, G), zero4);
+                    if (rb >= 2) PU = mfma16h(ub[1], afragT(S + kOffP, 16 * rb + m, 1, G), PU);
+                    const int tok = 16 * rb + m;
+                    const float e = esm[tok];
+                    f32x4 ov;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ov[i] = scale * (e * QM[rb][i] + PU[i]);
+                    if (t0 + tok < g.L) {
+                        const long long off = ((long long)bh * g.L + t0 + tok) * kD + c0;
+                        if (OUT_F32) {
+                            *reinterpret_cast<f32x4*>(static_cast<float*>(g.o) + off) = ov;
+                        } else {
+                            bf16x4 ob;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) ob[i] = (bf16)ov[i];
+                            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.o) + off) = ob;
+                        }
+                    }
                 }
             }
         }
+        wait_vmcnt0();
     }
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st[(16 * kb + 4 * G + i) * kD + col] = Mr[kb][i];
 }
 
 }  // namespace
@@ -387,15 +446,15 @@ hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream, int parts) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (!(parts & kGlaScan)) return hipSuccess;
-    const size_t smem = 2 * kStageBytes;   // > 64 KiB: raise the launch limit (current device)
+    const size_t smem = kScanLds;   // > 64 KiB: raise the launch limit (current device)
     const void* fn = g.out_f32 ? reinterpret_cast<const void*>(gla_scan_bf16_kernel<true>)
                                : reinterpret_cast<const void*>(gla_scan_bf16_kernel<false>);
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     if (g.out_f32)
-        hipLaunchKernelGGL(gla_scan_bf16_kernel<true>, dim3((unsigned)(g.BH * 2)), dim3(256), smem, stream, g);
+        hipLaunchKernelGGL(gla_scan_bf16_kernel<true>, dim3((unsigned)(g.BH * 2)), dim3(512), smem, stream, g);
     else
-        hipLaunchKernelGGL(gla_scan_bf16_kernel<false>, dim3((unsigned)(g.BH * 2)), dim3(256), smem, stream, g);
+        hipLaunchKernelGGL(gla_scan_bf16_kernel<false>, dim3((unsigned)(g.BH * 2)), dim3(512), smem, stream, g);
     return hipGetLastError();
 }
 

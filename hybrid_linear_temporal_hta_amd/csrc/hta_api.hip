@@ -42,6 +42,16 @@ Range range_of(const void* p, size_t bytes) {
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
+// Sequence tensors, states, rings, saved activations and workspaces are read and
+// written 16 bytes at a time (mask 15); per-token gates and statistics one float
+// at a time (mask 3). NULL pointers pass.
+template <typename... P>
+int check_align(uintptr_t mask, const P*... p) {
+    uintptr_t bits = 0;
+    ((bits |= reinterpret_cast<uintptr_t>(p)), ...);
+    return (bits & mask) ? HTA_ERR_ALIGN : HTA_OK;
+}
+
 // Shape checks shared by every entry point. L = T*P.
 int check_shape(const hta_shape* s) {
     if (!s) return HTA_ERR_NULL;
@@ -502,6 +512,7 @@ const char* hta_status_string(int status) {
         case HTA_ERR_RING: return "HTA_ERR_RING: ring buffer shorter than the attention windows";
         case HTA_ERR_HIP: return "HTA_ERR_HIP: a HIP runtime call failed";
         case HTA_ERR_ALIAS: return "HTA_ERR_ALIAS: an output overlaps an input";
+        case HTA_ERR_ALIGN: return "HTA_ERR_ALIGN: a device pointer is not aligned as required";
         default: return "unknown hta status";
     }
 }
@@ -539,6 +550,7 @@ static int window_fwd(int kind, const hta_shape* s, const void* q, const void* k
     int st;
     if ((st = check_shape(s)) != HTA_OK) return st;
     if (!q || !k || !v || !o) return HTA_ERR_NULL;
+    if ((st = check_align(15, q, k, v, o)) != HTA_OK) return st;
     if ((st = (kind == 0 ? check_window(a) : check_dilated(a, b))) != HTA_OK) return st;
     if ((st = check_scale(scale)) != HTA_OK) return st;
     const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
@@ -569,6 +581,8 @@ static int window_fwd_lse(int kind, const hta_shape* s, const void* q, const voi
     int st;
     if ((st = check_shape(s)) != HTA_OK) return st;
     if (!q || !k || !v || !o || !lse) return HTA_ERR_NULL;
+    if ((st = check_align(15, q, k, v, o)) != HTA_OK || (st = check_align(3, lse)) != HTA_OK)
+        return st;
     if ((st = (kind == 0 ? check_window(a) : check_dilated(a, b))) != HTA_OK) return st;
     if ((st = check_scale(scale)) != HTA_OK) return st;
     const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
@@ -608,6 +622,9 @@ static int window_bwd(int kind, const hta_shape* s, const void* q, const void* k
     if ((st = check_scale(scale)) != HTA_OK) return st;
     const size_t need = attn_bwd_ws(s);
     if (!ws || ws_bytes < need) return HTA_ERR_WORKSPACE;
+    if ((st = check_align(15, q, k, v, o, dout, dq, dk, dv, ws)) != HTA_OK ||
+        (st = check_align(3, lse)) != HTA_OK)
+        return st;
     const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
     const Range in[6] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
                          range_of(o, out_bytes(s)), range_of(lse, gate_bytes(s)),
@@ -653,6 +670,7 @@ int hta_swa_dswa_fwd(const hta_shape* s, const hta_params* p, const void* q, con
     if ((st = check_dilated(p->dswa_taps, p->dswa_dilation)) != HTA_OK) return st;
     if ((st = check_scale(p->attn_scale)) != HTA_OK) return st;
     if (!q || !k || !v || !o) return HTA_ERR_NULL;
+    if ((st = check_align(15, q, k, v, o, add)) != HTA_OK) return st;
     const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
     const Range rq = range_of(q, nq), rk = range_of(k, nq), rv = range_of(v, nv);
     const Range ro = range_of(o, out_bytes(s));
@@ -684,6 +702,7 @@ int hta_swa_dswa_fwd_ex(const hta_shape* s, const hta_params* p, const void* q, 
     if (!q || !k || !v || !o) return HTA_ERR_NULL;
     const size_t need = swa_dswa_ws(s);
     if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    if ((st = check_align(15, q, k, v, o, add, workspace)) != HTA_OK) return st;
     const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
     const Range rq = range_of(q, nq), rk = range_of(k, nq), rv = range_of(v, nv);
     const Range ro = range_of(o, out_bytes(s)), rw = range_of(workspace, need);
@@ -714,6 +733,10 @@ static int check_gla_buffers(const hta_shape* s, const void* q, const void* k, c
                              const void* o, const void* ws, size_t ws_bytes, size_t ws_need) {
     if (!q || !k || !v || !alpha || !beta || !state || !o) return HTA_ERR_NULL;
     if (!ws || ws_bytes < ws_need) return HTA_ERR_WORKSPACE;
+    int st;
+    if ((st = check_align(15, q, k, v, o, state, ws)) != HTA_OK ||
+        (st = check_align(3, alpha, beta)) != HTA_OK)
+        return st;
     const size_t nq = seq_bytes(s, s->dk), nv = seq_bytes(s, s->dv);
     const Range in[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
                          range_of(alpha, gate_bytes(s)), range_of(beta, gate_bytes(s))};
@@ -780,6 +803,9 @@ int hta_gla_bwd(const hta_shape* shape, const hta_params* params, const void* q,
         return HTA_ERR_NULL;
     const size_t need = gla_bwd_ws(shape);
     if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    if ((st = check_align(15, q, k, v, state0, dout, dstate, dq, dk, dv, workspace)) != HTA_OK ||
+        (st = check_align(3, alpha, beta, dalpha, dbeta)) != HTA_OK)
+        return st;
     const size_t nq = seq_bytes(shape, shape->dk), nv = seq_bytes(shape, shape->dv);
     const Range in[7] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
                          range_of(alpha, gate_bytes(shape)), range_of(beta, gate_bytes(shape)),
@@ -817,6 +843,7 @@ int hta_hybrid_fwd_train(const hta_shape* shape, const hta_params* params, const
     if ((st = check_gla_buffers(shape, q, k, v, alpha, beta, state, o, workspace, workspace_bytes,
                                 need)) != HTA_OK)
         return st;
+    if ((st = check_align(15, saved)) != HTA_OK) return st;
     const size_t nq = seq_bytes(shape, shape->dk), nv = seq_bytes(shape, shape->dv);
     const Range rs = range_of(saved, saved_bytes(shape));
     const Range others[8] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
@@ -877,6 +904,9 @@ int hta_hybrid_bwd(const hta_shape* shape, const hta_params* params, const void*
         return HTA_ERR_NULL;
     const size_t need = hybrid_bwd_ws(shape);
     if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    if ((st = check_align(15, q, k, v, saved, dout, dstate, dq, dk, dv, workspace)) != HTA_OK ||
+        (st = check_align(3, alpha, beta, dalpha, dbeta)) != HTA_OK)
+        return st;
     const size_t nq = seq_bytes(shape, shape->dk), nv = seq_bytes(shape, shape->dv);
     const Range in[7] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),
                          range_of(alpha, gate_bytes(shape)), range_of(beta, gate_bytes(shape)),
@@ -1020,6 +1050,8 @@ int hta_project_fwd(const hta_shape* s, int d_model, const void* x, const void* 
     if (d_model < 64 || d_model % 64 != 0) return HTA_ERR_UNSUPPORTED;
     if (flags & ~(HTA_NORM_Q | HTA_NORM_K)) return HTA_ERR_UNSUPPORTED;
     if (!x || !w || !q || !k || !v || !alpha || !beta) return HTA_ERR_NULL;
+    if ((st = check_align(15, x, w, q, k, v)) != HTA_OK || (st = check_align(3, alpha, beta)) != HTA_OK)
+        return st;
     const long long L = (long long)s->T * s->P;
     const long long M = (long long)s->B * L;
     const long long N = 3LL * s->H * 128 + 2LL * s->H;
@@ -1052,6 +1084,7 @@ static int check_ctx(const hta_stream_ctx* c) {
     if ((st = check_shape(&s1)) != HTA_OK) return st;
     if ((st = check_params(&s1, &c->p)) != HTA_OK) return st;
     if (!c->ring_k || !c->ring_v || !c->state) return HTA_ERR_NULL;
+    if ((st = check_align(15, c->ring_k, c->ring_v, c->state)) != HTA_OK) return st;
     const long long need = (long long)(c->p.dswa_taps - 1) * c->p.dswa_dilation + 1;
     if (c->R < 1 || c->R < c->p.swa_window || c->R < need) return HTA_ERR_RING;
     if (c->n_frames < 0) return HTA_ERR_SHAPE;
@@ -1068,6 +1101,7 @@ int hta_stream_init(hta_stream_ctx* ctx, const void* k_prefix, const void* v_pre
     if ((st = check_ctx(ctx)) != HTA_OK) return st;
     if (T_prefix < 0) return HTA_ERR_SHAPE;
     if (T_prefix > 0 && (!k_prefix || !v_prefix)) return HTA_ERR_NULL;
+    if ((st = check_align(15, k_prefix, v_prefix, state_prefix)) != HTA_OK) return st;
     const hta_shape& s = ctx->s;
     const int BH = s.B * s.H;
     const Range rk = range_of(ctx->ring_k, ring_bytes(ctx, s.dk));
@@ -1130,6 +1164,9 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
     const size_t need_gla = gla_ws(&s, ctx->p.gla_chunk);
     const size_t need = need_gla + (o ? partial_ws(&s) : 0);
     if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
+    if ((st = check_align(15, q, k, v, o, workspace)) != HTA_OK ||
+        (st = check_align(3, alpha, beta)) != HTA_OK)
+        return st;
     const int BH = s.B * s.H;
     const size_t nq = seq_bytes(&s, s.dk), nv = seq_bytes(&s, s.dv);
     const Range in[5] = {range_of(q, nq), range_of(k, nq), range_of(v, nv),

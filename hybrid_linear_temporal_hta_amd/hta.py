@@ -27,6 +27,7 @@ HTA_ERR_WORKSPACE = -6
 HTA_ERR_RING = -7
 HTA_ERR_HIP = -8
 HTA_ERR_ALIAS = -9
+HTA_ERR_ALIGN = -10
 
 HTA_F32 = 0
 HTA_BF16 = 1

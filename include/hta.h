@@ -32,6 +32,11 @@
  *   - All arguments are checked before anything is enqueued. On a non-zero
  *     status nothing has been enqueued and no output, state or ring is touched.
  *   - Outputs must not alias inputs. The state is updated in place.
+ *   - Alignment: every sequence tensor (q, k, v, o, add, dout, dq, dk, dv, the
+ *     projection's x, w, q, k, v), state, ring buffer, saved-activation block
+ *     and workspace must start on a 16-byte boundary; alpha, beta, lse, dalpha
+ *     and dbeta on a 4-byte boundary. Otherwise the call returns HTA_ERR_ALIGN.
+ *     (Fresh torch or hipMalloc allocations are 256-byte aligned.)
  *
  * Readings of the pages that the library implements (where they are silent):
  *   - the SWA window counts the current frame: frames f-W+1..f; attention is
@@ -64,6 +69,7 @@ extern "C" {
 #define HTA_ERR_RING        (-7)  /* ring has fewer frames than the windows reach      */
 #define HTA_ERR_HIP         (-8)  /* a HIP call failed; see hta_last_hip_error()       */
 #define HTA_ERR_ALIAS       (-9)  /* an output overlaps an input                       */
+#define HTA_ERR_ALIGN      (-10)  /* a device pointer is not aligned as required        */
 
 typedef enum { HTA_F32 = 0, HTA_BF16 = 1 } hta_dtype;
 
