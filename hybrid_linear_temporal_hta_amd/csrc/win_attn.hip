@@ -266,7 +266,7 @@ void win_attn_bf16_kernel(WinLaunch w) {
 
     int sg = 0, tk = 0;   // tile being consumed
     // One tile in stage ST (compile-time, so LDS addresses fold into immediates).
-    auto step = [&](int it, auto stage_tag) {
+    auto step = [&](int it, auto stage_tag) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage_tag)::value;
         wait_vmcnt<0>();   // this tile's loads (issued one tile ago) have landed ...
         __syncthreads();   // ... for every wave; and the stage refilled next was read by all
@@ -278,34 +278,47 @@ void win_attn_bf16_kernel(WinLaunch w) {
         if (wave_rows) {   // waves whose 32 query rows all lie past the frame only stage tiles
             Acc& acc = (NBR != 2 || sg < nSegA) ? A : Bacc;
             attend_tile(acc, qf, Kst[ST], Vst[ST], L, nvalid, c, lane);
-            if (NBR == 3 && tk == ntk - 1) {
-                // own frame done: park the state branch B resumes from
-                if (sg == 0) park_store(A, park);
-                // branch A done: write its output, resume from the parked state
-                if (sg == nSegA - 1) {
-                    const float inv = 1.f / halves_sum(A.l);
-                    float* oa = w.oa + (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
-                    if (qrow < w.P) {
-#pragma unroll
-                        for (int db = 0; db < 4; ++db)
-#pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                const int d0 = db * 32 + 8 * g + 4 * h;
-                                *reinterpret_cast<f32x4*>(oa + d0) =
-                                    f32x4{A.o[db][4 * g] * inv, A.o[db][4 * g + 1] * inv,
-                                          A.o[db][4 * g + 2] * inv, A.o[db][4 * g + 3] * inv};
-                            }
-                    }
-                    park_load(A, park);
-                }
-            }
+            // own frame done: park the state branch B resumes from
+            if (NBR == 3 && sg == 0 && tk == ntk - 1) park_store(A, park);
         }
         if (NBR == 2 && sg == 0 && tk == ntk - 1) Bacc = A;   // own frame seeds branch B
         if (++tk == ntk) { tk = 0; ++sg; }
     };
-    for (int it = 0; it < nit; it += 2) {
-        step(it, std::integral_constant<int, 0>{});
-        if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
+    // Tiles [it0, it1) with tile it in stage it & 1 (S0 = it0 & 1).
+    auto run = [&](int it0, int it1, auto first_stage) __attribute__((always_inline)) {
+        constexpr int S0 = decltype(first_stage)::value;
+        for (int it = it0; it < it1; it += 2) {
+            step(it, std::integral_constant<int, S0>{});
+            if (it + 1 < it1) step(it + 1, std::integral_constant<int, S0 ^ 1>{});
+        }
+    };
+    if (NBR == 3) {
+        // Branch A's tiles (own frame first), then branch B's in a loop of their
+        // own: the switch between them -- branch A's output written, the parked
+        // own-frame state reloaded -- stays off the per-tile path, so the
+        // accumulators keep their registers through both loops.
+        const int nitA = nSegA * ntk;
+        run(0, nitA, std::integral_constant<int, 0>{});
+        if (wave_rows) {
+            const float inv = 1.f / halves_sum(A.l);
+            float* oa = w.oa + (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
+            if (qrow < w.P) {
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d0 = db * 32 + 8 * g + 4 * h;
+                        *reinterpret_cast<f32x4*>(oa + d0) =
+                            f32x4{A.o[db][4 * g] * inv, A.o[db][4 * g + 1] * inv,
+                                  A.o[db][4 * g + 2] * inv, A.o[db][4 * g + 3] * inv};
+                    }
+            }
+            park_load(A, park);
+        }
+        if (nitA & 1) run(nitA, nit, std::integral_constant<int, 1>{});
+        else run(nitA, nit, std::integral_constant<int, 0>{});
+    } else {
+        run(0, nit, std::integral_constant<int, 0>{});
     }
 
     // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add) (+ add2), rounded once.

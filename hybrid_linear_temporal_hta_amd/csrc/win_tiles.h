@@ -48,15 +48,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // stage (it cannot tell the buffers apart); completion is tracked by wait_vmcnt.
 // It has no register outputs.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-    // the base is wave-uniform; readfirstlane pins it to SGPRs for the asm operand
+    // the bases are wave-uniform; readfirstlane pins them to SGPRs for the asm operands
     // (readfirstlane returns int: widen each half as uint32_t, never sign-extended)
     const uint64_t b = (uint64_t)(uintptr_t)sbase;
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
     const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);   // uniform too
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds), "v"(voff), "s"(sb)
+                 : "s"(ls), "v"(voff), "s"(sb)
                  : "m0");
 }
 
@@ -67,9 +68,10 @@ __device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t 
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
     const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                  :
-                 : "s"(lds), "v"(voff), "s"(sb)
+                 : "s"(ls), "v"(voff), "s"(sb)
                  : "m0");
 }
 
