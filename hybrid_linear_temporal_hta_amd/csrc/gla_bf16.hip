@@ -53,15 +53,28 @@ using namespace glat;
 
 // ------------------------------------------------------------------ prep
 
-constexpr int kKsP = kD + 8;      // padded K row (bf16)
+constexpr int kKsP = kD + 8;      // padded K / Q row (bf16)
 constexpr int kAsP = 68;          // padded A row (fp32), permuted columns
+static_assert(kC * kKsP * 2 == kC * kAsP * 4, "Q staging shares the A buffer");
+static_assert(kC * kKsP * 2 >= 2 * 64 * 128, "Pm and T staging fit in the K buffer");
 
-__global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
-    __shared__ __attribute__((aligned(16))) bf16 Ks[kC * kKsP];
-    __shared__ __attribute__((aligned(16))) float As[kC * kAsP];   // A[i][(j&3)*16 + (j>>2)]
+// One workgroup per chunk. Phases, separated by barriers:
+//   1. loads: alpha, beta (wave 0), K and Q rows; K and Q kept in LDS as bf16 and
+//      written to the block as fp16; the decay prefix sums (wave 0);
+//   2. K K^T and Q K^T on MFMA, one 32x32 block per wave;
+//   3. A into LDS (the Q buffer), Pm into LDS staging in the block layout;
+//   4. Pm copied out with 16-byte stores beside the forward substitution for T,
+//      whose fp16 result is staged the same way and copied out last.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
+    __shared__ __attribute__((aligned(16))) bf16 Ks[kC * kKsP];   // K; later Pm, T staging
+    __shared__ __attribute__((aligned(16))) float As[kC * kAsP];  // Q (bf16) first, then A[i][(j&3)*16 + (j>>2)]
     __shared__ float gs[kC];
     __shared__ float gps[kC];   // decay exponent of the erase path (see kOffX)
     __shared__ float bs[kC];
+    bf16* Qs = reinterpret_cast<bf16*>(As);
+    char* stP = reinterpret_cast<char*>(Ks);          // Pm, 8 KiB, block layout
+    char* stT = reinterpret_cast<char*>(Ks) + 8192;   // T, 8 KiB, block layout
 
     const int cid = blockIdx.x;
     const int bh = cid / nch, c = cid - bh * nch;
@@ -72,23 +85,35 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
     const bf16* qp = static_cast<const bf16*>(g.q) + ((long long)bh * g.L + t0) * kD;
     char* blk = static_cast<char*>(g.ws) + (size_t)cid * kChunkBytes;
 
+    float alpha_t = 1.f, beta_t = 0.f;
+    if (wave == 0 && lane < n) {
+        alpha_t = g.alpha[(long long)bh * g.L + t0 + lane];
+        beta_t = g.beta[(long long)bh * g.L + t0 + lane];
+    }
+    u32x4 kv[4], qv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int ci = tid + 256 * r, row = ci >> 4, cc = ci & 15;
-        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+        kv[r] = u32x4{0u, 0u, 0u, 0u};
+        qv[r] = u32x4{0u, 0u, 0u, 0u};
         if (row < n) {
-            kv = *reinterpret_cast<const u32x4*>(kp + (long long)row * kD + 8 * cc);
-            qv = *reinterpret_cast<const u32x4*>(qp + (long long)row * kD + 8 * cc);
+            kv[r] = *reinterpret_cast<const u32x4*>(kp + (long long)row * kD + 8 * cc);
+            qv[r] = *reinterpret_cast<const u32x4*>(qp + (long long)row * kD + 8 * cc);
         }
-        *reinterpret_cast<u32x4*>(Ks + row * kKsP + 8 * cc) = kv;
-        *reinterpret_cast<u32x4*>(blk + kOffK + offK(row, 8 * cc)) = bf16x8_to_f16x8(kv);
-        *reinterpret_cast<u32x4*>(blk + kOffQ + offK(row, 8 * cc)) = bf16x8_to_f16x8(qv);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int ci = tid + 256 * r, row = ci >> 4, cc = ci & 15;
+        *reinterpret_cast<u32x4*>(Ks + row * kKsP + 8 * cc) = kv[r];
+        *reinterpret_cast<u32x4*>(Qs + row * kKsP + 8 * cc) = qv[r];
+        *reinterpret_cast<u32x4*>(blk + kOffK + offK(row, 8 * cc)) = bf16x8_to_f16x8(kv[r]);
+        *reinterpret_cast<u32x4*>(blk + kOffQ + offK(row, 8 * cc)) = bf16x8_to_f16x8(qv[r]);
     }
     if (wave == 0) {
         // inclusive prefix sum of log(alpha) over the chunk (alpha = 1 past the end)
         float la = 0.f;
         if (lane < n) {
-            const float lg = logf(g.alpha[(long long)bh * g.L + t0 + lane]);
+            const float lg = logf(alpha_t);
             la = (lg < kLogFloor) ? kLogFloor : lg;   // NaN passes through
         }
 #pragma unroll
@@ -96,42 +121,37 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
             const float y = __shfl_up(la, off, 64);
             if (lane >= off) la += y;
         }
-        const float b = lane < n ? g.beta[(long long)bh * g.L + t0 + lane] : 0.f;
         const float gC = __shfl(la, 63, 64);
         const float prev = __shfl_up(la, 1, 64);
         const float gp = g.form ? (lane == 0 ? 0.f : prev) : la;
         gs[lane] = la;
         gps[lane] = gp;
-        bs[lane] = b;
+        bs[lane] = beta_t;
         reinterpret_cast<float*>(blk + kOffE)[lane] = __expf(la);
         reinterpret_cast<float*>(blk + kOffD)[lane] = __expf(gC - la);
-        reinterpret_cast<float*>(blk + kOffB)[lane] = b;
+        reinterpret_cast<float*>(blk + kOffB)[lane] = beta_t;
         reinterpret_cast<float*>(blk + kOffX)[lane] = __expf(gp);
     }
     __syncthreads();
 
     // K K^T and Q K^T, one 32x32 block per wave.
-    {
-        const int mb = wave >> 1, nb = wave & 1;
-        const int nn = lane & 31, h = lane >> 5;
-        f32x16 kk, qk;
+    const int mb = wave >> 1, nb = wave & 1;
+    const int nn = lane & 31, h = lane >> 5;
+    f32x16 kk, qk;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { kk[i] = 0.f; qk[i] = 0.f; }
-        if (mb >= nb) {
-            const int qrow = mb * 32 + nn;
+    for (int i = 0; i < 16; ++i) { kk[i] = 0.f; qk[i] = 0.f; }
+    if (mb >= nb) {
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + nn) * kKsP + 16 * ks + 8 * h);
-                const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (nb * 32 + nn) * kKsP + 16 * ks + 8 * h);
-                bf16x8 qa;
-                if (qrow < n) qa = *reinterpret_cast<const bf16x8*>(qp + (long long)qrow * kD + 16 * ks + 8 * h);
-                else
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) qa[j] = (bf16)0.f;
-                kk = mfma32(ka, kb, kk);
-                qk = mfma32(qa, kb, qk);
-            }
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + (mb * 32 + nn) * kKsP + 16 * ks + 8 * h);
+            const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (nb * 32 + nn) * kKsP + 16 * ks + 8 * h);
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (mb * 32 + nn) * kKsP + 16 * ks + 8 * h);
+            kk = mfma32(ka, kb, kk);
+            qk = mfma32(qa, kb, qk);
         }
+    }
+    __syncthreads();   // K and Q read by every wave: their buffers are reused below
+    {
         const int j = nb * 32 + nn;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -139,10 +159,17 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
             const float dec = (j <= i) ? __expf(gs[i] - gs[j]) : 0.f;
             const float deca = (j < i) ? __expf(gps[i] - gs[j]) : 0.f;
             As[i * kAsP + (j & 3) * 16 + (j >> 2)] = (j < i) ? bs[i] * deca * kk[e] : 0.f;
-            *reinterpret_cast<f16*>(blk + kOffP + offT(i, j)) = (f16)((j <= i) ? dec * qk[e] : 0.f);
+            *reinterpret_cast<f16*>(stP + offT(i, j)) = (f16)((j <= i) ? dec * qk[e] : 0.f);
         }
     }
     __syncthreads();
+
+    // Pm to the block, 16 bytes per thread and step
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int q = tid + 256 * r;
+        *reinterpret_cast<u32x4*>(blk + kOffP + 16 * q) = *reinterpret_cast<const u32x4*>(stP + 16 * q);
+    }
 
     // T = (I + A)^-1 by forward substitution: lane (col, sub) keeps x_j for j = sub (mod 4).
     {
@@ -152,14 +179,16 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
         for (int m = 0; m < 16; ++m) x[m] = 0.f;
 #pragma unroll
         for (int i = 0; i < kC; ++i) {
-            float part = 0.f;
+            // four partial sums keep the dependency chain of each step short
+            float p4[4] = {0.f, 0.f, 0.f, 0.f};
             const float* arow = As + i * kAsP + sub * 16;
 #pragma unroll
             for (int m4 = 0; m4 < (i + 15) / 16; ++m4) {
                 const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + 4 * m4);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) part += a4[u] * x[4 * m4 + u];
+                for (int u = 0; u < 4; ++u) p4[u] += a4[u] * x[4 * m4 + u];
             }
+            float part = (p4[0] + p4[1]) + (p4[2] + p4[3]);
             part += __shfl_xor(part, 1, 64);
             part += __shfl_xor(part, 2, 64);
             const float xi = (i == col ? 1.f : 0.f) - part;
@@ -167,7 +196,13 @@ __global__ __launch_bounds__(256) void gla_prep_bf16_kernel(GlaLaunch g, int nch
         }
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            *reinterpret_cast<f16*>(blk + kOffT + offT(sub + 4 * m, col)) = (f16)x[m];
+            *reinterpret_cast<f16*>(stT + offT(sub + 4 * m, col)) = (f16)x[m];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int q = tid + 256 * r;
+        *reinterpret_cast<u32x4*>(blk + kOffT + 16 * q) = *reinterpret_cast<const u32x4*>(stT + 16 * q);
     }
 }
 
