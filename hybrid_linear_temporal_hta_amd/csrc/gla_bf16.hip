@@ -58,6 +58,14 @@ constexpr int kAsP = 68;          // padded A row (fp32), permuted columns
 static_assert(kC * kKsP * 2 == kC * kAsP * 4, "Q staging shares the A buffer");
 static_assert(kC * kKsP * 2 >= 2 * 64 * 128, "Pm and T staging fit in the K buffer");
 
+// Lane l reads lane l ^ 1 (resp. l ^ 2) of its quad: DPP quad permutes.
+__device__ __forceinline__ float quad_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
 // One workgroup per chunk. Phases, separated by barriers:
 //   1. loads: alpha, beta (wave 0), K and Q rows; K and Q kept in LDS as bf16 and
 //      written to the block as fp16; the decay prefix sums (wave 0);
@@ -189,8 +197,8 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
                 for (int u = 0; u < 4; ++u) p4[u] += a4[u] * x[4 * m4 + u];
             }
             float part = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-            part += __shfl_xor(part, 1, 64);
-            part += __shfl_xor(part, 2, 64);
+            part += quad_xor1(part);   // sum over the quad's four lanes, in registers
+            part += quad_xor2(part);
             const float xi = (i == col ? 1.f : 0.f) - part;
             if ((i & 3) == sub) x[i >> 2] = xi;
         }
