@@ -224,7 +224,46 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
 constexpr int kXchM = 2 * kStageBytes;
 constexpr int kXchU = kXchM + 4 * 4 * 64 * 16;
 constexpr int kScanLds = kXchU + 4 * 2 * 64 * 16;
-static_assert(kScanLds <= 160 * 1024, "scan LDS exceeds one CU");
+// With the states saved for a backward pass: per output wave, a column-major
+// staging of its 16 columns (kSaveCol bytes per column: up to 128 rows + padding
+// that spreads the banks) for the transposed copy-out.
+constexpr int kSaveCol = 288;
+constexpr int kSaveSt = kScanLds;
+constexpr int kScanLdsSave = kSaveSt + 4 * 16 * kSaveCol;
+static_assert(kScanLdsSave <= 160 * 1024, "scan LDS exceeds one CU");
+
+// Copy a wave's NF fp16 B fragments of its 16 columns -- fragment k holds rows
+// 32k + 4G + i and 32k + 16 + 4G + i (i < 4) of column m -- to the row-major
+// [rows][kD] tensor at dst (which points at the wave's first column): staged
+// column by column in LDS, read back by transposed reads as rows of 8 columns,
+// and stored 16 bytes per lane.
+template <int NF>
+__device__ __forceinline__ void save_rows(char* st, const f16x8 (&fr)[NF], f16* dst, int lane) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int m = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) {
+        *reinterpret_cast<f16x4*>(st + m * kSaveCol + (32 * k + 4 * G) * 2) =
+            f16x4{fr[k][0], fr[k][1], fr[k][2], fr[k][3]};
+        *reinterpret_cast<f16x4*>(st + m * kSaveCol + (32 * k + 16 + 4 * G) * 2) =
+            f16x4{fr[k][4], fr[k][5], fr[k][6], fr[k][7]};
+    }
+    // block q: rows 16 (q >> 1) .. +15, columns 8 (q & 1) .. +7. In a transposed
+    // read, source lane 4j + a addresses staged column c + j at rows r0 + 4a .. +3,
+    // and lane 4a + b receives row r0 + 4a + b of columns c .. c + 3.
+    const int j = m >> 2, a = m & 3;
+#pragma unroll
+    for (int t = 0; t < NF; ++t) {
+        const int q = G + 4 * t, r0 = 16 * (q >> 1), c0 = 8 * (q & 1);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(st + (c0 + j) * kSaveCol + (r0 + 4 * a) * 2));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(st + (c0 + 4 + j) * kSaveCol + (r0 + 4 * a) * 2));
+        *reinterpret_cast<f16x8*>(dst + (r0 + m) * kD + c0) =
+            cat(__builtin_bit_cast(f16x4, lo), __builtin_bit_cast(f16x4, hi));
+    }
+}
 
 // Enqueue chunk c's operand block and 64-column V tile into an LDS stage; ow is
 // the issuing wave among the four output waves.
@@ -399,16 +438,11 @@ void gla_scan_bf16_kernel(GlaLaunch g) {
             f16x8 bM[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) bM[ks] = xm[64 * ks];
-            if (g.save_m) {   // the state entering this chunk, for a backward pass
-                f16* sm = static_cast<f16*>(g.save_m) + ((long long)bh * nch + c) * kD * kD + col;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sm[(32 * ks + 4 * G + i) * kD] = bM[ks][i];
-                        sm[(32 * ks + 16 + 4 * G + i) * kD] = bM[ks][4 + i];
-                    }
-            }
+            if (g.save_m)   // the state entering this chunk, for a backward pass
+                save_rows<4>(smem + kSaveSt + cg * 16 * kSaveCol, bM,
+                             static_cast<f16*>(g.save_m) + ((long long)bh * nch + c) * kD * kD +
+                                 tile * 64 + cg * 16,
+                             lane);
             // The output is formed transposed, O^T = M0^T Q^T + U^T Pm^T: an A fragment
             // and a B fragment of the 16x16x32 product have the same lane layout, so the
             // same registers serve with the operands swapped, and lane (m, G) ends up
@@ -425,16 +459,11 @@ void gla_scan_bf16_kernel(GlaLaunch g) {
             }
             __syncthreads();   // B2
             const f16x8 ub[2] = {xu[0], xu[64]};
-            if (g.save_u) {
-                f16* su = static_cast<f16*>(g.save_u) + ((long long)bh * nch + c) * kC * kD + col;
-#pragma unroll
-                for (int k = 0; k < 2; ++k)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        su[(32 * k + 4 * G + i) * kD] = ub[k][i];
-                        su[(32 * k + 16 + 4 * G + i) * kD] = ub[k][4 + i];
-                    }
-            }
+            if (g.save_u)
+                save_rows<2>(smem + kSaveSt + cg * 16 * kSaveCol, ub,
+                             static_cast<f16*>(g.save_u) + ((long long)bh * nch + c) * kC * kD +
+                                 tile * 64 + cg * 16,
+                             lane);
             if (g.o) {
                 const float* esm = reinterpret_cast<const float*>(S + kOffE);
                 const long long t0 = c * kC;
@@ -489,10 +518,11 @@ hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream, int parts) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (!(parts & kGlaScan)) return hipSuccess;
-    const size_t smem = kScanLds;   // > 64 KiB: raise the launch limit (current device)
+    // > 64 KiB: raise the launch limit (current device)
+    const size_t smem = (g.save_m || g.save_u) ? kScanLdsSave : kScanLds;
     const void* fn = g.out_f32 ? reinterpret_cast<const void*>(gla_scan_bf16_kernel<true>)
                                : reinterpret_cast<const void*>(gla_scan_bf16_kernel<false>);
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScanLdsSave);
     if (e != hipSuccess) return e;
     if (g.out_f32)
         hipLaunchKernelGGL(gla_scan_bf16_kernel<true>, dim3((unsigned)(g.BH * 2)), dim3(512), smem, stream, g);
