@@ -306,45 +306,13 @@ hta::GlaBwdLaunch gla_bwd_base(const hta_shape* s, const hta_params* p, const vo
     return b;
 }
 
-// Training outputs of the attention passes (all optional): each branch's
-// log-sum-exp, and the DSWA branch's own output (the SWA one is `mid`).
+// Training outputs of the attention pass (all optional): each branch's
+// log-sum-exp, and the DSWA branch's own output.
 struct TrainOut {
     float* lse_a = nullptr;
     float* lse_b = nullptr;
     float* obr_b = nullptr;
 };
-
-hipError_t run_hybrid_overlapped(const hta::GlaLaunch& g, const hta::WinLaunch& w, float* mid,
-                                 const hta_params* p, hipStream_t sm,
-                                 const TrainOut& tr = TrainOut()) {
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    Aux* a = nullptr;
-    hipError_t e = aux_for_current_device(&a);
-    if (e != hipSuccess) return e;
-    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
-    if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return e;
-    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaScan)) != hipSuccess) return e;
-    hta::WinLaunch sw = w;
-    sw.nbr = 1;
-    taps_swa(sw.taps, p->swa_window);
-    sw.o = mid;
-    sw.out_f32 = 1;
-    sw.add = nullptr;
-    sw.add2 = nullptr;
-    sw.lse = tr.lse_a;
-    if ((e = hta::launch_win_attn(sw, a->s)) != hipSuccess) return e;
-    if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return e;
-    hta::WinLaunch dw = w;
-    dw.nbr = 1;
-    taps_dswa(dw.taps, p->dswa_taps, p->dswa_dilation);
-    dw.add = mid;
-    dw.add2 = static_cast<const float*>(g.o);
-    dw.lse = tr.lse_b;
-    dw.obr = tr.obr_b;
-    return hta::launch_win_attn(dw, sm);
-}
 
 // hta_swa_dswa_fwd_ex workspace: [park][fp32 branch-A output]; fp32 inputs need none.
 size_t swa_dswa_ws(const hta_shape* s) {
@@ -358,8 +326,11 @@ size_t swa_dswa_ws(const hta_shape* s) {
 // softmax state is parked in memory while the SWA taps finish, then resumed for
 // the DSWA taps) into `att` (fp32: o itself, or a partial for a bf16 o); then
 // o = att + the GLA partial, rounded once.
+// For a training forward, `tr` receives each branch's log-sum-exp and branch B's
+// (DSWA's) output, and `oa` (when given) branch A's (SWA's) output.
 hipError_t run_hybrid_fused(const hta::GlaLaunch& g, const hta::WinLaunch& w, float* att,
-                            float* park, const hta_params* p, hipStream_t sm) {
+                            float* park, const hta_params* p, hipStream_t sm,
+                            const TrainOut& tr = TrainOut(), float* oa = nullptr) {
     std::lock_guard<std::mutex> lock(g_aux_mu);
     Aux* a = nullptr;
     hipError_t e = aux_for_current_device(&a);
@@ -373,10 +344,13 @@ hipError_t run_hybrid_fused(const hta::GlaLaunch& g, const hta::WinLaunch& w, fl
     taps_hybrid(f.taps, p->swa_window, p->dswa_taps, p->dswa_dilation);
     f.o = att;
     f.out_f32 = 1;
-    f.oa = att;
+    f.oa = oa ? oa : att;
     f.park = park;
     f.add = nullptr;
     f.add2 = nullptr;
+    f.lse = tr.lse_a;
+    f.lse2 = tr.lse_b;
+    f.obr = tr.obr_b;
     if ((e = hta::launch_win_attn(f, a->s)) != hipSuccess) return e;
     if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return e;
@@ -859,8 +833,13 @@ int hta_hybrid_fwd_train(const hta_shape* shape, const hta_params* params, const
     if (e != hipSuccess) return hip_fail(e);
     hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
     if (shape->dtype == HTA_BF16) {
+        // the one-pass attention of the inference forward, writing what the backward
+        // reads besides o: the SWA output and both branches' log-sum-exp
         char* wsb = static_cast<char*>(workspace);
         float* gpart = reinterpret_cast<float*>(wsb + need_gla);
+        float* att = shape->out_dtype == HTA_F32
+                         ? static_cast<float*>(o)
+                         : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(shape));
         hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, gpart, params->gla_chunk,
                                     params->gla_scale, workspace, need_gla, params->gla_form);
         g.out_f32 = 1;
@@ -868,7 +847,7 @@ int hta_hybrid_fwd_train(const hta_shape* shape, const hta_params* params, const
         tr.lse_a = sv.lse_swa;
         tr.lse_b = sv.lse_dswa;
         tr.obr_b = sv.o_dswa;
-        e = run_hybrid_overlapped(g, w, sv.o_swa, params, sm, tr);
+        e = run_hybrid_fused(g, w, att, park_of(shape, wsb + need_gla), params, sm, tr, sv.o_swa);
         return e == hipSuccess ? HTA_OK : hip_fail(e);
     }
     // fp32: GLA into o, the SWA pass into saved, the DSWA pass adding both into o

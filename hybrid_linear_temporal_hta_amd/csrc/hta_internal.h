@@ -42,8 +42,11 @@ struct WinLaunch {
                             //   set (bf16): the own frame's state is parked in `park`
                             //   and resumed for branch B after branch A is written to `oa`
     WinTaps taps;
-    float* lse;             // optional [BH][Tq*P]: log-sum-exp of the scaled logits (one branch)
-    float* obr;             // optional fp32 [BH][Tq*P][dv]: this branch's own output (one branch)
+    float* lse;             // optional [BH][Tq*P]: log-sum-exp of the scaled logits (one
+                            //   branch; nbr 3: branch A's)
+    float* lse2;            // nbr 3, optional: branch B's log-sum-exp
+    float* obr;             // optional fp32 [BH][Tq*P][dv]: this branch's own output (one
+                            //   branch; nbr 3: branch B's)
     float* park;            // nbr 3: scratch, win_attn_park_bytes(BH, Tq, P) bytes
     float* oa;              // nbr 3: fp32 [BH][Tq*P][dv] for branch A's output (may be o when
                             //   o is fp32 and no partial is added)

@@ -300,7 +300,10 @@ void win_attn_bf16_kernel(WinLaunch w) {
         const int nitA = nSegA * ntk;
         run(0, nitA, std::integral_constant<int, 0>{});
         if (wave_rows) {
-            const float inv = 1.f / halves_sum(A.l);
+            const float lA = halves_sum(A.l);
+            const float inv = 1.f / lA;
+            if (w.lse && h == 0 && qrow < w.P)
+                w.lse[(long long)bh * w.Tq * w.P + (long long)fq * w.P + qrow] = A.m * w.scale + logf(lA);
             float* oa = w.oa + (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
             if (qrow < w.P) {
 #pragma unroll
@@ -329,6 +332,8 @@ void win_attn_bf16_kernel(WinLaunch w) {
     // exp(scale (s - m)), m in raw logit units
     if (NBR == 1 && w.lse && h == 0)
         w.lse[(long long)bh * w.Tq * w.P + (long long)fq * w.P + qrow] = A.m * w.scale + logf(lA);
+    if (NBR == 3 && w.lse2 && h == 0)   // branch B's (the resumed state's)
+        w.lse2[(long long)bh * w.Tq * w.P + (long long)fq * w.P + qrow] = A.m * w.scale + logf(lA);
     float invB = 0.f;
     if (NBR == 2) invB = 1.f / halves_sum(Bacc.l);
     const long long orow = (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
@@ -346,7 +351,7 @@ void win_attn_bf16_kernel(WinLaunch w) {
                 r[i] = A.o[db][4 * g + i] * invA;
                 if (NBR == 2) r[i] += Bacc.o[db][4 * g + i] * invB;
             }
-            if (NBR == 1 && w.obr)
+            if ((NBR == 1 || NBR == 3) && w.obr)   // this branch's (nbr 3: branch B's) output
                 *reinterpret_cast<f32x4*>(w.obr + orow + d0) = f32x4{r[0], r[1], r[2], r[3]};
             if (NBR == 3) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(apa + d0);
