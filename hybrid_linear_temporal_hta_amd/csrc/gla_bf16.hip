@@ -54,9 +54,9 @@ using namespace glat;
 // ------------------------------------------------------------------ prep
 
 constexpr int kKsP = kD + 8;      // padded K / Q row (bf16)
-constexpr int kAsP = 68;          // padded A row (fp32), permuted columns
-static_assert(kC * kKsP * 2 == kC * kAsP * 4, "Q staging shares the A buffer");
-static_assert(kC * kKsP * 2 >= 2 * 64 * 128, "Pm and T staging fit in the K buffer");
+constexpr int kAsP = 68;          // padded A / T row (fp32)
+static_assert(kC * kKsP * 2 == kC * kAsP * 4, "Q staging shares the A buffer; T the K buffer");
+static_assert(kC * kKsP * 2 >= 64 * 128, "Pm and T staging fit in a buffer");
 
 // Lane l reads lane l ^ 1 (resp. l ^ 2) of its quad: DPP quad permutes.
 __device__ __forceinline__ float quad_xor1(float x) {
@@ -66,23 +66,38 @@ __device__ __forceinline__ float quad_xor2(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
 
+// 16x16x16 fp32 product on v_mfma_f32_16x16x4_f32: acc += X Y for 16x16 blocks X
+// (row stride xld) and Y (row stride yld) in LDS; lane l ends with rows
+// 4 (l / 16) + i of column l % 16.
+__device__ __forceinline__ f32x4 mm16f(const float* X, int xld, const float* Y, int yld,
+                                       f32x4 acc, int lane) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * xld + 4 * s + g], Y[(4 * s + g) * yld + m],
+                                                   acc, 0, 0, 0);
+    return acc;
+}
+
 // One workgroup per chunk. Phases, separated by barriers:
 //   1. loads: alpha, beta (wave 0), K and Q rows; K and Q kept in LDS as bf16 and
 //      written to the block as fp16; the decay prefix sums (wave 0);
 //   2. K K^T and Q K^T on MFMA, one 32x32 block per wave;
 //   3. A into LDS (the Q buffer), Pm into LDS staging in the block layout;
-//   4. Pm copied out with 16-byte stores beside the forward substitution for T,
-//      whose fp16 result is staged the same way and copied out last.
+//   4. Pm copied out with 16-byte stores; T = (I + A)^-1 in fp32 by 16x16 blocks
+//      (the K buffer): each wave inverts one diagonal block by forward
+//      substitution, then the blocks below the diagonal follow in three levels of
+//      products, T_ik = -T_ii sum_{k <= j < i} A_ij T_jk (from (I + A) T = I);
+//      T is staged in fp16 in the block layout (the A buffer) and copied out last.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
-    __shared__ __attribute__((aligned(16))) bf16 Ks[kC * kKsP];   // K; later Pm, T staging
-    __shared__ __attribute__((aligned(16))) float As[kC * kAsP];  // Q (bf16) first, then A[i][(j&3)*16 + (j>>2)]
+    __shared__ __attribute__((aligned(16))) bf16 Ks[kC * kKsP];   // K; then Pm staging, then T (fp32)
+    __shared__ __attribute__((aligned(16))) float As[kC * kAsP];  // Q (bf16); then A; then T staging[i][(j&3)*16 + (j>>2)]
     __shared__ float gs[kC];
     __shared__ float gps[kC];   // decay exponent of the erase path (see kOffX)
     __shared__ float bs[kC];
     bf16* Qs = reinterpret_cast<bf16*>(As);
     char* stP = reinterpret_cast<char*>(Ks);          // Pm, 8 KiB, block layout
-    char* stT = reinterpret_cast<char*>(Ks) + 8192;   // T, 8 KiB, block layout
 
     const int cid = blockIdx.x;
     const int bh = cid / nch, c = cid - bh * nch;
@@ -166,7 +181,7 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
             const int i = mb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
             const float dec = (j <= i) ? __expf(gs[i] - gs[j]) : 0.f;
             const float deca = (j < i) ? __expf(gps[i] - gs[j]) : 0.f;
-            As[i * kAsP + (j & 3) * 16 + (j >> 2)] = (j < i) ? bs[i] * deca * kk[e] : 0.f;
+            As[i * kAsP + j] = (j < i) ? bs[i] * deca * kk[e] : 0.f;
             *reinterpret_cast<f16*>(stP + offT(i, j)) = (f16)((j <= i) ? dec * qk[e] : 0.f);
         }
     }
@@ -179,32 +194,61 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
         *reinterpret_cast<u32x4*>(blk + kOffP + 16 * q) = *reinterpret_cast<const u32x4*>(stP + 16 * q);
     }
 
-    // T = (I + A)^-1 by forward substitution: lane (col, sub) keeps x_j for j = sub (mod 4).
+    // Diagonal block kb = wave of T by forward substitution: lane (column c, sub)
+    // keeps x_r for the block's rows r = 4 m + sub (entries not yet solved are 0,
+    // and so is A on and above the diagonal, so every product term is safe).
+    float* Ts = reinterpret_cast<float*>(Ks);   // T, fp32 [64][kAsP]
     {
-        const int col = wave * 16 + (lane >> 2), sub = lane & 3;
-        float x[16];
+        const int kb = wave, c = lane >> 2, sub = lane & 3;
+        const float* Ab = As + 16 * kb * kAsP + 16 * kb;
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 16; ++m) x[m] = 0.f;
-#pragma unroll
-        for (int i = 0; i < kC; ++i) {
-            // four partial sums keep the dependency chain of each step short
-            float p4[4] = {0.f, 0.f, 0.f, 0.f};
-            const float* arow = As + i * kAsP + sub * 16;
-#pragma unroll
-            for (int m4 = 0; m4 < (i + 15) / 16; ++m4) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + 4 * m4);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) p4[u] += a4[u] * x[4 * m4 + u];
-            }
-            float part = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+        for (int i = 0; i < 16; ++i) {
+            const float* ar = Ab + i * kAsP + sub;
+            float part = (ar[0] * x[0] + ar[4] * x[1]) + (ar[8] * x[2] + ar[12] * x[3]);
             part += quad_xor1(part);   // sum over the quad's four lanes, in registers
             part += quad_xor2(part);
-            const float xi = (i == col ? 1.f : 0.f) - part;
+            const float xi = (i == c ? 1.f : 0.f) - part;
             if ((i & 3) == sub) x[i >> 2] = xi;
         }
+        __syncthreads();   // the Pm staging (same buffer) has been copied out
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
-            *reinterpret_cast<f16*>(stT + offT(sub + 4 * m, col)) = (f16)x[m];
+        for (int m = 0; m < 4; ++m) Ts[(16 * kb + 4 * m + sub) * kAsP + 16 * kb + c] = x[m];
+    }
+    __syncthreads();
+    // Blocks (k + d, k) at level d, wave k: S = sum_j A_ij T_jk, then T_ik = -T_ii S
+    // (S staged in the block's own slot: each wave reads it back before overwriting).
+    {
+        const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+        const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+            if (wave < 4 - d) {
+                const int k = wave, i = k + d;
+                f32x4 sacc = zero4;
+                for (int j = k; j < i; ++j)
+                    sacc = mm16f(As + 16 * i * kAsP + 16 * j, kAsP, Ts + 16 * j * kAsP + 16 * k, kAsP,
+                                 sacc, lane);
+                float* Tik = Ts + 16 * i * kAsP + 16 * k;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tik[(4 * g + r) * kAsP + n] = sacc[r];
+                const f32x4 t = mm16f(Ts + 16 * i * kAsP + 16 * i, kAsP, Tik, kAsP, zero4, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Tik[(4 * g + r) * kAsP + n] = -t[r];
+            }
+            __syncthreads();
+        }
+    }
+    // T (lower triangular, unit diagonal) in fp16, staged in the block layout in the A buffer
+    char* stT = reinterpret_cast<char*>(As);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int q = tid + 256 * r, i = q >> 3, j0 = (q & 7) * 8;
+        const float* tr = Ts + i * kAsP + j0;
+        f16x8 h8;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) h8[u] = (f16)((j0 + u <= i) ? tr[u] : 0.f);
+        *reinterpret_cast<f16x8*>(stT + offT(i, j0)) = h8;
     }
     __syncthreads();
 #pragma unroll
