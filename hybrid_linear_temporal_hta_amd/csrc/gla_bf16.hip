@@ -19,11 +19,11 @@
 //
 // Two kernels:
 //   prep (one workgroup per chunk, all chunks in parallel): g, A and Pm from
-//     K K^T and Q K^T on v_mfma_f32_32x32x16_bf16, T by a register-resident
-//     forward substitution in fp32, and the chunk's operand block -- K, Q (fp16),
-//     T, Pm (fp16), e^{g}, e^{g_C - g}, beta, e^{gp} (fp32) -- written
-//     contiguously in exactly the LDS layout the scan consumes (bank-conflict-free
-//     swizzles included).
+//     K K^T and Q K^T on v_mfma_f32_32x32x16_bf16, T in fp32 by 16x16 blocks
+//     (diagonal blocks by forward substitution, the blocks below them by fp32
+//     MFMA products), and the chunk's operand block -- K, Q (fp16), T, Pm
+//     (fp16), e^{g}, e^{g_C - g}, beta, e^{gp} (fp32) -- written contiguously in
+//     exactly the LDS layout the scan consumes (swizzles included).
 //
 // The printed form of the update (GlaLaunch::form = 1: the erase term uses the
 // state before the forget gate, S_t = alpha S - beta (S k) k^T + beta v k^T)
@@ -31,14 +31,15 @@
 // term of X take e^{g_{i-1}} (exclusive cumulative sum, "gp") instead of e^{g_i}.
 // Pm, the output and the state update are the same.
 //   scan (one workgroup per (batch, head, 64 value columns), chunks in order):
-//     each wave owns 16 value columns of the fp32 state as eight 16x16 MFMA
-//     accumulator tiles. K M0, Q M0, T X, Pm U and K^T U run on
-//     v_mfma_f32_16x16x32_f16; the B operands that are previous results (M0,
-//     X, U) come straight from accumulator registers (token order permuted
-//     identically in A and B), and K^T fragments are transposed LDS reads of
-//     row-major K. The next chunk's operand block and value tile stream into
-//     the other half of a two-stage LDS ring with direct global->LDS loads
-//     while the current chunk computes.
+//     eight waves in two roles over the same 16-column groups. State waves hold
+//     their 16 value columns of the fp32 state as eight 16x16 MFMA accumulator
+//     tiles and run the recurrence (K M0, T X, K^T U on v_mfma_f32_16x16x32_f16;
+//     the B operands that are previous results -- M0, X, U -- come straight
+//     from accumulator registers, token order permuted identically in A and B;
+//     K^T fragments are transposed LDS reads of row-major K). Output waves
+//     stream the next chunk's operand block and value tile into the other half
+//     of a two-stage LDS ring with direct global->LDS loads, and form and store
+//     the output from the M0 and U the state waves hand over in LDS.
 #include <type_traits>
 
 #include "device_common.h"

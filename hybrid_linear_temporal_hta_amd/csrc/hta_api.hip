@@ -215,19 +215,15 @@ void taps_hybrid(hta::WinTaps& t, int window, int taps, int dil) {
     for (int j = 1; j < taps; ++j) t.offB[j - 1] = j * dil;
 }
 
-// SWA + DSWA (+ w.add) into w.o. Split (default): an SWA pass into an fp32
-// buffer (o itself, or the caller's fp32 partial), then a DSWA pass adding it;
-// each pass keeps one accumulator set and runs at two waves per SIMD. Fused:
-// one pass sharing the query's own frame between the branches (21% fewer MFMA
-// operations) but two accumulator sets, hence one wave per SIMD: measured
-// 8.6 ms vs 5.5 ms for split on the B2 H16 L32760 workload.
-#ifndef HTA_FUSED_BRANCHES
-#define HTA_FUSED_BRANCHES 0
-#endif
+// SWA + DSWA (+ w.add) into w.o without a workspace (hta_swa_dswa_fwd, the fp32
+// hybrid and stream paths; the bf16 hybrid runs the one-pass kernel, which
+// parks state in a workspace). Split: an SWA pass into an fp32 buffer (o itself,
+// or the caller's fp32 partial), then a DSWA pass adding it; each pass keeps one
+// accumulator set and runs at two waves per SIMD. With a bf16 o and no fp32
+// partial to accumulate in: one pass with two accumulator sets (one wave per
+// SIMD), which rounds the sum once without an intermediate buffer.
 hipError_t run_swa_dswa(hta::WinLaunch w, int window, int taps, int dil, hipStream_t st) {
-    // bf16 output with no fp32 partial to accumulate in: the fused pass, which
-    // rounds the sum once without an intermediate buffer.
-    if (HTA_FUSED_BRANCHES || w.dtype != HTA_BF16 || (!w.out_f32 && !w.add)) {
+    if (w.dtype != HTA_BF16 || (!w.out_f32 && !w.add)) {
         w.nbr = 2;
         taps_hybrid(w.taps, window, taps, dil);
         return hta::launch_win_attn(w, st);

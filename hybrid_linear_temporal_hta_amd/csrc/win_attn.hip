@@ -20,11 +20,12 @@
 //     global->LDS loads (16 bytes per lane, no register round trip), issued
 //     one tile ahead; A fragments of V^T are transposed LDS reads
 //     (ds_read_b64_tr_b16) of the row-major V tile;
-//   * one branch per launch by default: the SWA pass writes its fp32 partial
-//     (plus the optional added partial), the DSWA pass adds onto it. A fused
-//     two-branch variant (the query's own frame, common to both, processed
-//     once and its softmax state seeding the second branch) exists but needs
-//     more registers, which halves occupancy; the split passes run faster;
+//   * three forms (NBR): one branch per launch (the SWA pass writes its fp32
+//     partial, the DSWA pass adds onto it); both branches in one launch with
+//     one accumulator set (the hybrid's pass: the query's own frame, common to
+//     both, is attended once, its softmax state parked in a workspace while the
+//     SWA taps finish and resumed for the DSWA taps); both branches with two
+//     live accumulator sets (no workspace, one wave per SIMD);
 //   * running max is updated lazily (only when a logit exceeds it by more than
 //     8 in log2 units), so the O rescale is rare; exp2 with the log2(e) scale
 //     folded into one FMA;
