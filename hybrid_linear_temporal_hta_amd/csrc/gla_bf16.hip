@@ -102,6 +102,8 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
 
     const int cid = blockIdx.x;
     const int bh = cid / nch, c = cid - bh * nch;
+    if (g.done && cid == 0)   // the scan's completion counters start from zero
+        for (int i = threadIdx.x; i < g.BH; i += 256) g.done[i] = 0;
     const long long t0 = (long long)c * kC;
     const int n = (int)min((long long)kC, g.L - t0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -537,6 +539,11 @@ void gla_scan_bf16_kernel(GlaLaunch g) {
             }
         }
         wait_vmcnt0();
+    }
+    if (g.done) {   // every thread's stores made visible device-wide, then this workgroup counted
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(g.done + bh, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

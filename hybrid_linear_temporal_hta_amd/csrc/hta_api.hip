@@ -129,13 +129,32 @@ size_t fp32_seq_bytes(const hta_shape* s) {
 size_t park_ws(const hta_shape* s) {
     return align_up(hta::win_attn_park_bytes(s->B * s->H, s->T, s->P));
 }
+// The hybrid's hand-off between the GLA scan and the attention pass: one
+// completion counter per head, one pending flag per attention wave.
+size_t sync_ws(const hta_shape* s) {
+    return align_up((size_t)s->B * s->H * sizeof(unsigned)) +
+           align_up(hta::win_pend_bytes(s->B * s->H, s->T, s->P));
+}
 size_t partial_ws(const hta_shape* s) {
     if (s->dtype == HTA_F32) return 0;
-    return fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2) + park_ws(s);
+    return fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2) + park_ws(s) + sync_ws(s);
 }
-// Layout of partial_ws: [GLA partial][attention partial (bf16 o only)][park].
-float* park_of(const hta_shape* s, char* partials) {
-    return reinterpret_cast<float*>(partials + fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2));
+// Layout of partial_ws: [GLA partial][attention partial (bf16 o only)][park]
+// [scan counters][pending flags].
+struct Partials {
+    float* park;
+    unsigned* done;
+    unsigned char* pend;
+};
+Partials partials_of(const hta_shape* s, char* partials) {
+    char* c = partials + fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2);
+    Partials pt;
+    pt.park = reinterpret_cast<float*>(c);
+    c += park_ws(s);
+    pt.done = reinterpret_cast<unsigned*>(c);
+    c += align_up((size_t)s->B * s->H * sizeof(unsigned));
+    pt.pend = reinterpret_cast<unsigned char*>(c);
+    return pt;
 }
 
 // One auxiliary stream and two events per device, created on first use and
@@ -146,6 +165,7 @@ float* park_of(const hta_shape* s, char* partials) {
 struct Aux {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
+    int cus = 0;   // compute units of the device
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_aux_mu;
@@ -162,6 +182,7 @@ hipError_t aux_for_current_device(Aux** out) {   // g_aux_mu held
         e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) {
             if (n.join) (void)hipEventDestroy(n.join);
             if (n.fork) (void)hipEventDestroy(n.fork);
@@ -266,13 +287,6 @@ hipError_t run_gla(const hta::GlaLaunch& g, hipStream_t st) {
     return g.dtype == HTA_F32 ? hta::launch_gla_f32(g, st) : hta::launch_gla_bf16(g, st);
 }
 
-// bf16 hybrid: the GLA prep (chunk-parallel, the whole chip) on `sm`, then the
-// GLA scan (one workgroup per (b, h, 64 value columns), latency-bound) also on
-// `sm`, while the SWA pass (into fp32 `mid`) runs on the auxiliary stream,
-// forked from `sm` after the prep. The scan is next in its queue when the prep
-// ends, so its few workgroups take their CUs before the attention workgroups
-// (which can never share a CU with a scan workgroup: LDS) fill the chip. The
-// DSWA pass waits for the SWA pass and adds both partials, writing w.o.
 size_t gla_bwd_ws(const hta_shape* s) {
     return align_up(hta::gla_bwd_workspace_bytes(s->dtype, s->B * s->H, (long long)s->T * s->P,
                                                  s->dk));
@@ -316,40 +330,63 @@ size_t swa_dswa_ws(const hta_shape* s) {
     return park_ws(s) + fp32_seq_bytes(s);
 }
 
-// bf16 hybrid (inference): the GLA prep, then the GLA scan on `sm`, beside ONE
-// attention pass on the auxiliary stream that runs both windows with one
-// accumulator set (the query's own frame, common to both, attended once: its
-// softmax state is parked in memory while the SWA taps finish, then resumed for
-// the DSWA taps) into `att` (fp32: o itself, or a partial for a bf16 o); then
-// o = att + the GLA partial, rounded once.
+// bf16 hybrid: the GLA prep (chunk-parallel, the whole chip), then the GLA scan
+// (one workgroup per (b, h, 64 value columns), latency-bound) on `sm`, beside
+// ONE attention pass on the auxiliary stream, forked after the prep, that runs
+// both windows with one accumulator set (the query's own frame, common to both,
+// attended once: its softmax state is parked in memory while the SWA taps
+// finish, then resumed for the DSWA taps). The scan is next in its queue when
+// the prep ends, so its few workgroups take their CUs before the attention
+// workgroups (which can never share a CU with a scan workgroup) fill the chip.
+// When the attention pass spans several waves of workgroups, it adds the GLA
+// partial itself wherever the scan has already finished that head (a counter
+// per head, read once per wave, never waited on); the rows it finished earlier
+// go to `att` (fp32: o itself, or a partial for a bf16 o) and a last kernel adds
+// the partial to those only, rounding once. Both routes sum in the same order,
+// so the result does not depend on the timing. A pass of one wave (a streamed
+// frame) ends long after its scan, all at once: there the partial is added by
+// one kernel after it, which keeps the extra reads out of the pass's tail.
 // For a training forward, `tr` receives each branch's log-sum-exp and branch B's
 // (DSWA's) output, and `oa` (when given) branch A's (SWA's) output.
-hipError_t run_hybrid_fused(const hta::GlaLaunch& g, const hta::WinLaunch& w, float* att,
-                            float* park, const hta_params* p, hipStream_t sm,
+hipError_t run_hybrid_fused(hta::GlaLaunch g, const hta::WinLaunch& w, float* att,
+                            const Partials& pt, const hta_params* p, hipStream_t sm,
                             const TrainOut& tr = TrainOut(), float* oa = nullptr) {
     std::lock_guard<std::mutex> lock(g_aux_mu);
     Aux* a = nullptr;
     hipError_t e = aux_for_current_device(&a);
     if (e != hipSuccess) return e;
-    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
-    if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return e;
-    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaScan)) != hipSuccess) return e;
     hta::WinLaunch f = w;
     f.nbr = 3;
     taps_hybrid(f.taps, p->swa_window, p->dswa_taps, p->dswa_dilation);
-    f.o = att;
-    f.out_f32 = 1;
     f.oa = oa ? oa : att;
-    f.park = park;
-    f.add = nullptr;
+    f.park = pt.park;
     f.add2 = nullptr;
     f.lse = tr.lse_a;
     f.lse2 = tr.lse_b;
     f.obr = tr.obr_b;
+    // The scan signals completion (each workgroup writes its XCD's L2 back)
+    // only when the pass reads the signal.
+    const bool handoff = hta::win_attn_workgroups(f) > 2LL * a->cus;
+    if (handoff) {
+        g.done = pt.done;
+        f.add = static_cast<const float*>(g.o);
+        f.add_ready = pt.done;
+        f.add_need = 2;   // the head's two scan workgroups
+        f.part = att;
+        f.pend = pt.pend;
+    } else {
+        f.o = att;
+        f.out_f32 = 1;
+        f.add = nullptr;
+    }
+    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
+    if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return e;
+    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaScan)) != hipSuccess) return e;
     if ((e = hta::launch_win_attn(f, a->s)) != hipSuccess) return e;
     if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return e;
+    if (handoff) return hta::launch_win_add_pending(f, sm);
     const long long n = (long long)w.BH * w.Tq * w.P * w.d;
     return hta::launch_add_f32(w.o, w.out_f32 ? 0 : 1, att, static_cast<const float*>(g.o), n, sm);
 }
@@ -843,7 +880,7 @@ int hta_hybrid_fwd_train(const hta_shape* shape, const hta_params* params, const
         tr.lse_a = sv.lse_swa;
         tr.lse_b = sv.lse_dswa;
         tr.obr_b = sv.o_dswa;
-        e = run_hybrid_fused(g, w, att, park_of(shape, wsb + need_gla), params, sm, tr, sv.o_swa);
+        e = run_hybrid_fused(g, w, att, partials_of(shape, wsb + need_gla), params, sm, tr, sv.o_swa);
         return e == hipSuccess ? HTA_OK : hip_fail(e);
     }
     // fp32: GLA into o, the SWA pass into saved, the DSWA pass adding both into o
@@ -998,7 +1035,7 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void*
                                     params->gla_scale, workspace, need_gla, params->gla_form);
         g.out_f32 = 1;
         hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
-        hipError_t e = run_hybrid_fused(g, w, mid, park_of(shape, wsb + need_gla), params, sm);
+        hipError_t e = run_hybrid_fused(g, w, mid, partials_of(shape, wsb + need_gla), params, sm);
         return e == hipSuccess ? HTA_OK : hip_fail(e);
     }
     // fp32 inputs: GLA into o, then SWA + DSWA adding it in place.
@@ -1179,7 +1216,7 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, gpart, ctx->p.gla_chunk,
                                     ctx->p.gla_scale, workspace, need_gla, ctx->p.gla_form);
         g.out_f32 = 1;
-        e = run_hybrid_fused(g, ring_launch(ctx, s, q, o, n), mid, park_of(&s, wsb + need_gla),
+        e = run_hybrid_fused(g, ring_launch(ctx, s, q, o, n), mid, partials_of(&s, wsb + need_gla),
                              &ctx->p, sm);
         if (e != hipSuccess) return hip_fail(e);
     } else {

@@ -50,7 +50,18 @@ struct WinLaunch {
     float* park;            // nbr 3: scratch, win_attn_park_bytes(BH, Tq, P) bytes
     float* oa;              // nbr 3: fp32 [BH][Tq*P][dv] for branch A's output (may be o when
                             //   o is fp32 and no partial is added)
+    const unsigned* add_ready;  // nbr 3, optional [BH]: `add` of head bh is complete once
+                            //   add_ready[bh] >= add_need, read once per wave, never waited
+                            //   on; a wave that finds it incomplete writes its rows without
+                            //   the add to `part` and flags them in `pend`
+    unsigned add_need;
+    float* part;            // with add_ready: fp32 [BH][Tq*P][dv] (may be o when o is fp32)
+    unsigned char* pend;    // with add_ready: one byte per (workgroup, wave), win_pend_bytes
 };
+size_t win_pend_bytes(int BH, int Tq, int P);
+long long win_attn_workgroups(const WinLaunch& w);   // of launch_win_attn (bf16 inputs)
+// o = part + add for the rows a win_attn pass (nbr 3, add_ready set) flagged in pend.
+hipError_t launch_win_add_pending(const WinLaunch& w, hipStream_t stream);
 size_t win_attn_park_bytes(int BH, int Tq, int P);
 
 // dst = a + b elementwise (fp32), written as fp32 or rounded to bf16; n a multiple of 4.
@@ -135,6 +146,9 @@ struct GlaLaunch {
     size_t ws_bytes;
     void* save_m;           // optional fp16 [BH][nch][d][d]: the state entering each chunk
     void* save_u;           // optional fp16 [BH][nch][64][d]: each chunk's U (bf16 path)
+    unsigned* done;         // optional [BH] (bf16 path): the prep zeroes it; each of a head's
+                            //   two scan workgroups adds 1 once its output rows are visible
+                            //   device-wide, so a head's output is complete at 2
 };
 
 // Backward of the GLA branch over one sequence per (b,h): given dL/do and

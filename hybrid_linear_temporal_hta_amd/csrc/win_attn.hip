@@ -325,6 +325,15 @@ void win_attn_bf16_kernel(WinLaunch w) {
         run(0, nit, std::integral_constant<int, 0>{});
     }
 
+    // Hybrid: `add` is taken only if its producer has finished this head;
+    // otherwise the rows go to `part` without it, flagged for the pending pass.
+    bool pending = false;
+    if (NBR == 3 && w.add_ready && wave_rows) {
+        const unsigned r = __hip_atomic_load(w.add_ready + bh, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        pending = __builtin_amdgcn_readfirstlane(r) < w.add_need;
+        if (lane == 0) w.pend[(size_t)wid * 4 + wave] = pending ? 1 : 0;
+    }
+
     // Epilogue: o = O_A / l_A (+ O_B / l_B) (+ add) (+ add2), rounded once.
     if (qrow >= w.P) return;
     const float lA = halves_sum(A.l);
@@ -338,7 +347,7 @@ void win_attn_bf16_kernel(WinLaunch w) {
     float invB = 0.f;
     if (NBR == 2) invB = 1.f / halves_sum(Bacc.l);
     const long long orow = (long long)bh * w.q_bh + ((long long)fq * w.P + qrow) * kD;
-    const float* ap = w.add ? w.add + orow : nullptr;
+    const float* ap = (w.add && !pending) ? w.add + orow : nullptr;
     const float* ap2 = w.add2 ? w.add2 + orow : nullptr;
     const float* apa = NBR == 3 ? w.oa + orow : nullptr;   // branch A's output
 #pragma unroll
@@ -369,7 +378,9 @@ void win_attn_bf16_kernel(WinLaunch w) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) r[i] += x[i];
             }
-            if (w.out_f32) {
+            if (pending) {
+                *reinterpret_cast<f32x4*>(w.part + orow + d0) = f32x4{r[0], r[1], r[2], r[3]};
+            } else if (w.out_f32) {
                 *reinterpret_cast<f32x4*>(static_cast<float*>(w.o) + orow + d0) =
                     f32x4{r[0], r[1], r[2], r[3]};
             } else {
@@ -379,6 +390,36 @@ void win_attn_bf16_kernel(WinLaunch w) {
                 *reinterpret_cast<bf16x4*>(static_cast<bf16*>(w.o) + orow + d0) = ov;
             }
         }
+}
+
+// The rows a hybrid pass left in `part` (flagged per wave): o = part + add, the
+// same sum the pass forms when `add` is ready, rounded once. One workgroup per
+// attention workgroup (same index and rows), one wave per 32 rows.
+__global__ __launch_bounds__(256) void win_add_pending_kernel(WinLaunch w) {
+    const int nqt = (w.P + kBQ - 1) / kBQ;
+    const int wid = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int qt = wid % nqt;
+    const int fq = w.Tq - 1 - (wid / nqt) % w.Tq;
+    const int bh = wid / (nqt * w.Tq);
+    const int row0 = qt * kBQ + wave * 32;
+    if (row0 >= w.P || !w.pend[(size_t)wid * 4 + wave]) return;
+    const int n4 = min(32, w.P - row0) * (kD / 4);
+    const long long base = (long long)bh * w.q_bh + ((long long)fq * w.P + row0) * kD;
+    const f32x4* pp = reinterpret_cast<const f32x4*>(w.part + base);
+    const f32x4* ap = reinterpret_cast<const f32x4*>(w.add + base);
+    for (int i = lane; i < n4; i += 64) {
+        const f32x4 x = pp[i], y = ap[i];
+        const f32x4 r = {x[0] + y[0], x[1] + y[1], x[2] + y[2], x[3] + y[3]};
+        if (w.out_f32) {
+            reinterpret_cast<f32x4*>(static_cast<float*>(w.o) + base)[i] = r;
+        } else {
+            bf16x4 ov;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ov[j] = f2bf(r[j]);
+            reinterpret_cast<bf16x4*>(static_cast<bf16*>(w.o) + base)[i] = ov;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -481,6 +522,25 @@ size_t win_attn_park_bytes(int BH, int Tq, int P) {
     return (size_t)nwg * 4 * kParkPerLane * 64 * sizeof(float);
 }
 
+long long win_attn_workgroups(const WinLaunch& w) {
+    return (long long)w.BH * w.Tq * ((w.P + kBQ - 1) / kBQ);
+}
+
+size_t win_pend_bytes(int BH, int Tq, int P) {
+    const long long nqt = (P + kBQ - 1) / kBQ;
+    return (size_t)BH * Tq * nqt * 4;
+}
+
+hipError_t launch_win_add_pending(const WinLaunch& w, hipStream_t stream) {
+    if (w.BH == 0 || w.Tq == 0 || w.P == 0) return hipSuccess;
+    if (w.dtype != 1 || w.d != kD || !w.add || !w.part || !w.pend) return hipErrorInvalidValue;
+    const int nqt = (w.P + kBQ - 1) / kBQ;
+    const long long nwg = (long long)w.BH * w.Tq * nqt;
+    if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(win_add_pending_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, w);
+    return hipGetLastError();
+}
+
 hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream) {
     if (w.BH == 0 || w.Tq == 0 || w.P == 0) return hipSuccess;
     if (w.dtype == 1) {  // bf16, d == 128
@@ -489,6 +549,7 @@ hipError_t launch_win_attn(const WinLaunch& w, hipStream_t stream) {
         if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
         if (w.nbr == 3) {
             if (!w.park || !w.oa) return hipErrorInvalidValue;
+            if (w.add_ready && (!w.add || w.add2 || !w.part || !w.pend)) return hipErrorInvalidValue;
             hipLaunchKernelGGL((win_attn_bf16_kernel<3>), dim3((unsigned)nwg), dim3(256), 0, stream, w);
         } else if (w.nbr == 2)
             hipLaunchKernelGGL((win_attn_bf16_kernel<2>), dim3((unsigned)nwg), dim3(256), 0, stream, w);

@@ -16,7 +16,7 @@ Usage:
   python -m hybrid_linear_temporal_hta_amd.profiling stats CSV --out FILE --command CMD
   python -m hybrid_linear_temporal_hta_amd.profiling traffic --kernel SUBSTR \\
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N \\
-      --source FILE --out FILE --command CMD
+      --source FILE --out FILE --command CMD [--last N]
 """
 from __future__ import annotations
 
@@ -107,19 +107,24 @@ def trace_by_grid(path: str, prefix: str = "hta::"):
     return out
 
 
-def counter_per_dispatch(path: str, counter: str, kernel: str):
+def counter_per_dispatch(path: str, counter: str, kernel: str, last: int = 0):
     """Mean over dispatches of `kernel` (substring) of one counter's value, and
-    the dispatch count. Values of one dispatch spread over several rows (one per
-    counter dimension) are summed first."""
+    the dispatch count; with `last`, over the last that many dispatches only.
+    Values of one dispatch spread over several rows (one per counter dimension)
+    are summed first."""
     per = {}
     with open(_find(path, "counter_collection.csv")) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter or kernel not in r["Kernel_Name"]:
                 continue
-            d = r["Dispatch_Id"]
+            d = int(r["Dispatch_Id"])
             per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
     if not per:
         raise ValueError(f"no {counter} rows for kernel {kernel!r} in {path}")
+    if last:
+        if len(per) < last:
+            raise ValueError(f"{len(per)} dispatches of {kernel!r} in {path}, fewer than {last}")
+        per = {d: per[d] for d in sorted(per)[-last:]}
     return sum(per.values()) / len(per), len(per)
 
 
@@ -148,8 +153,8 @@ def cmd_stats(a):
 def cmd_traffic(a):
     cf, ncf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
     cw, ncw = counter_per_dispatch(a.copy_write, "WRITE_SIZE", COPY_KERNEL)
-    kf, nkf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
-    kw, nkw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    kf, nkf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel, a.last)
+    kw, nkw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel, a.last)
     # the copy kernel reads and writes copy_bytes each: bytes per counted KiB
     f_fetch = a.copy_bytes / cf
     f_write = a.copy_bytes / cw
@@ -182,6 +187,8 @@ def main(argv=None):
     for k in ("kernel", "fetch", "write", "copy_fetch", "copy_write", "source", "out", "command"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--copy-bytes", dest="copy_bytes", type=float, required=True)
+    t.add_argument("--last", type=int, default=0,
+                   help="only the last N dispatches of the kernel (default: all)")
     a = ap.parse_args(argv)
     (cmd_stats if a.cmd == "stats" else cmd_traffic)(a)
 

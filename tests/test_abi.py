@@ -146,9 +146,12 @@ def test_workspace_bytes_rules():
     part = (part + 255) // 256 * 256
     park = so.B * so.H * so.T * ((so.P + 127) // 128) * 4 * 64 * 68 * 4
     park = (park + 255) // 256 * 256
+    # the hybrid's hand-off: a scan counter per head, a pending flag per attention wave
+    up = lambda n: (n + 255) // 256 * 256
+    sync = up(so.B * so.H * 4) + up(so.B * so.H * so.T * ((so.P + 127) // 128) * 4)
     gla = hta.hta_workspace_bytes(hta.HTA_OP_GLA, so, prm)
-    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, so, prm) == gla + part + park
-    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape(), prm) == gla + 2 * part + park
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, so, prm) == gla + part + park + sync
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape(), prm) == gla + 2 * part + park + sync
     assert hta.hta_workspace_bytes(hta.HTA_OP_SWA_DSWA, so, None) == park + part
     # fp32 inputs run the branches in sequence with the GLA partial in o
     f32 = shape(dtype=hta.HTA_F32, d=64)

@@ -126,6 +126,52 @@ def test_hybrid_full_size_sampled():
     assert_parity(f64(o).reshape(-1, 128)[rows], ref, w.dtype, "hybrid full-size sampled o")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_hybrid_handoff_bitwise(out_dtype):
+    """The hybrid's attention pass adds the GLA partial itself for every head
+    whose scan has finished when a wave reaches its epilogue, and leaves the other
+    rows (flagged) to a last pass; both routes form the same fp32 sum in the same
+    order, so at the benchmark workload (B2 H16 T21 P1560 bf16) the output equals,
+    bit for bit, the GLA partial added by a separate one-pass attention call,
+    whatever mix of routes the timing produced (printed from the flags)."""
+    w = WORKLOADS["hybrid_stream"]
+    print(f"[case] hybrid hand-off {w.name} out {out_dtype}", flush=True)
+    x = make_inputs(w, device="cuda", frames=w.T)
+    q, k, v = x["q"], x["k"], x["v"]
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    o = torch.empty(w.B, w.H, w.L, 128, dtype=out_dtype, device="cuda")
+    shp = hta.make_shape(q, v, w.P, o)
+    ws = torch.zeros(hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shp, prm), dtype=torch.uint8,
+                     device="cuda")
+    st = torch.zeros(w.B, w.H, 128, 128, device="cuda")
+    hta.hta_hybrid_fwd(q, k, v, x["alpha"], x["beta"], st, o, w.P, prm, workspace=ws)
+    torch.cuda.synchronize()
+    # the hand-off region: [GLA blocks][fp32 partials][park][counters][flags]
+    up = lambda n: (n + 255) // 256 * 256
+    BH, nqt = w.B * w.H, (w.P + 127) // 128
+    off = hta.hta_workspace_bytes(hta.HTA_OP_GLA, shp, prm) + \
+        up(BH * w.L * 128 * 4) * (1 if out_dtype == torch.float32 else 2) + \
+        up(BH * w.T * nqt * 4 * 64 * 68 * 4)
+    counters = ws[off:off + BH * 4].cpu().view(torch.int32)
+    off += up(BH * 4)
+    flags = ws[off:off + BH * w.T * nqt * 4].cpu().numpy().reshape(-1, nqt, 4)
+    used = (np.arange(nqt)[:, None] * 128 + np.arange(4)[None, :] * 32) < w.P
+    fl = flags[:, used]
+    print(f"[handoff] waves adding in the pass: {int((fl == 0).sum())}, "
+          f"left to the last pass: {int((fl == 1).sum())}", flush=True)
+    assert torch.all(counters == 2), "every head's two scan workgroups counted"
+    assert np.all((fl == 0) | (fl == 1))
+    gp = torch.empty(w.B, w.H, w.L, 128, dtype=torch.float32, device="cuda")
+    st2 = torch.zeros_like(st)
+    hta.hta_gla_fwd(q, k, v, x["alpha"], x["beta"], st2, gp, w.P, w.chunk)
+    ref = torch.empty_like(o)
+    hta.hta_swa_dswa_fwd_ex(q, k, v, ref, w.P, prm, add=gp)
+    torch.cuda.synchronize()
+    assert torch.equal(st, st2)
+    bits = torch.int32 if out_dtype == torch.float32 else torch.int16
+    assert torch.equal(o.view(bits), ref.view(bits)), "hybrid differs from GLA + attention"
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_gla_printed_form_parity(dtype):
     """The printed update (forget gate not applied to the erase term) against the
