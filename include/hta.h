@@ -257,9 +257,12 @@ int hta_gla_bwd(const hta_shape* shape, const hta_params* params,
  * bf16 inputs: the GLA chunk scan (into an fp32 partial in the workspace) runs
  * on `stream` beside the attention, which runs on the library's auxiliary stream
  * (forked from `stream` by an event) as one pass over both windows (as in
- * hta_swa_dswa_fwd_ex; into o when out_dtype is HTA_F32, else into a second
- * fp32 workspace partial); `stream` then waits for it and one elementwise pass
- * adds the GLA partial, rounding once. Everything the call enqueues is ordered
+ * hta_swa_dswa_fwd_ex). Where the scan has already finished a head when the pass
+ * completes a block of its rows, the pass adds the GLA partial and writes o
+ * itself; the other rows go to o (HTA_F32) or a second fp32 workspace partial,
+ * and after `stream` waits for the pass, one more kernel adds the GLA partial to
+ * those rows. Either way o is the same fp32 sum rounded once, independent of the
+ * timing. Everything the call enqueues is ordered
  * after the work already on `stream`, and later work on `stream` is ordered
  * after all of it. The fork/join is serialised across host threads.
  * fp32 inputs: GLA into o, then SWA + DSWA adding it, all on `stream`.
