@@ -538,10 +538,21 @@ __device__ __forceinline__ void mm_cc(const f16* A, int lda, const f16* Bt, int 
     }
 }
 
-// Sum over the 16 lanes of a lane group (the 16 columns of a tile row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a lane group (the 16 columns of a tile row), in
+// registers: xor 1 and xor 2 inside each quad, then rotations by 4 and by 8
+// inside the 16-lane row (DPP). Every lane of the group ends with the sum (the
+// additions are associated differently per lane; callers read one lane). All 64
+// lanes must be active.
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-    for (int s = 1; s < 16; s <<= 1) v += __shfl_xor(v, s, 64);
+    v += dpp_mov<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_mov<0x124>(v);   // row_ror:4
+    v += dpp_mov<0x128>(v);   // row_ror:8
     return v;
 }
 
@@ -568,8 +579,40 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     const float sig = sigma_of(*w.maxbits);
     const long long tok0 = (long long)bh * b.L + t0;   // first token row of the chunk
     const long long ci = (long long)bh * nch + c;      // chunk index
+    // Pm at this lane's phase-4 positions (rows 16 mt + 4G + i, column 16 wave + m),
+    // fetched with the other operands rather than inside phase 4
+    const char* pmb = w.blocks + (size_t)ci * kChunkBytes + kOffP;
+    f16 pmv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        pmv[r] = *reinterpret_cast<const f16*>(pmb + offT(16 * (r >> 2) + 4 * G + (r & 3), 16 * wave + m));
 
-    // ---- phase 0: stage operands (rows >= n zero) and per-token factors
+    // ---- phase 0: stage operands (rows >= n zero) and per-token factors. Every
+    // global operand of the chunk is requested first, so that the loads are in
+    // flight together; dM_C and V stay in registers until they are used.
+    const f16* m0g = w.save_m + ci * kD * kD;
+    const f16* dmg = w.dme + ci * kD * kD;
+    bf16x8 kin[4], qin[4], vin[4];
+    f16x8 gin[4], rin[4], uin[4], m0in[8], dmin[8];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+        if (row < n) {
+            const long long tr = (tok0 + row) * kD + c8, cr = (ci * kC + row) * kD + c8;
+            kin[it] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.k) + tr);
+            qin[it] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.q) + tr);
+            vin[it] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.v) + tr);
+            gin[it] = *reinterpret_cast<const f16x8*>(w.gh + tr);
+            rin[it] = *reinterpret_cast<const f16x8*>(w.dr + cr);
+            uin[it] = *reinterpret_cast<const f16x8*>(w.save_u + cr);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+        m0in[it] = *reinterpret_cast<const f16x8*>(m0g + row * kD + c8);
+        dmin[it] = *reinterpret_cast<const f16x8*>(dmg + row * kD + c8);
+    }
     if (wave == 0) {
         float la = 0.f, a = 1.f;
         if (lane < n) {
@@ -596,17 +639,17 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
         dgp[lane] = 0.f;
         dbt[lane] = 0.f;
     }
-    for (int e = tid; e < kC * 16; e += 256) {   // 16-byte pieces of 64 rows x 128
-        const int row = e >> 4, c8 = (e & 15) * 8;
+    // (the chunk's global operands were all requested at the top: see phase 0)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {   // 16-byte pieces of 64 rows x 128
+        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
         f16x8 kk, qq, gg, rr, uu;
         if (row < n) {
-            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.k) + (tok0 + row) * kD + c8);
-            const bf16x8 qv = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.q) + (tok0 + row) * kD + c8);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { kk[i] = (f16)bf2f(kv[i]); qq[i] = (f16)bf2f(qv[i]); }
-            gg = *reinterpret_cast<const f16x8*>(w.gh + (tok0 + row) * kD + c8);
-            rr = *reinterpret_cast<const f16x8*>(w.dr + (ci * kC + row) * kD + c8);
-            uu = *reinterpret_cast<const f16x8*>(w.save_u + (ci * kC + row) * kD + c8);
+            for (int i = 0; i < 8; ++i) { kk[i] = (f16)bf2f(kin[it][i]); qq[i] = (f16)bf2f(qin[it][i]); }
+            gg = gin[it];
+            rr = rin[it];
+            uu = uin[it];
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) { kk[i] = 0; qq[i] = 0; gg[i] = 0; rr[i] = 0; uu[i] = 0; }
@@ -621,16 +664,13 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
             QT[(c8 + i) * kLc + row] = qq[i];
         }
     }
-    const f16* m0g = w.save_m + ci * kD * kD;
-    const f16* dmg = w.dme + ci * kD * kD;
     float sdot = 0.f;   // <dM_C, M0>
-    for (int e = tid; e < kD * 16; e += 256) {
-        const int row = e >> 4, c8 = (e & 15) * 8;
-        const f16x8 mv = *reinterpret_cast<const f16x8*>(m0g + row * kD + c8);
-        const f16x8 dv = *reinterpret_cast<const f16x8*>(dmg + row * kD + c8);
-        *reinterpret_cast<f16x8*>(Mb + row * kLd + c8) = mv;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sdot += (float)mv[i] * (float)dv[i];
+    for (int it = 0; it < 8; ++it) {
+        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+        *reinterpret_cast<f16x8*>(Mb + row * kLd + c8) = m0in[it];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sdot += (float)m0in[it][i] * (float)dmin[it][i];
     }
     sdot = wave_sum(sdot);
     if (lane == 0) red[wave] = sdot;
@@ -684,9 +724,10 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
             }
         }
     __syncthreads();   // every wave is done with M0
-    for (int e = tid; e < kD * 16; e += 256) {
-        const int row = e >> 4, c8 = (e & 15) * 8;
-        *reinterpret_cast<f16x8*>(Mb + row * kLd + c8) = *reinterpret_cast<const f16x8*>(dmg + row * kD + c8);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+        *reinterpret_cast<f16x8*>(Mb + row * kLd + c8) = dmin[it];
     }
     __syncthreads();
     // ---- phase 3: U dM_C^T -> dK (diag(Dn)); dg terms of M_C
@@ -717,7 +758,6 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     f16* D1 = Mb;
     f16* D1T = Mb + kC * kLc;
     f16* Bs = Mb + 2 * kC * kLc;
-    const char* pmb = w.blocks + (size_t)ci * kChunkBytes + kOffP;
     // ---- phase 4: Gb U^T -> D1 = (.) o Gamma (incl. lower), dg from Pm
     {
         f32x4 C4[4] = {zero4, zero4, zero4, zero4};
@@ -730,7 +770,7 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * mt + 4 * G + i;
                 const float x = C4[mt][i];
-                const float pm = (float)*reinterpret_cast<const f16*>(pmb + offT(row, j));
+                const float pm = (float)pmv[4 * mt + i];
                 const float y = x * pm;
                 const float rs = group16_sum(y);
                 if (m == 0) atomicAdd(&dg[row], rs);
@@ -802,11 +842,12 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
             }
         }
     // dV = diag(beta) dR; dbeta += dR_i . V_i (16 lanes per row)
-    for (int e = tid; e < kC * 16; e += 256) {
-        const int row = e >> 4, c8 = (e & 15) * 8;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
         float s = 0.f;
         if (row < n) {
-            const bf16x8 vv = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.v) + (tok0 + row) * kD + c8);
+            const bf16x8 vv = vin[it];
             float ov[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
