@@ -494,38 +494,22 @@ __global__ __launch_bounds__(256) void gla_rscan_kernel(GlaBwdLaunch b, BwdWs w)
 }
 
 // ---------------------------------------------------------------------------------
-// Chunk gradient kernel: one workgroup (4 waves) per chunk. Operands sit in LDS
-// as row-major fp16 with padded rows; every product is C = A Bt^T with both
+// Chunk gradient kernel: one workgroup of 8 waves (two per SIMD, so that one
+// wave's latencies overlap the other's) per chunk. Operands sit in LDS as
+// row-major fp16 with padded rows; every product is C = A Bt^T with both
 // operands contiguous along the contraction, on v_mfma_f32_16x16x32_f16.
 // Output tile (mt, nt) of 16x16: lane (G, m) holds rows 16 mt + 4G + i, column
-// 16 nt + m. [64 x 128] outputs: wave w owns columns 32w .. 32w + 31 (tiles
-// nt = 2w, 2w + 1), all four row tiles. [64 x 64] outputs: wave w owns nt = w.
+// 16 nt + m. [64 x 128] outputs: wave w owns columns 16w .. 16w + 15 (tile
+// nt = w), all four row tiles. [64 x 64] outputs: wave w owns column tile
+// nt = w & 3 and row tiles 2 (w >> 2), 2 (w >> 2) + 1.
+constexpr int kGradThreads = 512;
 
 constexpr int kLd = kD + 8;   // padded row (halfs) of a 128-wide operand
 constexpr int kLc = kC + 8;   // padded row of a 64-wide operand
 
 template <int K>
 __device__ __forceinline__ void mm_wide(const f16* A, int lda, const f16* Bt, int ldb,
-                                        f32x4 (&acc)[8], int wave, int lane) {
-    const int m = lane & 15, G = lane >> 4;
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        f16x8 bf[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            bf[q] = *reinterpret_cast<const f16x8*>(Bt + (32 * wave + 16 * q + m) * ldb + k0 + 8 * G);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const f16x8 af = *reinterpret_cast<const f16x8*>(A + (16 * mt + m) * lda + k0 + 8 * G);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) acc[2 * mt + q] = mfma16h(af, bf[q], acc[2 * mt + q]);
-        }
-    }
-}
-
-template <int K>
-__device__ __forceinline__ void mm_cc(const f16* A, int lda, const f16* Bt, int ldb,
-                                      f32x4 (&acc)[4], int wave, int lane) {
+                                        f32x4 (&acc)[4], int wave, int lane) {
     const int m = lane & 15, G = lane >> 4;
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 32) {
@@ -534,6 +518,22 @@ __device__ __forceinline__ void mm_cc(const f16* A, int lda, const f16* Bt, int 
         for (int mt = 0; mt < 4; ++mt) {
             const f16x8 af = *reinterpret_cast<const f16x8*>(A + (16 * mt + m) * lda + k0 + 8 * G);
             acc[mt] = mfma16h(af, bf, acc[mt]);
+        }
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void mm_cc(const f16* A, int lda, const f16* Bt, int ldb,
+                                      f32x4 (&acc)[2], int wave, int lane) {
+    const int m = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const f16x8 bf = *reinterpret_cast<const f16x8*>(Bt + (16 * (wave & 3) + m) * ldb + k0 + 8 * G);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int mt = 2 * (wave >> 2) + h;
+            const f16x8 af = *reinterpret_cast<const f16x8*>(A + (16 * mt + m) * lda + k0 + 8 * G);
+            acc[h] = mfma16h(af, bf, acc[h]);
         }
     }
 }
@@ -556,7 +556,7 @@ __device__ __forceinline__ float group16_sum(float v) {
     return v;
 }
 
-__global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) {
+__global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) {
     __shared__ __attribute__((aligned(16))) f16 Kr[kC * kLd];     // K   [64][128]
     __shared__ __attribute__((aligned(16))) f16 KT[kD * kLc];     // K^T [128][64]
     __shared__ __attribute__((aligned(16))) f16 QT[kD * kLc];     // Q^T [128][64]
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     __shared__ __attribute__((aligned(16))) f16 Mb[kD * kLd];     // M0, then dM_C; then 3 [64][64]
     __shared__ float gs[kC], gps[kC], Es[kC], Dn[kC], bs[kC], Eps[kC], als[kC];
     __shared__ float dg[kC], dgp[kC], dbt[kC];
-    __shared__ float red[4];
+    __shared__ float red[kGradThreads / 64];
 
     const long long nch = (b.L + kC - 1) / kC;
     const int cid = blockIdx.x;
@@ -579,24 +579,26 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     const float sig = sigma_of(*w.maxbits);
     const long long tok0 = (long long)bh * b.L + t0;   // first token row of the chunk
     const long long ci = (long long)bh * nch + c;      // chunk index
-    // Pm at this lane's phase-4 positions (rows 16 mt + 4G + i, column 16 wave + m),
-    // fetched with the other operands rather than inside phase 4
+    // Pm at this lane's phase-4 positions (rows 16 mt + 4G + i of the wave's two row
+    // tiles, column 16 (wave & 3) + m), fetched with the other operands rather than
+    // inside phase 4
     const char* pmb = w.blocks + (size_t)ci * kChunkBytes + kOffP;
-    f16 pmv[16];
+    f16 pmv[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-        pmv[r] = *reinterpret_cast<const f16*>(pmb + offT(16 * (r >> 2) + 4 * G + (r & 3), 16 * wave + m));
+    for (int r = 0; r < 8; ++r)
+        pmv[r] = *reinterpret_cast<const f16*>(
+            pmb + offT(16 * (2 * (wave >> 2) + (r >> 2)) + 4 * G + (r & 3), 16 * (wave & 3) + m));
 
     // ---- phase 0: stage operands (rows >= n zero) and per-token factors. Every
     // global operand of the chunk is requested first, so that the loads are in
     // flight together; dM_C and V stay in registers until they are used.
     const f16* m0g = w.save_m + ci * kD * kD;
     const f16* dmg = w.dme + ci * kD * kD;
-    bf16x8 kin[4], qin[4], vin[4];
-    f16x8 gin[4], rin[4], uin[4], m0in[8], dmin[8];
+    bf16x8 kin[2], qin[2], vin[2];
+    f16x8 gin[2], rin[2], uin[2], m0in[4], dmin[4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < 2; ++it) {
+        const int e = tid + kGradThreads * it, row = e >> 4, c8 = (e & 15) * 8;
         if (row < n) {
             const long long tr = (tok0 + row) * kD + c8, cr = (ci * kC + row) * kD + c8;
             kin[it] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(b.k) + tr);
@@ -608,8 +610,8 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
         }
     }
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < 4; ++it) {
+        const int e = tid + kGradThreads * it, row = e >> 4, c8 = (e & 15) * 8;
         m0in[it] = *reinterpret_cast<const f16x8*>(m0g + row * kD + c8);
         dmin[it] = *reinterpret_cast<const f16x8*>(dmg + row * kD + c8);
     }
@@ -641,8 +643,8 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     }
     // (the chunk's global operands were all requested at the top: see phase 0)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {   // 16-byte pieces of 64 rows x 128
-        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < 2; ++it) {   // 16-byte pieces of 64 rows x 128
+        const int e = tid + kGradThreads * it, row = e >> 4, c8 = (e & 15) * 8;
         f16x8 kk, qq, gg, rr, uu;
         if (row < n) {
 #pragma unroll
@@ -666,8 +668,8 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     }
     float sdot = 0.f;   // <dM_C, M0>
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < 4; ++it) {
+        const int e = tid + kGradThreads * it, row = e >> 4, c8 = (e & 15) * 8;
         *reinterpret_cast<f16x8*>(Mb + row * kLd + c8) = m0in[it];
 #pragma unroll
         for (int i = 0; i < 8; ++i) sdot += (float)m0in[it][i] * (float)dmin[it][i];
@@ -675,48 +677,45 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     sdot = wave_sum(sdot);
     if (lane == 0) red[wave] = sdot;
     __syncthreads();
-    if (tid == 0) atomicAdd(&dg[kC - 1], Es[kC - 1] * (red[0] + red[1] + red[2] + red[3]));
+    if (tid == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int i = 0; i < kGradThreads / 64; ++i) t += red[i];
+        atomicAdd(&dg[kC - 1], Es[kC - 1] * t);
+    }
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 accQ[8], accK[8], X[8];
+    f32x4 accQ[4], accK[4], X[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) { accQ[t] = zero4; accK[t] = zero4; }
+    for (int t = 0; t < 4; ++t) { accQ[t] = zero4; accK[t] = zero4; }
 
     // ---- phase 1: Gb M0^T -> dQ (diag(E)), dg += E_i Q_i . (Gb M0^T)_i
 #pragma unroll
-    for (int t = 0; t < 8; ++t) X[t] = zero4;
+    for (int t = 0; t < 4; ++t) X[t] = zero4;
     mm_wide<kD>(Gr, kLd, Mb, kLd, X, wave, lane);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * mt + 4 * G + i;
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int col = 32 * wave + 16 * q + m;
-                accQ[2 * mt + q][i] = Es[row] * X[2 * mt + q][i];
-                s += (float)QT[col * kLc + row] * X[2 * mt + q][i];
-            }
+            const int col = 16 * wave + m;
+            accQ[mt][i] = Es[row] * X[mt][i];
+            float s = (float)QT[col * kLc + row] * X[mt][i];
             s = group16_sum(s);
             if (m == 0) atomicAdd(&dg[row], Es[row] * s);
         }
     // ---- phase 2: dR M0^T -> dK (-diag(beta Ep)); dgp, dbeta
 #pragma unroll
-    for (int t = 0; t < 8; ++t) X[t] = zero4;
+    for (int t = 0; t < 4; ++t) X[t] = zero4;
     mm_wide<kD>(Rr, kLd, Mb, kLd, X, wave, lane);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * mt + 4 * G + i;
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int col = 32 * wave + 16 * q + m;
-                accK[2 * mt + q][i] = -bs[row] * Eps[row] * X[2 * mt + q][i];
-                s += (float)Kr[row * kLd + col] * X[2 * mt + q][i];
-            }
+            const int col = 16 * wave + m;
+            accK[mt][i] = -bs[row] * Eps[row] * X[mt][i];
+            float s = (float)Kr[row * kLd + col] * X[mt][i];
             s = group16_sum(s);
             if (m == 0) {
                 atomicAdd(&dgp[row], -bs[row] * Eps[row] * s);
@@ -725,14 +724,14 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
         }
     __syncthreads();   // every wave is done with M0
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < 4; ++it) {
+        const int e = tid + kGradThreads * it, row = e >> 4, c8 = (e & 15) * 8;
         *reinterpret_cast<f16x8*>(Mb + row * kLd + c8) = dmin[it];
     }
     __syncthreads();
     // ---- phase 3: U dM_C^T -> dK (diag(Dn)); dg terms of M_C
 #pragma unroll
-    for (int t = 0; t < 8; ++t) X[t] = zero4;
+    for (int t = 0; t < 4; ++t) X[t] = zero4;
     mm_wide<kD>(Ur, kLd, Mb, kLd, X, wave, lane);
     float slast = 0.f;
 #pragma unroll
@@ -740,13 +739,9 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * mt + 4 * G + i;
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int col = 32 * wave + 16 * q + m;
-                accK[2 * mt + q][i] += Dn[row] * X[2 * mt + q][i];
-                s += (float)Kr[row * kLd + col] * X[2 * mt + q][i];
-            }
+            const int col = 16 * wave + m;
+            accK[mt][i] += Dn[row] * X[mt][i];
+            float s = (float)Kr[row * kLd + col] * X[mt][i];
             s = group16_sum(s) * Dn[row];
             if (m == 0) {
                 atomicAdd(&dg[row], -s);
@@ -760,17 +755,17 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     f16* Bs = Mb + 2 * kC * kLc;
     // ---- phase 4: Gb U^T -> D1 = (.) o Gamma (incl. lower), dg from Pm
     {
-        f32x4 C4[4] = {zero4, zero4, zero4, zero4};
+        f32x4 C4[2] = {zero4, zero4};
         mm_cc<kD>(Gr, kLd, Ur, kLd, C4, wave, lane);
-        const int j = 16 * wave + m;
+        const int j = 16 * (wave & 3) + m;
         float colsum = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 16 * mt + 4 * G + i;
-                const float x = C4[mt][i];
-                const float pm = (float)pmv[4 * mt + i];
+                const int row = 16 * (2 * (wave >> 2) + h) + 4 * G + i;
+                const float x = C4[h][i];
+                const float pm = (float)pmv[4 * h + i];
                 const float y = x * pm;
                 const float rs = group16_sum(y);
                 if (m == 0) atomicAdd(&dg[row], rs);
@@ -785,23 +780,23 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
     }
     // ---- phase 5: dA = -strictly-lower(dR U^T), K K^T -> dbeta, dgp, dg, Bs
     {
-        f32x4 P5[4] = {zero4, zero4, zero4, zero4}, KK[4] = {zero4, zero4, zero4, zero4};
+        f32x4 P5[2] = {zero4, zero4}, KK[2] = {zero4, zero4};
         mm_cc<kD>(Rr, kLd, Ur, kLd, P5, wave, lane);
         mm_cc<kD>(Kr, kLd, Kr, kLd, KK, wave, lane);
-        const int j = 16 * wave + m;
+        const int j = 16 * (wave & 3) + m;
         float colsum = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int row = 16 * mt + 4 * G + i;
+                const int row = 16 * (2 * (wave >> 2) + h) + 4 * G + i;
                 float bm = 0.f, zk = 0.f, da_a = 0.f;
                 if (j < row) {
                     const float lam = __expf(gps[row] - gs[j]);
-                    const float dA = -P5[mt][i];
+                    const float dA = -P5[h][i];
                     const float z = dA * lam;
-                    zk = z * KK[mt][i];
-                    da_a = dA * bs[row] * KK[mt][i] * lam;
+                    zk = z * KK[h][i];
+                    da_a = dA * bs[row] * KK[h][i] * lam;
                     bm = bs[row] * z;
                 }
                 const float r1 = group16_sum(zk), r2 = group16_sum(da_a);
@@ -827,24 +822,21 @@ __global__ __launch_bounds__(256) void gla_grad_kernel(GlaBwdLaunch b, BwdWs w) 
         for (int i = 0; i < 4; ++i) {
             const int row = 16 * mt + 4 * G + i;
             if (row < n) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const long long o = (tok0 + row) * kD + 32 * wave + 16 * q + m;
-                    const float xq = accQ[2 * mt + q][i] * inv, xk = accK[2 * mt + q][i] * inv;
-                    if (b.grad_f32) {
-                        static_cast<float*>(b.dq)[o] = xq;
-                        static_cast<float*>(b.dk)[o] = xk;
-                    } else {
-                        static_cast<bf16*>(b.dq)[o] = f2bf(xq);
-                        static_cast<bf16*>(b.dk)[o] = f2bf(xk);
-                    }
+                const long long o = (tok0 + row) * kD + 16 * wave + m;
+                const float xq = accQ[mt][i] * inv, xk = accK[mt][i] * inv;
+                if (b.grad_f32) {
+                    static_cast<float*>(b.dq)[o] = xq;
+                    static_cast<float*>(b.dk)[o] = xk;
+                } else {
+                    static_cast<bf16*>(b.dq)[o] = f2bf(xq);
+                    static_cast<bf16*>(b.dk)[o] = f2bf(xk);
                 }
             }
         }
     // dV = diag(beta) dR; dbeta += dR_i . V_i (16 lanes per row)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int e = tid + 256 * it, row = e >> 4, c8 = (e & 15) * 8;
+    for (int it = 0; it < 2; ++it) {
+        const int e = tid + kGradThreads * it, row = e >> 4, c8 = (e & 15) * 8;
         float s = 0.f;
         if (row < n) {
             const bf16x8 vv = vin[it];
@@ -941,7 +933,7 @@ hipError_t launch_gla_bwd(const GlaBwdLaunch& b, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gla_rscan_kernel, dim3((unsigned)(b.BH * 2)), dim3(256), smem, stream, b, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(gla_grad_kernel, dim3((unsigned)(b.BH * nch)), dim3(256), 0, stream, b, w);
+    hipLaunchKernelGGL(gla_grad_kernel, dim3((unsigned)(b.BH * nch)), dim3(kGradThreads), 0, stream, b, w);
     return hipGetLastError();
 }
 
