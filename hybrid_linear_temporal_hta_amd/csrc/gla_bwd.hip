@@ -297,18 +297,44 @@ __device__ __forceinline__ float sigma_of(unsigned bits) {
 }
 
 // max |scale dO| and |dL/dM_L| (atomic max on the bits of non-negative floats).
+// dO is read 16 bytes per lane, four loads in flight per thread; |scale| is
+// applied to the maximum (rounding is monotonic: the same value as the maximum
+// of the rounded products).
 __global__ __launch_bounds__(256) void gla_bwd_max_kernel(GlaBwdLaunch b, unsigned* maxbits) {
     const long long nd = (long long)b.BH * b.L * kD, ns = (long long)b.BH * kD * kD;
+    const long long stride = (long long)gridDim.x * 256;
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
     float m = 0.f;
-    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < nd + ns;
-         e += (long long)gridDim.x * 256) {
-        float x;
-        if (e < nd) x = b.do_f32 ? static_cast<const float*>(b.dout)[e]
-                                 : bf2f(static_cast<const bf16*>(b.dout)[e]);
-        else x = b.dstate[e - nd];
-        if (e < nd) x *= b.scale;
-        m = fmaxf(m, fabsf(x));
+    if (b.do_f32) {
+        const long long n4 = nd / 4;
+        const f32x4* p = static_cast<const f32x4*>(b.dout);
+        for (long long e = t; e < n4; e += 4 * stride) {
+            f32x4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                x[u] = e + u * stride < n4 ? p[e + u * stride] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(x[u][i]));
+        }
+    } else {
+        const long long n8 = nd / 8;
+        const bf16x8* p = static_cast<const bf16x8*>(b.dout);
+        for (long long e = t; e < n8; e += 4 * stride) {
+            bf16x8 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e + u * stride < n8) x[u] = p[e + u * stride];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e + u * stride < n8)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(bf2f(x[u][i])));
+        }
     }
+    m *= fabsf(b.scale);
+    for (long long e = t; e < ns; e += stride) m = fmaxf(m, fabsf(b.dstate[e]));
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
     if ((threadIdx.x & 63) == 0) atomicMax(maxbits, __float_as_uint(m));
