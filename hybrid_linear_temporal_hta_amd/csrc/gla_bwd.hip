@@ -337,7 +337,11 @@ __global__ __launch_bounds__(256) void gla_bwd_max_kernel(GlaBwdLaunch b, unsign
     for (long long e = t; e < ns; e += stride) m = fmaxf(m, fabsf(b.dstate[e]));
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-    if ((threadIdx.x & 63) == 0) atomicMax(maxbits, __float_as_uint(m));
+    __shared__ float wm[4];   // one atomic per workgroup: same-address atomics serialise
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(maxbits, __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
 }
 
 // gh = fp16(sigma * scale * dO), 8 elements per thread.
@@ -946,7 +950,7 @@ hipError_t launch_gla_bwd(const GlaBwdLaunch& b, hipStream_t stream) {
     g.save_u = w.save_u;
     if ((e = launch_gla_bf16(g, stream)) != hipSuccess) return e;
     const long long nd = (long long)b.BH * b.L * kD;
-    const long long gmax = min(4096LL, (nd + 255) / 256);
+    const long long gmax = min(1024LL, (nd + 255) / 256);
     hipLaunchKernelGGL(gla_bwd_max_kernel, dim3((unsigned)gmax), dim3(256), 0, stream, b, w.maxbits);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const long long n8 = (nd / 8 + 255) / 256;
