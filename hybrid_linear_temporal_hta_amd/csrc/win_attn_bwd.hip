@@ -28,6 +28,7 @@
 // ring with direct global->LDS loads, as the forward does; the logits' register
 // layout is reused as the B operand of the next product, so P and dS never go
 // through LDS. The fp32 kernels are plain vector-ALU loops for small workloads.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -43,64 +44,67 @@ using namespace tiles;
 constexpr int kRows = 128;   // queries (query pass) or keys (key pass) per workgroup
 
 // ---------------------------------------------------------------------------------
-// prep: stats[row] = {lse * log2(e), dO . o}; 16 lanes per row.
+// prep: stats[row] = {lse * log2(e), dO . o}; 16 lanes per row, 16 rows per
+// block, the blocks strided over the grid (so that the maxima take one atomic
+// pair per workgroup: same-address atomics serialise).
 
 template <int D>
 __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
     __shared__ float mx[2][4];
-    const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int sub = threadIdx.x & 15, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const bool ok = row < p.rows;   // whole 16-lane groups alike
     constexpr int E = D / 16;       // elements per lane
-    float dov[E], ov[E];
-    const long long base = (ok ? row : 0) * D + sub * E;
-    if (p.do_f32) {
-        const float* s = static_cast<const float*>(p.dout) + base;
+    const long long nblk = (p.rows + 15) / 16;
+    float md = 0.f, mv = 0.f;       // running maxima of |dout| and |v|
+    for (long long blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const long long row = blk * 16 + (threadIdx.x >> 4);
+        const bool ok = row < p.rows;   // whole 16-lane groups alike
+        float dov[E], ov[E];
+        const long long base = (ok ? row : 0) * D + sub * E;
+        if (p.do_f32) {
+            const float* s = static_cast<const float*>(p.dout) + base;
 #pragma unroll
-        for (int i = 0; i < E; ++i) dov[i] = s[i];
-    } else {
-        const bf16* s = static_cast<const bf16*>(p.dout) + base;
+            for (int i = 0; i < E; ++i) dov[i] = s[i];
+        } else {
+            const bf16* s = static_cast<const bf16*>(p.dout) + base;
 #pragma unroll
-        for (int i = 0; i < E; ++i) dov[i] = bf2f(s[i]);
-    }
-    if (p.o_f32) {
-        const float* s = static_cast<const float*>(p.o) + base;
+            for (int i = 0; i < E; ++i) dov[i] = bf2f(s[i]);
+        }
+        if (p.o_f32) {
+            const float* s = static_cast<const float*>(p.o) + base;
 #pragma unroll
-        for (int i = 0; i < E; ++i) ov[i] = s[i];
-    } else {
-        const bf16* s = static_cast<const bf16*>(p.o) + base;
+            for (int i = 0; i < E; ++i) ov[i] = s[i];
+        } else {
+            const bf16* s = static_cast<const bf16*>(p.o) + base;
 #pragma unroll
-        for (int i = 0; i < E; ++i) ov[i] = bf2f(s[i]);
-    }
-    if (p.round_do) {
+            for (int i = 0; i < E; ++i) ov[i] = bf2f(s[i]);
+        }
+        if (p.round_do) {
 #pragma unroll
-        for (int i = 0; i < E; ++i) dov[i] = bf2f(f2bf(dov[i]));
-    }
-    if (p.dout_bf16 && ok) {
-        bf16* dst = static_cast<bf16*>(p.dout_bf16) + base;
+            for (int i = 0; i < E; ++i) dov[i] = bf2f(f2bf(dov[i]));
+        }
+        if (p.dout_bf16 && ok) {
+            bf16* dst = static_cast<bf16*>(p.dout_bf16) + base;
 #pragma unroll
-        for (int i = 0; i < E; ++i) dst[i] = f2bf(dov[i]);
-    }
-    if (p.q16 && ok) {   // exact fp16 copies of q and k (D == 128 here: 8 per lane)
-        const bf16* qs = static_cast<const bf16*>(p.q) + base;
-        const bf16* ks = static_cast<const bf16*>(p.k) + base;
-        f16* qd = static_cast<f16*>(p.q16) + base;
-        f16* kd = static_cast<f16*>(p.k16) + base;
+            for (int i = 0; i < E; ++i) dst[i] = f2bf(dov[i]);
+        }
+        if (p.q16 && ok) {   // exact fp16 copies of q and k (D == 128 here: 8 per lane)
+            const bf16* qs = static_cast<const bf16*>(p.q) + base;
+            const bf16* ks = static_cast<const bf16*>(p.k) + base;
+            f16* qd = static_cast<f16*>(p.q16) + base;
+            f16* kd = static_cast<f16*>(p.k16) + base;
 #pragma unroll
-        for (int i = 0; i < E; ++i) { qd[i] = (f16)bf2f(qs[i]); kd[i] = (f16)bf2f(ks[i]); }
-    }
-    float acc = 0.f;
+            for (int i = 0; i < E; ++i) { qd[i] = (f16)bf2f(qs[i]); kd[i] = (f16)bf2f(ks[i]); }
+        }
+        float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc = __builtin_fmaf(dov[i], ov[i], acc);
+        for (int i = 0; i < E; ++i) acc = __builtin_fmaf(dov[i], ov[i], acc);
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (sub == 0 && ok) {
-        p.stats[2 * row] = p.lse[row] * kLog2e;
-        p.stats[2 * row + 1] = acc;
-    }
-    if (p.gmax) {   // block maxima of |dout| and |v|, one atomic each per block
-        float md = 0.f, mv = 0.f;
-        if (ok) {
+        for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 64);
+        if (sub == 0 && ok) {
+            p.stats[2 * row] = p.lse[row] * kLog2e;
+            p.stats[2 * row + 1] = acc;
+        }
+        if (p.gmax && ok) {
             const bf16* vs = static_cast<const bf16*>(p.v) + base;
 #pragma unroll
             for (int i = 0; i < E; ++i) {
@@ -108,6 +112,8 @@ __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
                 mv = fmaxf(mv, fabsf(bf2f(vs[i])));
             }
         }
+    }
+    if (p.gmax) {   // maxima of |dout| and |v|, one atomic each per workgroup
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
             md = fmaxf(md, __shfl_xor(md, m, 64));
@@ -571,8 +577,7 @@ __global__ __launch_bounds__(256) void win_bwd_dkdv_f32_kernel(BwdLaunch w) {
 
 hipError_t launch_win_bwd_prep(const BwdPrep& p, hipStream_t stream) {
     if (p.rows == 0) return hipSuccess;
-    const long long nwg = (p.rows + 15) / 16;
-    if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long nwg = std::min((p.rows + 15) / 16, 4096LL);
     if (p.d == 128)
         hipLaunchKernelGGL((win_bwd_prep_kernel<128>), dim3((unsigned)nwg), dim3(256), 0, stream, p);
     else if (p.d == 64)
