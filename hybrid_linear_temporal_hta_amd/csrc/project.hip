@@ -10,7 +10,8 @@
 // Y = X W with X [M = B*L][Dm] and W [Dm][N], N = 3*H*128 + 2*H (columns q | k |
 // v | alpha | beta, head-major within each group). One workgroup computes a
 // 128-token x 128-column tile: column tile j < 3H is one head of q, k or v, tile
-// 3H holds the 2H gate columns. Four waves in a 2 x 2 arrangement each own a
+// 3H holds the 2H gate columns. Workgroups run in groups of four token tiles per
+// column tile, so concurrent ones share X and W slices in L2. Four waves in a 2 x 2 arrangement each own a
 // 64 x 64 sub-tile (2 x 2 blocks of v_mfma_f32_32x32x16_bf16). X and W tiles of
 // 64 along Dm stream into a two-stage LDS ring with direct global->LDS loads:
 // A fragments (X rows) are 16-byte reads of chunk-swizzled 128-byte rows, B
@@ -29,6 +30,7 @@ namespace hta {
 namespace {
 
 constexpr int kBM = 128;             // tokens per tile
+constexpr int kGroupM = 4;           // token tiles per column tile in the launch order
 constexpr int kBN = 128;             // columns per tile (one head of q, k or v)
 constexpr int kBK = 64;              // depth per LDS stage
 constexpr int kXRow = kBK * 2;       // 128-byte rows of the X tile
@@ -75,8 +77,16 @@ void project_kernel(ProjLaunch p) {
     const int ntile = 3 * p.H + 1;
     const int nwg = p.nmt * ntile;
     const int wid = xcd_remap(blockIdx.x, nwg);
-    const int nt = wid % ntile;          // column tiles of one token tile run together
-    const int mt = wid / ntile;
+    // Grouped order: each column tile visits kGroupM token tiles in a row, so the
+    // workgroups in flight on one XCD share their X and W slices in its L2 (one
+    // token tile with all its column tiles streamed all of W per token tile).
+    const int gsz = kGroupM * ntile;
+    const int grp = wid / gsz;
+    const int first = grp * kGroupM;
+    const int gm = min((int)p.nmt - first, kGroupM);
+    const int rr = wid - grp * gsz;
+    const int mt = first + rr % gm;
+    const int nt = rr / gm;
     const long long m0 = (long long)mt * kBM;
     const int n0 = nt * kBN;
     const int nvalid_cols = nt < 3 * p.H ? kBN : 2 * p.H;
