@@ -37,13 +37,13 @@
 //   dbeta_i = dR_i.V_i - Ep_i K_i.(dR M0^T)_i + sum_j (dA o e^{gp_i - g_j} o K K^T)_ij
 //   and dg, dgp (then dlog alpha = reverse cumulative sums) from every place g
 //   and gp enter: E in O, Pm, A, Ep in R, and M_C.
-// Five launches: the forward prep and scan (saving each chunk's M0 and U in
-// fp16), a pass that scales scale * dO into fp16 by a power of two taken from
-// max |scale dO| and max |dL/dM_L| (so the fp16 operands keep their precision
-// whatever the gradient's magnitude; the results are scaled back exactly), the
-// reverse scan (one workgroup per (b, h, 64 value columns), chunks in reverse
-// order, dM in fp32 registers; it saves dM_C and dR per chunk in fp16), and the
-// chunk-parallel gradient kernel (one workgroup per chunk).
+// Six launches: the forward prep and scan (saving each chunk's M0 and U in
+// fp16); a pass taking max |scale dO| and max |dL/dM_L|, and one scaling
+// scale * dO into fp16 by the power of two taken from them (so the fp16 operands
+// keep their precision whatever the gradient's magnitude; the results are scaled
+// back exactly); the reverse scan (one workgroup per (b, h, 64 value columns),
+// chunks in reverse order, dM in fp32 registers; it saves dM_C and dR per chunk
+// in fp16); and the chunk-parallel gradient kernel (one workgroup per chunk).
 #include <string.h>
 
 #include <type_traits>
