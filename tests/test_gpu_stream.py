@@ -114,6 +114,21 @@ def test_stream_from_empty_prefix():
     assert_parity(s.state, ref_st, w.dtype, "stream from empty state")
 
 
+def test_stream_step_wide_grid():
+    """A stream step whose attention grid spans more than one wave of workgroups
+    (B4 H16 P1040: 64 heads x 9 query tiles = 576 workgroups, over two per CU on
+    256 CUs), where the attention pass adds the GLA partial itself for heads whose
+    scan has finished and flags the rest: sampled rows of two steps against the
+    oracle on the whole history, the final state and the ring."""
+    print("[case] stream step, wide grid B4 H16 P1040", flush=True)
+    w = Workload("case", 4, 16, 4, 1040, 128, 128, torch.bfloat16, window=3, taps=4, dilation=4,
+                 k_unit=True, alpha_mu=3.0, ring=13, seed=47)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.array([0, 1, 127, 128, 1023, 1024, 1039]),
+                                     rng.integers(0, w.P, 40)]))
+    _run_and_check(w, 4, 2, rows=rows)
+
+
 def test_stream_equals_batch_and_commit_only():
     """I9: stream steps reproduce the batch hybrid over prefix + frames (GPU vs
     GPU, different chunk boundaries, so within tolerance); commit-only steps
