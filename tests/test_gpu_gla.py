@@ -133,7 +133,8 @@ def test_hybrid_handoff_bitwise(out_dtype):
     rows (flagged) to a last pass; both routes form the same fp32 sum in the same
     order, so at the benchmark workload (B2 H16 T21 P1560 bf16) the output equals,
     bit for bit, the GLA partial added by a separate one-pass attention call,
-    whatever mix of routes the timing produced (printed from the flags)."""
+    whatever mix of routes the timing produced (printed from the flags), also on a
+    second call over the same workspace."""
     w = WORKLOADS["hybrid_stream"]
     print(f"[case] hybrid hand-off {w.name} out {out_dtype}", flush=True)
     x = make_inputs(w, device="cuda", frames=w.T)
@@ -170,6 +171,14 @@ def test_hybrid_handoff_bitwise(out_dtype):
     assert torch.equal(st, st2)
     bits = torch.int32 if out_dtype == torch.float32 else torch.int16
     assert torch.equal(o.view(bits), ref.view(bits)), "hybrid differs from GLA + attention"
+    # a second call on the same workspace (counters and flags left by the first)
+    # from the same initial state gives the same output
+    st.zero_()
+    o2 = torch.full_like(o, float("nan"))
+    hta.hta_hybrid_fwd(q, k, v, x["alpha"], x["beta"], st, o2, w.P, prm, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.view(bits), ref.view(bits)), "second call on the same workspace differs"
+    assert torch.equal(st, st2)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
