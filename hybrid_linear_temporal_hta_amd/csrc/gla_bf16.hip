@@ -116,7 +116,7 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
         alpha_t = g.alpha[(long long)bh * g.L + t0 + lane];
         beta_t = g.beta[(long long)bh * g.L + t0 + lane];
     }
-    u32x4 kv[4], qv[4];
+    u32x4 kv[4], qv[4], vv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int ci = tid + 256 * r, row = ci >> 4, cc = ci & 15;
@@ -125,6 +125,9 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
         if (row < n) {
             kv[r] = *reinterpret_cast<const u32x4*>(kp + (long long)row * kD + 8 * cc);
             qv[r] = *reinterpret_cast<const u32x4*>(qp + (long long)row * kD + 8 * cc);
+            if (g.ring_v)
+                vv[r] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(g.v) +
+                                                        ((long long)bh * g.L + t0 + row) * kD + 8 * cc);
         }
     }
 #pragma unroll
@@ -134,6 +137,11 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
         *reinterpret_cast<u32x4*>(Qs + row * kKsP + 8 * cc) = qv[r];
         *reinterpret_cast<u32x4*>(blk + kOffK + offK(row, 8 * cc)) = bf16x8_to_f16x8(kv[r]);
         *reinterpret_cast<u32x4*>(blk + kOffQ + offK(row, 8 * cc)) = bf16x8_to_f16x8(qv[r]);
+        if (g.ring_k && row < n) {   // the chunk's K and V rows into the ring slot, unchanged
+            const long long ro = (long long)bh * g.ring_bh + g.ring_off + (t0 + row) * kD + 8 * cc;
+            *reinterpret_cast<u32x4*>(static_cast<bf16*>(g.ring_k) + ro) = kv[r];
+            *reinterpret_cast<u32x4*>(static_cast<bf16*>(g.ring_v) + ro) = vv[r];
+        }
     }
     if (wave == 0) {
         // inclusive prefix sum of log(alpha) over the chunk (alpha = 1 past the end)

@@ -1197,13 +1197,25 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
     const long long n = ctx->n_frames;
     const long long slot = n % ctx->R;
     const long long fe = (long long)s.P * s.dk;
-    // 1. K/V of the new frame into ring slot n mod R.
-    hipError_t e = hta::launch_copy_frames(k, ctx->ring_k, BH, fe, (long long)ctx->R * fe, 0,
-                                           slot * fe, fe, elem_bytes(s.dtype), sm);
-    if (e == hipSuccess)
-        e = hta::launch_copy_frames(v, ctx->ring_v, BH, fe, (long long)ctx->R * fe, 0, slot * fe,
+    hipError_t e = hipSuccess;
+    // 1. K/V of the new frame into ring slot n mod R: for bf16 inputs the GLA prep
+    //    copies them while it reads the frame (before anything reads the ring).
+    const bool fused_copy = s.dtype == HTA_BF16;
+    auto ring_into = [&](hta::GlaLaunch& g) {
+        if (!fused_copy) return;
+        g.ring_k = ctx->ring_k;
+        g.ring_v = ctx->ring_v;
+        g.ring_bh = (long long)ctx->R * fe;
+        g.ring_off = slot * fe;
+    };
+    if (!fused_copy) {
+        e = hta::launch_copy_frames(k, ctx->ring_k, BH, fe, (long long)ctx->R * fe, 0, slot * fe,
                                     fe, elem_bytes(s.dtype), sm);
-    if (e != hipSuccess) return hip_fail(e);
+        if (e == hipSuccess)
+            e = hta::launch_copy_frames(v, ctx->ring_v, BH, fe, (long long)ctx->R * fe, 0,
+                                        slot * fe, fe, elem_bytes(s.dtype), sm);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     // 2. GLA over the frame's P tokens from the carried state (chunks start at
     //    the frame), and 3. the frame's queries over the ring plus the GLA
     //    partial -- the two side by side for bf16 inputs.
@@ -1216,6 +1228,7 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, gpart, ctx->p.gla_chunk,
                                     ctx->p.gla_scale, workspace, need_gla, ctx->p.gla_form);
         g.out_f32 = 1;
+        ring_into(g);
         e = run_hybrid_fused(g, ring_launch(ctx, s, q, o, n), mid, partials_of(&s, wsb + need_gla),
                              &ctx->p, sm);
         if (e != hipSuccess) return hip_fail(e);
@@ -1223,6 +1236,7 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, o, ctx->p.gla_chunk,
                                     ctx->p.gla_scale, workspace, need_gla, ctx->p.gla_form);
         g.out_f32 = 1;
+        ring_into(g);
         e = run_gla(g, sm);
         if (e != hipSuccess) return hip_fail(e);
         if (o) {

@@ -138,8 +138,8 @@ struct GlaLaunch {
     float scale;
     int dtype;
     int form;               // 0: GatedDeltaNet reading, 1: the printed update (erase not gated)
-    void* ring_k;           // optional: copy k/v of these tokens into a ring slot
-    void* ring_v;
+    void* ring_k;           // optional (bf16 prep): k and v of these tokens are also copied,
+    void* ring_v;           //   unchanged, to ring + bh * ring_bh + ring_off + token * d
     long long ring_bh;      // elements between (b,h) slices of the ring
     long long ring_off;     // element offset of the slot inside a (b,h) slice
     void* ws;               // workspace
