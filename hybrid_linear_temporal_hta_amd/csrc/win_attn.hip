@@ -33,7 +33,11 @@
 //     PV product (v_dot2_f32_bf16 against ones), so the output is an exact
 //     convex combination of those weights;
 //   * the epilogue adds up to two fp32 partials (the other branches) and writes
-//     the fp32 sum, or rounds it once to bf16.
+//     the fp32 sum, or rounds it once to bf16. In the hybrid's pass the GLA
+//     partial is added only if its head's scan has already signalled completion
+//     (one acquire load per wave, never waited on); otherwise the wave leaves its
+//     rows in an fp32 buffer and flags them, and win_add_pending_kernel adds the
+//     partial to the flagged rows afterwards, with the same sum and rounding.
 // fp32 kernel (d = 64 or 128): a plain per-row online softmax on the vector
 // ALU (4 lanes per query row); used for fp32 inputs, whose workloads are tiny.
 #include <type_traits>
