@@ -23,7 +23,9 @@
 //     (diagonal blocks by forward substitution, the blocks below them by fp32
 //     MFMA products), and the chunk's operand block -- K, Q (fp16), T, Pm
 //     (fp16), e^{g}, e^{g_C - g}, beta, e^{gp} (fp32) -- written contiguously in
-//     exactly the LDS layout the scan consumes (swizzles included).
+//     exactly the LDS layout the scan consumes (swizzles included). Optionally
+//     it also copies the tokens' K and V into a ring slot (a streamed frame) and
+//     zeroes the scan's completion counters.
 //
 // The printed form of the update (GlaLaunch::form = 1: the erase term uses the
 // state before the forget gate, S_t = alpha S - beta (S k) k^T + beta v k^T)
@@ -39,7 +41,9 @@
 //     K^T fragments are transposed LDS reads of row-major K). Output waves
 //     stream the next chunk's operand block and value tile into the other half
 //     of a two-stage LDS ring with direct global->LDS loads, and form and store
-//     the output from the M0 and U the state waves hand over in LDS.
+//     the output from the M0 and U the state waves hand over in LDS. Optionally
+//     each workgroup, once its output is stored, makes it visible device-wide
+//     and counts itself done for its head (read by the hybrid's attention pass).
 #include <type_traits>
 
 #include "device_common.h"
