@@ -1,4 +1,7 @@
-// gla_bf16.hip -- chunked gated-delta GLA on MFMA (gfx950), bf16 in, fp32 state.
+// gla_bf16.hip -- the chunked gated-delta GLA forward that the GLA backward
+// re-runs (gfx950, bf16 in, fp32 state): besides the final state it saves, per
+// chunk, the state entering it (M0) and U, in fp16, for the reverse scan and the
+// chunk gradients. (The inference forward is gla_fwd.hip.)
 //
 // Method: page "Kairos：面向物理 AI 的原生世界模型栈" (yingwang.github.io), section
 // 二、方法, GLA paragraph and update equations, GatedDeltaNet reading:
@@ -14,8 +17,12 @@
 // kernels build themselves (K and Q re-expressed in fp16 -- exact --, T, Pm,
 // the state copy fed to K M0 / Q M0, X, U) are fp16, whose 11-bit significand
 // keeps the chunk algebra about 8x closer to exact than bf16 operands would.
-// fp16 bounds their range: |v| and |state| must stay below 65504 (with
-// unit-norm keys, as the contraction of the update needs).
+// fp16 bounds their range: the backward hands the scan V and the initial state
+// multiplied by a power of two sigma_v (GlaLaunch::vscale) that maps their largest
+// magnitude into [1, 2), so the fp16 operands stay in range for any finite v and
+// state as long as the update does not grow the state beyond ~3e4 times that
+// maximum (with unit-norm keys and alpha < 1 the state stays within
+// max|v| sqrt(d) / sqrt(1 - alpha^2)); saved M0 and U then carry the same factor.
 //
 // Two kernels:
 //   prep (one workgroup per chunk, all chunks in parallel): g, A and Pm from
@@ -23,9 +30,7 @@
 //     (diagonal blocks by forward substitution, the blocks below them by fp32
 //     MFMA products), and the chunk's operand block -- K, Q (fp16), T, Pm
 //     (fp16), e^{g}, e^{g_C - g}, beta, e^{gp} (fp32) -- written contiguously in
-//     exactly the LDS layout the scan consumes (swizzles included). Optionally
-//     it also copies the tokens' K and V into a ring slot (a streamed frame) and
-//     zeroes the scan's completion counters.
+//     exactly the LDS layout the scan consumes (swizzles included).
 //
 // The printed form of the update (GlaLaunch::form = 1: the erase term uses the
 // state before the forget gate, S_t = alpha S - beta (S k) k^T + beta v k^T)
@@ -41,9 +46,7 @@
 //     K^T fragments are transposed LDS reads of row-major K). Output waves
 //     stream the next chunk's operand block and value tile into the other half
 //     of a two-stage LDS ring with direct global->LDS loads, and form and store
-//     the output from the M0 and U the state waves hand over in LDS. Optionally
-//     each workgroup, once its output is stored, makes it visible device-wide
-//     and counts itself done for its head (read by the hybrid's attention pass).
+//     the output from the M0 and U the state waves hand over in LDS.
 #include <type_traits>
 
 #include "device_common.h"
@@ -62,27 +65,6 @@ constexpr int kKsP = kD + 8;      // padded K / Q row (bf16)
 constexpr int kAsP = 68;          // padded A / T row (fp32)
 static_assert(kC * kKsP * 2 == kC * kAsP * 4, "Q staging shares the A buffer; T the K buffer");
 static_assert(kC * kKsP * 2 >= 64 * 128, "Pm and T staging fit in a buffer");
-
-// Lane l reads lane l ^ 1 (resp. l ^ 2) of its quad: DPP quad permutes.
-__device__ __forceinline__ float quad_xor1(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float quad_xor2(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-
-// 16x16x16 fp32 product on v_mfma_f32_16x16x4_f32: acc += X Y for 16x16 blocks X
-// (row stride xld) and Y (row stride yld) in LDS; lane l ends with rows
-// 4 (l / 16) + i of column l % 16.
-__device__ __forceinline__ f32x4 mm16f(const float* X, int xld, const float* Y, int yld,
-                                       f32x4 acc, int lane) {
-    const int m = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * xld + 4 * s + g], Y[(4 * s + g) * yld + m],
-                                                   acc, 0, 0, 0);
-    return acc;
-}
 
 // One workgroup per chunk. Phases, separated by barriers:
 //   1. loads: alpha, beta (wave 0), K and Q rows; K and Q kept in LDS as bf16 and
@@ -106,8 +88,6 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
 
     const int cid = blockIdx.x;
     const int bh = cid / nch, c = cid - bh * nch;
-    if (g.done && cid == 0)   // the scan's completion counters start from zero
-        for (int i = threadIdx.x; i < g.BH; i += 256) g.done[i] = 0;
     const long long t0 = (long long)c * kC;
     const int n = (int)min((long long)kC, g.L - t0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,7 +100,7 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
         alpha_t = g.alpha[(long long)bh * g.L + t0 + lane];
         beta_t = g.beta[(long long)bh * g.L + t0 + lane];
     }
-    u32x4 kv[4], qv[4], vv[4];
+    u32x4 kv[4], qv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int ci = tid + 256 * r, row = ci >> 4, cc = ci & 15;
@@ -129,9 +109,6 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
         if (row < n) {
             kv[r] = *reinterpret_cast<const u32x4*>(kp + (long long)row * kD + 8 * cc);
             qv[r] = *reinterpret_cast<const u32x4*>(qp + (long long)row * kD + 8 * cc);
-            if (g.ring_v)
-                vv[r] = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(g.v) +
-                                                        ((long long)bh * g.L + t0 + row) * kD + 8 * cc);
         }
     }
 #pragma unroll
@@ -141,11 +118,6 @@ void gla_prep_bf16_kernel(GlaLaunch g, int nch) {
         *reinterpret_cast<u32x4*>(Qs + row * kKsP + 8 * cc) = qv[r];
         *reinterpret_cast<u32x4*>(blk + kOffK + offK(row, 8 * cc)) = bf16x8_to_f16x8(kv[r]);
         *reinterpret_cast<u32x4*>(blk + kOffQ + offK(row, 8 * cc)) = bf16x8_to_f16x8(qv[r]);
-        if (g.ring_k && row < n) {   // the chunk's K and V rows into the ring slot, unchanged
-            const long long ro = (long long)bh * g.ring_bh + g.ring_off + (t0 + row) * kD + 8 * cc;
-            *reinterpret_cast<u32x4*>(static_cast<bf16*>(g.ring_k) + ro) = kv[r];
-            *reinterpret_cast<u32x4*>(static_cast<bf16*>(g.ring_v) + ro) = vv[r];
-        }
     }
     if (wave == 0) {
         // inclusive prefix sum of log(alpha) over the chunk (alpha = 1 past the end)
@@ -332,9 +304,9 @@ __device__ __forceinline__ void issue_chunk(char* stage, const GlaLaunch& g, int
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
         const int q = 12 * ow + i;
-        dma16(blk + 1024 * q + 16 * lane, stage + 1024 * q);
+        dma16p(blk + 1024 * q + 16 * lane, stage + 1024 * q);
     }
-    if (ow == 0 && lane < kTailChunks) dma16(blk + kBlockMain + 16 * lane, stage + kBlockMain);
+    if (ow == 0 && lane < kTailChunks) dma16p(blk + kBlockMain + 16 * lane, stage + kBlockMain);
     const long long t0 = c * kC;
     const int n = (int)min((long long)kC, g.L - t0);
     const bf16* vb = static_cast<const bf16*>(g.v) + ((long long)bh * g.L + t0) * kD + tile * 64;
@@ -343,7 +315,7 @@ __device__ __forceinline__ void issue_chunk(char* stage, const GlaLaunch& g, int
         const int p = 64 * (2 * ow + i) + lane;
         const int tok = p >> 3;
         const int cc = (p & 7) ^ swzv(tok);
-        dma16(vb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * ow + i));
+        dma16p(vb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * ow + i));
     }
 }
 
@@ -380,11 +352,12 @@ void gla_scan_bf16_kernel(GlaLaunch g) {
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     if (state_wave) {
-        f32x4 Mr[8];                                   // M[16kb + 4G + i][col]
+        const float sv = g.vscale ? sigma_of(*g.vscale) : 1.f;
+        f32x4 Mr[8];                                   // sv M[16kb + 4G + i][col]
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Mr[kb][i] = st[(16 * kb + 4 * G + i) * kD + col];
+            for (int i = 0; i < 4; ++i) Mr[kb][i] = st[(16 * kb + 4 * G + i) * kD + col] * sv;
         f16x8 bM[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -447,7 +420,7 @@ void gla_scan_bf16_kernel(GlaLaunch g) {
             for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    X[rb][i] = b4[rb][i] * (bf2f(v4[rb][i]) - x4[rb][i] * KM[rb][i]);
+                    X[rb][i] = b4[rb][i] * (bf2f(v4[rb][i]) * sv - x4[rb][i] * KM[rb][i]);
             const f16x8 xb[2] = {bfrag(X[0], X[1]), bfrag(X[2], X[3])};
             // U = T X (T lower triangular: row blocks 0,1 only see k-step 0)
             f32x4 U[4];
@@ -485,12 +458,12 @@ void gla_scan_bf16_kernel(GlaLaunch g) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st[(16 * kb + 4 * G + i) * kD + col] = Mr[kb][i];
+            for (int i = 0; i < 4; ++i) st[(16 * kb + 4 * G + i) * kD + col] = Mr[kb][i] / sv;
     } else {
-        const float scale = g.scale;
+        const float scale = g.scale / (g.vscale ? sigma_of(*g.vscale) : 1.f);
         issue_chunk(smem, g, bh, tile, 0, nch, cg, lane);
         for (long long c = 0; c < nch; ++c) {
-            wait_vmcnt0();     // this wave's part of chunk c has landed
+            wait_vmcnt<0>();     // this wave's part of chunk c has landed
             __syncthreads();   // B1
             if (c + 1 < nch) issue_chunk(smem + ((c + 1) & 1) * kStageBytes, g, bh, tile, c + 1, nch, cg, lane);
             const char* S = smem + (c & 1) * kStageBytes;
@@ -550,12 +523,7 @@ void gla_scan_bf16_kernel(GlaLaunch g) {
                 }
             }
         }
-        wait_vmcnt0();
-    }
-    if (g.done) {   // every thread's stores made visible device-wide, then this workgroup counted
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_add(g.done + bh, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        wait_vmcnt<0>();
     }
 }
 

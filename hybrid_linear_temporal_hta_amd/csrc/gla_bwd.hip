@@ -258,7 +258,7 @@ constexpr size_t kAl = 256;
 __host__ __device__ inline size_t al256(size_t x) { return (x + kAl - 1) / kAl * kAl; }
 
 struct BwdWs {
-    unsigned* maxbits;   // max |scale dO|, |dL/dM_L| as float bits
+    unsigned* maxbits;   // float bits: [0] max |scale dO|, |dL/dM_L|; [1] max |v|, |M_0|
     float* state;        // copy of the initial state (the forward scan runs in place)
     char* blocks;        // chunk operand blocks of the forward prep
     f16* save_m;         // [BH][nch][128][128] M0 per chunk
@@ -289,22 +289,31 @@ inline size_t bwd_ws_bytes(int BH, long long L) {
            al256((size_t)BH * L * kD * 2);
 }
 
-// Power of two sigma with max * sigma in [1, 2) (1 when the max is 0).
-__device__ __forceinline__ float sigma_of(unsigned bits) {
-    if (bits == 0u) return 1.f;
-    const int e = (int)((bits >> 23) & 0xffu) - 127;
-    return ldexpf(1.f, -max(-126, min(e, 126)));
-}
-
-// max |scale dO| and |dL/dM_L| (atomic max on the bits of non-negative floats).
-// dO is read 16 bytes per lane, four loads in flight per thread; |scale| is
-// applied to the maximum (rounding is monotonic: the same value as the maximum
-// of the rounded products).
+// maxbits[0] = max(|scale dO|, |dL/dM_L|) and maxbits[1] = max(|v|, |M_0|) (atomic
+// max on the bits of non-negative floats). dO and v are read 16 bytes per lane,
+// four loads in flight per thread; |scale| is applied to the maximum (rounding is
+// monotonic: the same value as the maximum of the rounded products).
 __global__ __launch_bounds__(256) void gla_bwd_max_kernel(GlaBwdLaunch b, unsigned* maxbits) {
     const long long nd = (long long)b.BH * b.L * kD, ns = (long long)b.BH * kD * kD;
     const long long stride = (long long)gridDim.x * 256;
     const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-    float m = 0.f;
+    float m = 0.f, mv = 0.f;
+    {
+        const long long n8 = nd / 8;
+        const bf16x8* p = static_cast<const bf16x8*>(b.v);
+        for (long long e = t; e < n8; e += 4 * stride) {
+            bf16x8 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e + u * stride < n8) x[u] = p[e + u * stride];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (e + u * stride < n8)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) mv = fmaxf(mv, fabsf(bf2f(x[u][i])));
+        }
+        for (long long e = t; e < ns; e += stride) mv = fmaxf(mv, fabsf(b.state0[e]));
+    }
     if (b.do_f32) {
         const long long n4 = nd / 4;
         const f32x4* p = static_cast<const f32x4*>(b.dout);
@@ -336,12 +345,20 @@ __global__ __launch_bounds__(256) void gla_bwd_max_kernel(GlaBwdLaunch b, unsign
     m *= fabsf(b.scale);
     for (long long e = t; e < ns; e += stride) m = fmaxf(m, fabsf(b.dstate[e]));
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-    __shared__ float wm[4];   // one atomic per workgroup: same-address atomics serialise
-    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+    for (int s = 32; s >= 1; s >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, s, 64));
+        mv = fmaxf(mv, __shfl_xor(mv, s, 64));
+    }
+    __shared__ float wm[2][4];   // one atomic per workgroup: same-address atomics serialise
+    if ((threadIdx.x & 63) == 0) {
+        wm[0][threadIdx.x >> 6] = m;
+        wm[1][threadIdx.x >> 6] = mv;
+    }
     __syncthreads();
-    if (threadIdx.x == 0)
-        atomicMax(maxbits, __float_as_uint(fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]))));
+    if (threadIdx.x < 2) {
+        const float* r = wm[threadIdx.x];
+        atomicMax(maxbits + threadIdx.x, __float_as_uint(fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]))));
+    }
 }
 
 // gh = fp16(sigma * scale * dO), 8 elements per thread.
@@ -350,7 +367,7 @@ __global__ __launch_bounds__(256) void gla_bwd_gh_kernel(GlaBwdLaunch b, const u
     const long long n8 = (long long)b.BH * b.L * kD / 8;
     const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
     if (e >= n8) return;
-    const float f = sigma_of(*maxbits) * b.scale;
+    const float f = sigma_of(maxbits[0]) * b.scale;
     f16x8 o;
     if (b.do_f32) {
         const f32x4* s = reinterpret_cast<const f32x4*>(b.dout) + 2 * e;
@@ -374,9 +391,9 @@ __device__ __forceinline__ void issue_rchunk(char* stage, const char* blocks, co
 #pragma unroll
     for (int i = 0; i < 12; ++i) {
         const int q = 12 * wave + i;
-        dma16(blk + 1024 * q + 16 * lane, stage + 1024 * q);
+        dma16p(blk + 1024 * q + 16 * lane, stage + 1024 * q);
     }
-    if (wave == 0 && lane < kTailChunks) dma16(blk + kBlockMain + 16 * lane, stage + kBlockMain);
+    if (wave == 0 && lane < kTailChunks) dma16p(blk + kBlockMain + 16 * lane, stage + kBlockMain);
     const long long t0 = c * kC;
     const int n = (int)min((long long)kC, L - t0);
     const f16* gb = gh + ((long long)bh * L + t0) * kD + tile * 64;
@@ -385,7 +402,7 @@ __device__ __forceinline__ void issue_rchunk(char* stage, const char* blocks, co
         const int p = 64 * (2 * wave + i) + lane;
         const int tok = p >> 3;
         const int cc = (p & 7) ^ swzv(tok);
-        dma16(gb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * wave + i));
+        dma16p(gb + (long long)min(tok, n - 1) * kD + 8 * cc, stage + kOffV + 1024 * (2 * wave + i));
     }
 }
 
@@ -405,7 +422,7 @@ __global__ __launch_bounds__(256) void gla_rscan_kernel(GlaBwdLaunch b, BwdWs w)
     const int colw = wave * 16 + m;
     const int col = tile * 64 + colw;
     const long long nch = (b.L + kC - 1) / kC;
-    const float sig = sigma_of(*w.maxbits);
+    const float sig = sigma_of(w.maxbits[0]);
 
     float* st = b.dstate + (long long)bh * kD * kD;
     f32x4 dM[8];
@@ -418,7 +435,7 @@ __global__ __launch_bounds__(256) void gla_rscan_kernel(GlaBwdLaunch b, BwdWs w)
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     for (long long cc = 0; cc < nch; ++cc) {
         const long long c = nch - 1 - cc;
-        wait_vmcnt0();
+        wait_vmcnt<0>();
         __syncthreads();
         if (c > 0) issue_rchunk(smem + ((cc + 1) & 1) * kStageBytes, w.blocks, w.gh, b.L, bh, tile,
                                 c - 1, nch, wave, lane);
@@ -606,7 +623,8 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
     const int n = (int)min((long long)kC, b.L - t0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int m = lane & 15, G = lane >> 4;
-    const float sig = sigma_of(*w.maxbits);
+    const float sig = sigma_of(w.maxbits[0]);
+    const float svv = sigma_of(w.maxbits[1]);          // the forward ran on sigma_v (v, M_0)
     const long long tok0 = (long long)bh * b.L + t0;   // first token row of the chunk
     const long long ci = (long long)bh * nch + c;      // chunk index
     // Pm at this lane's phase-4 positions (rows 16 mt + 4G + i of the wave's two row
@@ -844,8 +862,9 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
     mm_wide<kC>(D1, kLc, KT, kLc, accQ, wave, lane);
     mm_wide<kC>(D1T, kLc, QT, kLc, accK, wave, lane);
     mm_wide<kC>(Bs, kLc, KT, kLc, accK, wave, lane);
-    // ---- phase 7: outputs (scaled back by 1/sigma)
-    const float inv = 1.f / sig;
+    // ---- phase 7: outputs (scaled back by 1/sigma; those that scale with the
+    // forward's values, dq, dk, dalpha, dbeta, also by 1/sigma_v)
+    const float inv = 1.f / sig, invv = inv / svv;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -853,7 +872,7 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
             const int row = 16 * mt + 4 * G + i;
             if (row < n) {
                 const long long o = (tok0 + row) * kD + 16 * wave + m;
-                const float xq = accQ[mt][i] * inv, xk = accK[mt][i] * inv;
+                const float xq = accQ[mt][i] * invv, xk = accK[mt][i] * invv;
                 if (b.grad_f32) {
                     static_cast<float*>(b.dq)[o] = xq;
                     static_cast<float*>(b.dk)[o] = xk;
@@ -874,7 +893,7 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float r = (float)Rr[row * kLd + c8 + i];
-                s += r * bf2f(vv[i]);
+                s += r * (bf2f(vv[i]) * svv);
                 ov[i] = bs[row] * r * inv;
             }
             const long long o = (tok0 + row) * kD + c8;
@@ -905,8 +924,8 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
         }
         const float dla = sx + (b.form ? sy - y : sy);
         if (lane < n) {
-            b.dalpha[tok0 + lane] = dla / als[lane] * inv;
-            b.dbeta[tok0 + lane] = dbt[lane] * inv;
+            b.dalpha[tok0 + lane] = dla / als[lane] * invv;
+            b.dbeta[tok0 + lane] = dbt[lane] * invv;
         }
     }
 }
@@ -937,7 +956,11 @@ hipError_t launch_gla_bwd(const GlaBwdLaunch& b, hipStream_t stream) {
     BwdWs w = bwd_ws(b.ws, b.BH, b.L);
     hipError_t e;
     if ((e = launch_fill_f32(w.state, b.state0, (long long)b.BH * kD * kD, stream)) != hipSuccess) return e;
-    if ((e = launch_fill_f32(reinterpret_cast<float*>(w.maxbits), nullptr, 1, stream)) != hipSuccess) return e;
+    if ((e = launch_fill_f32(reinterpret_cast<float*>(w.maxbits), nullptr, 2, stream)) != hipSuccess) return e;
+    const long long nd = (long long)b.BH * b.L * kD;
+    const long long gmax = min(1024LL, (nd + 255) / 256);
+    hipLaunchKernelGGL(gla_bwd_max_kernel, dim3((unsigned)gmax), dim3(256), 0, stream, b, w.maxbits);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     GlaLaunch g;
     memset(&g, 0, sizeof(g));
     g.q = b.q; g.k = b.k; g.v = b.v; g.alpha = b.alpha; g.beta = b.beta;
@@ -948,11 +971,8 @@ hipError_t launch_gla_bwd(const GlaBwdLaunch& b, hipStream_t stream) {
     g.ws_bytes = (size_t)b.BH * nch * kChunkBytes;
     g.save_m = w.save_m;
     g.save_u = w.save_u;
+    g.vscale = w.maxbits + 1;
     if ((e = launch_gla_bf16(g, stream)) != hipSuccess) return e;
-    const long long nd = (long long)b.BH * b.L * kD;
-    const long long gmax = min(1024LL, (nd + 255) / 256);
-    hipLaunchKernelGGL(gla_bwd_max_kernel, dim3((unsigned)gmax), dim3(256), 0, stream, b, w.maxbits);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     const long long n8 = (nd / 8 + 255) / 256;
     hipLaunchKernelGGL(gla_bwd_gh_kernel, dim3((unsigned)n8), dim3(256), 0, stream, b,
                        (const unsigned*)w.maxbits, w.gh);

@@ -9,6 +9,7 @@
 
 #include "device_common.h"
 #include "hta_internal.h"
+#include "lds_dma.h"
 
 namespace hta {
 namespace glat {
@@ -46,18 +47,6 @@ __device__ __forceinline__ int offK(int row, int col) {   // byte offset of elem
 __device__ __forceinline__ int offT(int row, int col) {
     return row * 128 + 16 * ((col >> 3) ^ swz32(row)) + 2 * (col & 7);
 }
-
-// One global_load_lds_dwordx4 (16 bytes per lane into LDS at base + 16 * lane,
-// base wave-uniform). Written as asm so the compiler does not serialise it
-// against LDS reads of the other stage; completion is tracked by wait_vmcnt0.
-// It has no register outputs.
-__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
-    typedef __attribute__((address_space(3))) const char lds_char;
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)lds_base);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(gptr) : "m0");
-}
-
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
 
 // A fragment of a 16-row block from a swizzled fp16 tile: row `row`, k-step
 // columns 32*ks + 4G + j (j < 4) and 32*ks + 16 + 4G + (j - 4).
@@ -108,6 +97,34 @@ __device__ __forceinline__ f16x8 afragTt(const char* base, int rb, int kt, int l
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + offT(t0, col)));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + offT(t0 + 16, col)));
     return cat(__builtin_bit_cast(f16x4, lo), __builtin_bit_cast(f16x4, hi));
+}
+
+// Lane l reads lane l ^ 1 (resp. l ^ 2) of its quad: DPP quad permutes.
+__device__ __forceinline__ float quad_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+// 16x16x16 fp32 product on v_mfma_f32_16x16x4_f32: acc += X Y for 16x16 blocks X
+// (row stride xld) and Y (row stride yld) in LDS; lane l ends with rows
+// 4 (l / 16) + i of column l % 16.
+__device__ __forceinline__ f32x4 mm16f(const float* X, int xld, const float* Y, int yld,
+                                       f32x4 acc, int lane) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[m * xld + 4 * s + g], Y[(4 * s + g) * yld + m],
+                                                   acc, 0, 0, 0);
+    return acc;
+}
+
+// Power of two sigma with max * sigma in [1, 2) (1 when the max is 0).
+__device__ __forceinline__ float sigma_of(unsigned bits) {
+    if (bits == 0u) return 1.f;
+    const int e = (int)((bits >> 23) & 0xffu) - 127;
+    return ldexpf(1.f, -max(-126, min(e, 126)));
 }
 
 }  // namespace glat

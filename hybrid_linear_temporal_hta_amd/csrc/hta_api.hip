@@ -9,8 +9,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <mutex>
-
 #include "../../include/hta.h"
 #include "hta_internal.h"
 
@@ -98,6 +96,7 @@ int check_params(const hta_shape* s, const hta_params* p) {
     if (!isfinite(p->gla_scale)) return HTA_ERR_UNSUPPORTED;
     if (p->gla_form != HTA_GLA_GATED_DELTA && p->gla_form != HTA_GLA_PRINTED)
         return HTA_ERR_UNSUPPORTED;
+    if (p->side_stream && (!p->fork_event || !p->join_event)) return HTA_ERR_NULL;
     return HTA_OK;
 }
 
@@ -113,86 +112,71 @@ size_t out_bytes(const hta_shape* s) {
 size_t gate_bytes(const hta_shape* s) { return (size_t)s->B * s->H * (size_t)s->T * s->P * 4; }
 size_t state_bytes(const hta_shape* s) { return (size_t)s->B * s->H * s->dk * s->dv * 4; }
 
-// Workspace: [GLA scratch][fp32 GLA partial][fp32 SWA partial (bf16 o only)].
+// Workspace of the bf16 hybrid and stream step: [GLA chunk blocks][fp32 GLA
+// partial][fp32 SWA output (bf16 o only)][parked softmax states].
 size_t gla_ws(const hta_shape* s, int chunk) {
+    (void)chunk;
     if (s->dtype == HTA_F32) return kAlign;
     const long long L = (long long)s->T * s->P;
-    return align_up(hta::gla_bf16_workspace_bytes(s->B * s->H, L, chunk));
+    return align_up(hta::gla_fwd_workspace_bytes(s->B * s->H, L));
 }
-// bf16 inputs: the GLA branch runs beside the SWA pass, each into an fp32
-// partial of its own (the SWA one is o itself when o is fp32), and the DSWA
-// pass adds both. fp32 inputs (small workloads) run the branches in sequence
-// with the GLA partial in o.
 size_t fp32_seq_bytes(const hta_shape* s) {
     return align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dv * 4);
 }
 size_t park_ws(const hta_shape* s) {
     return align_up(hta::win_attn_park_bytes(s->B * s->H, s->T, s->P));
 }
-// The hybrid's hand-off between the GLA scan and the attention pass: one
-// completion counter per head, one pending flag per attention wave.
-size_t sync_ws(const hta_shape* s) {
-    return align_up((size_t)s->B * s->H * sizeof(unsigned)) +
-           align_up(hta::win_pend_bytes(s->B * s->H, s->T, s->P));
-}
+// bf16 inputs: the GLA branch runs first into an fp32 partial; the one-pass
+// attention then adds it in its epilogue. The SWA branch's output (written at the
+// switch between the windows) goes to o itself when o is fp32, else to an fp32
+// buffer. fp32 inputs (small workloads) keep the GLA partial in o.
 size_t partial_ws(const hta_shape* s) {
     if (s->dtype == HTA_F32) return 0;
-    return fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2) + park_ws(s) + sync_ws(s);
+    return fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2) + park_ws(s);
 }
-// Layout of partial_ws: [GLA partial][attention partial (bf16 o only)][park]
-// [scan counters][pending flags].
 struct Partials {
-    float* park;
-    unsigned* done;
-    unsigned char* pend;
+    float* gla;    // fp32 GLA partial
+    float* oa;     // fp32 SWA output (o itself when o is fp32)
+    float* park;   // parked softmax states
 };
-Partials partials_of(const hta_shape* s, char* partials) {
-    char* c = partials + fp32_seq_bytes(s) * (s->out_dtype == HTA_F32 ? 1 : 2);
+Partials partials_of(const hta_shape* s, char* partials, void* o) {
     Partials pt;
+    pt.gla = reinterpret_cast<float*>(partials);
+    char* c = partials + fp32_seq_bytes(s);
+    if (s->out_dtype == HTA_F32) {
+        pt.oa = static_cast<float*>(o);
+    } else {
+        pt.oa = reinterpret_cast<float*>(c);
+        c += fp32_seq_bytes(s);
+    }
     pt.park = reinterpret_cast<float*>(c);
-    c += park_ws(s);
-    pt.done = reinterpret_cast<unsigned*>(c);
-    c += align_up((size_t)s->B * s->H * sizeof(unsigned));
-    pt.pend = reinterpret_cast<unsigned char*>(c);
     return pt;
 }
 
-// One auxiliary stream and two events per device, created on first use and
-// kept until the process exits: the hybrid forks its GLA branch onto the
-// auxiliary stream so that the latency-bound chunk scan (few workgroups) runs
-// beside the SWA pass. The mutex makes each fork/join sequence atomic with
-// respect to other host threads sharing the events.
-struct Aux {
+// The caller's side stream (hta_params): work that runs beside `stream`, forked
+// and joined through the caller's two events. NULL: everything on `stream`.
+struct Side {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
-    int cus = 0;   // compute units of the device
 };
-constexpr int kMaxDevices = 64;
-std::mutex g_aux_mu;
-Aux g_aux[kMaxDevices];
-
-hipError_t aux_for_current_device(Aux** out) {   // g_aux_mu held
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    Aux& a = g_aux[dev];
-    if (!a.s) {
-        Aux n;
-        e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) {
-            if (n.join) (void)hipEventDestroy(n.join);
-            if (n.fork) (void)hipEventDestroy(n.fork);
-            if (n.s) (void)hipStreamDestroy(n.s);
-            return e;
-        }
-        a = n;
+Side side_of(const hta_params* p) {
+    Side d;
+    if (p && p->side_stream) {
+        d.s = static_cast<hipStream_t>(p->side_stream);
+        d.fork = static_cast<hipEvent_t>(p->fork_event);
+        d.join = static_cast<hipEvent_t>(p->join_event);
     }
-    *out = &a;
-    return hipSuccess;
+    return d;
+}
+// Work enqueued on d.s after fork() is ordered after everything already on sm;
+// join() orders later work on sm after everything enqueued on d.s.
+hipError_t fork(const Side& d, hipStream_t sm) {
+    hipError_t e = hipEventRecord(d.fork, sm);
+    return e == hipSuccess ? hipStreamWaitEvent(d.s, d.fork, 0) : e;
+}
+hipError_t join(const Side& d, hipStream_t sm) {
+    hipError_t e = hipEventRecord(d.join, d.s);
+    return e == hipSuccess ? hipStreamWaitEvent(sm, d.join, 0) : e;
 }
 
 hta::WinLaunch win_base(const hta_shape* s, const void* q, const void* k, const void* v, void* o,
@@ -284,7 +268,7 @@ hta::GlaLaunch gla_base(const hta_shape* s, const void* q, const void* k, const 
 }
 
 hipError_t run_gla(const hta::GlaLaunch& g, hipStream_t st) {
-    return g.dtype == HTA_F32 ? hta::launch_gla_f32(g, st) : hta::launch_gla_bf16(g, st);
+    return g.dtype == HTA_F32 ? hta::launch_gla_f32(g, st) : hta::launch_gla_fwd(g, st);
 }
 
 size_t gla_bwd_ws(const hta_shape* s) {
@@ -330,65 +314,55 @@ size_t swa_dswa_ws(const hta_shape* s) {
     return park_ws(s) + fp32_seq_bytes(s);
 }
 
-// bf16 hybrid: the GLA prep (chunk-parallel, the whole chip), then the GLA scan
-// (one workgroup per (b, h, 64 value columns), latency-bound) on `sm`, beside
-// ONE attention pass on the auxiliary stream, forked after the prep, that runs
-// both windows with one accumulator set (the query's own frame, common to both,
-// attended once: its softmax state is parked in memory while the SWA taps
-// finish, then resumed for the DSWA taps). The scan is next in its queue when
-// the prep ends, so its few workgroups take their CUs before the attention
-// workgroups (which can never share a CU with a scan workgroup) fill the chip.
-// When the attention pass spans several waves of workgroups, it adds the GLA
-// partial itself wherever the scan has already finished that head (a counter
-// per head, read once per wave, never waited on); the rows it finished earlier
-// go to `att` (fp32: o itself, or a partial for a bf16 o) and a last kernel adds
-// the partial to those only, rounding once. Both routes sum in the same order,
-// so the result does not depend on the timing. A pass of one wave (a streamed
-// frame) ends long after its scan, all at once: there the partial is added by
-// one kernel after it, which keeps the extra reads out of the pass's tail.
+// bf16 hybrid (and streamed frame). One attention pass runs both windows with one
+// accumulator set (the query's own frame, common to both, is attended once: its
+// softmax state is parked in memory while the SWA taps finish, then resumed for
+// the DSWA taps); the GLA branch (chunk-parallel prep, then the chunk scan) goes
+// into an fp32 partial.
+//   - Without a side stream, on `sm` in order: the GLA branch over the whole chip,
+//     then the attention pass, whose epilogue adds both windows and the GLA
+//     partial and rounds once.
+//   - With the caller's side stream: the GLA prep on `sm`, then the attention pass
+//     (its sum in fp32, no partial) on the side stream beside the GLA scan on `sm`
+//     in its narrow shape (two workgroups per head, so the pass keeps nearly the
+//     whole chip); after the join one elementwise pass adds the GLA partial and
+//     rounds once. Both routes form (DSWA + SWA) + GLA in fp32 in the same order,
+//     so they give the same bits.
 // For a training forward, `tr` receives each branch's log-sum-exp and branch B's
 // (DSWA's) output, and `oa` (when given) branch A's (SWA's) output.
-hipError_t run_hybrid_fused(hta::GlaLaunch g, const hta::WinLaunch& w, float* att,
-                            const Partials& pt, const hta_params* p, hipStream_t sm,
-                            const TrainOut& tr = TrainOut(), float* oa = nullptr) {
-    std::lock_guard<std::mutex> lock(g_aux_mu);
-    Aux* a = nullptr;
-    hipError_t e = aux_for_current_device(&a);
-    if (e != hipSuccess) return e;
+hipError_t run_hybrid(hta::GlaLaunch g, const hta::WinLaunch& w, const Partials& pt,
+                      const hta_params* p, hipStream_t sm, const TrainOut& tr = TrainOut(),
+                      float* oa = nullptr) {
+    g.o = pt.gla;
+    g.out_f32 = 1;
     hta::WinLaunch f = w;
     f.nbr = 3;
     taps_hybrid(f.taps, p->swa_window, p->dswa_taps, p->dswa_dilation);
-    f.oa = oa ? oa : att;
+    f.oa = oa ? oa : pt.oa;
     f.park = pt.park;
     f.add2 = nullptr;
     f.lse = tr.lse_a;
     f.lse2 = tr.lse_b;
     f.obr = tr.obr_b;
-    // The scan signals completion (each workgroup writes its XCD's L2 back)
-    // only when the pass reads the signal.
-    const bool handoff = hta::win_attn_workgroups(f) > 2LL * a->cus;
-    if (handoff) {
-        g.done = pt.done;
-        f.add = static_cast<const float*>(g.o);
-        f.add_ready = pt.done;
-        f.add_need = 2;   // the head's two scan workgroups
-        f.part = att;
-        f.pend = pt.pend;
-    } else {
-        f.o = att;
-        f.out_f32 = 1;
-        f.add = nullptr;
+    const Side d = side_of(p);
+    hipError_t e;
+    if (!d.s) {
+        if ((e = hta::launch_gla_fwd(g, sm)) != hipSuccess) return e;
+        f.add = pt.gla;
+        return hta::launch_win_attn(f, sm);
     }
-    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
-    if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return e;
-    if ((e = hta::launch_gla_bf16(g, sm, hta::kGlaScan)) != hipSuccess) return e;
-    if ((e = hta::launch_win_attn(f, a->s)) != hipSuccess) return e;
-    if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return e;
-    if (handoff) return hta::launch_win_add_pending(f, sm);
+    // the pass's fp32 sum: o itself, or the SWA buffer (read back in place, row by row)
+    float* att = w.out_f32 ? static_cast<float*>(w.o) : pt.oa;
+    f.o = att;
+    f.out_f32 = 1;
+    f.add = nullptr;
+    if ((e = hta::launch_gla_fwd(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
+    if ((e = fork(d, sm)) != hipSuccess) return e;
+    if ((e = hta::launch_gla_fwd(g, sm, hta::kGlaScanNarrow)) != hipSuccess) return e;
+    if ((e = hta::launch_win_attn(f, d.s)) != hipSuccess) return e;
+    if ((e = join(d, sm)) != hipSuccess) return e;
     const long long n = (long long)w.BH * w.Tq * w.P * w.d;
-    return hta::launch_add_f32(w.o, w.out_f32 ? 0 : 1, att, static_cast<const float*>(g.o), n, sm);
+    return hta::launch_add_f32(w.o, w.out_f32 ? 0 : 1, att, pt.gla, n, sm);
 }
 
 // What a training forward keeps for hta_hybrid_bwd (caller-owned `saved`).
@@ -421,7 +395,8 @@ Saved saved_of(const hta_shape* s, void* p) {
 size_t attn_bwd_stats_bytes(const hta_shape* s) {
     return align_up(((size_t)s->B * s->H * (size_t)s->T * s->P + 64) * 8);
 }
-// bf16 inputs: the maxima that scale dS (256 bytes) and fp16 copies of q and k.
+// bf16 inputs: the maxima that scale dS and the fp16 copies (256 bytes: |dO|, |v|,
+// |q|, |k|) and the fp16 copies of q and k.
 size_t attn_bwd_aux_bytes(const hta_shape* s) {
     if (s->dtype != HTA_BF16) return 0;
     return kAlign + 2 * align_up((size_t)s->B * s->H * (size_t)s->T * s->P * s->dk * 2);
@@ -443,7 +418,7 @@ hipError_t bind_bwd_aux(const hta_shape* s, char* aux, hta::BwdPrep& p, hipStrea
     p.gmax = reinterpret_cast<unsigned*>(aux);
     p.q16 = aux + kAlign;
     p.k16 = aux + kAlign + nqk;
-    return hta::launch_fill_f32(reinterpret_cast<float*>(aux), nullptr, 2, st);
+    return hta::launch_fill_f32(reinterpret_cast<float*>(aux), nullptr, 4, st);
 }
 void use_bwd_aux(const hta::BwdPrep& p, hta::BwdLaunch& b) {
     b.gmax = p.gmax;
@@ -866,21 +841,16 @@ int hta_hybrid_fwd_train(const hta_shape* shape, const hta_params* params, const
     if (e != hipSuccess) return hip_fail(e);
     hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
     if (shape->dtype == HTA_BF16) {
-        // the one-pass attention of the inference forward, writing what the backward
-        // reads besides o: the SWA output and both branches' log-sum-exp
+        // the inference forward's GLA branch and one-pass attention, writing what the
+        // backward reads besides o: the SWA output and both branches' log-sum-exp
         char* wsb = static_cast<char*>(workspace);
-        float* gpart = reinterpret_cast<float*>(wsb + need_gla);
-        float* att = shape->out_dtype == HTA_F32
-                         ? static_cast<float*>(o)
-                         : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(shape));
-        hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, gpart, params->gla_chunk,
+        hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, nullptr, params->gla_chunk,
                                     params->gla_scale, workspace, need_gla, params->gla_form);
-        g.out_f32 = 1;
         TrainOut tr;
         tr.lse_a = sv.lse_swa;
         tr.lse_b = sv.lse_dswa;
         tr.obr_b = sv.o_dswa;
-        e = run_hybrid_fused(g, w, att, partials_of(shape, wsb + need_gla), params, sm, tr, sv.o_swa);
+        e = run_hybrid(g, w, partials_of(shape, wsb + need_gla, o), params, sm, tr, sv.o_swa);
         return e == hipSuccess ? HTA_OK : hip_fail(e);
     }
     // fp32: GLA into o, the SWA pass into saved, the DSWA pass adding both into o
@@ -985,22 +955,18 @@ int hta_hybrid_bwd(const hta_shape* shape, const hta_params* params, const void*
     hta::BwdPrep pr2 = pr;
     pr2.q16 = nullptr; pr2.k16 = nullptr; pr2.gmax = nullptr; pr2.dout_bf16 = nullptr;
     pr2.o = sv.o_dswa; pr2.lse = sv.lse_dswa; pr2.stats = stats_b;
-    if (shape->dtype == HTA_BF16) {
+    const Side d = side_of(params);
+    if (d.s) {
         // The GLA backward (two latency-bound chunk scans with few workgroups, and a
         // chunk-parallel gradient kernel) on `sm`, beside the SWA backward on the
-        // auxiliary stream; the DSWA backward then adds both sets of partials.
-        std::lock_guard<std::mutex> lock(g_aux_mu);
-        Aux* a = nullptr;
-        if ((e = aux_for_current_device(&a)) != hipSuccess) return hip_fail(e);
-        if ((e = hipEventRecord(a->fork, sm)) != hipSuccess) return hip_fail(e);
-        if ((e = hipStreamWaitEvent(a->s, a->fork, 0)) != hipSuccess) return hip_fail(e);
+        // caller's side stream; the DSWA backward then adds both sets of partials.
+        if ((e = fork(d, sm)) != hipSuccess) return hip_fail(e);
         if ((e = hta::launch_gla_bwd(gb, sm)) != hipSuccess) return hip_fail(e);
         pr.o = sv.o_swa; pr.lse = sv.lse_swa; pr.stats = stats_a; pr.dout_bf16 = do_bf16;
-        if ((e = hta::launch_win_bwd_prep(pr, a->s)) != hipSuccess) return hip_fail(e);
-        if ((e = hta::launch_win_bwd(bs, a->s)) != hipSuccess) return hip_fail(e);
-        if ((e = hipEventRecord(a->join, a->s)) != hipSuccess) return hip_fail(e);
+        if ((e = hta::launch_win_bwd_prep(pr, d.s)) != hipSuccess) return hip_fail(e);
+        if ((e = hta::launch_win_bwd(bs, d.s)) != hipSuccess) return hip_fail(e);
         if ((e = hta::launch_win_bwd_prep(pr2, sm)) != hipSuccess) return hip_fail(e);
-        if ((e = hipStreamWaitEvent(sm, a->join, 0)) != hipSuccess) return hip_fail(e);
+        if ((e = join(d, sm)) != hipSuccess) return hip_fail(e);
         e = hta::launch_win_bwd(bd, sm);
         return e == hipSuccess ? HTA_OK : hip_fail(e);
     }
@@ -1027,15 +993,10 @@ int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params, const void*
     hipStream_t sm = static_cast<hipStream_t>(stream);
     char* wsb = static_cast<char*>(workspace);
     if (shape->dtype == HTA_BF16) {
-        float* gpart = reinterpret_cast<float*>(wsb + need_gla);
-        float* mid = shape->out_dtype == HTA_F32
-                         ? static_cast<float*>(o)
-                         : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(shape));
-        hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, gpart, params->gla_chunk,
+        hta::GlaLaunch g = gla_base(shape, q, k, v, alpha, beta, state, nullptr, params->gla_chunk,
                                     params->gla_scale, workspace, need_gla, params->gla_form);
-        g.out_f32 = 1;
         hta::WinLaunch w = win_base(shape, q, k, v, o, params->attn_scale);
-        hipError_t e = run_hybrid_fused(g, w, mid, partials_of(shape, wsb + need_gla), params, sm);
+        hipError_t e = run_hybrid(g, w, partials_of(shape, wsb + need_gla, o), params, sm);
         return e == hipSuccess ? HTA_OK : hip_fail(e);
     }
     // fp32 inputs: GLA into o, then SWA + DSWA adding it in place.
@@ -1221,16 +1182,11 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
     //    partial -- the two side by side for bf16 inputs.
     char* wsb = static_cast<char*>(workspace);
     if (o && s.dtype == HTA_BF16) {
-        float* gpart = reinterpret_cast<float*>(wsb + need_gla);
-        float* mid = s.out_dtype == HTA_F32
-                         ? static_cast<float*>(o)
-                         : reinterpret_cast<float*>(wsb + need_gla + fp32_seq_bytes(&s));
-        hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, gpart, ctx->p.gla_chunk,
+        hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, nullptr, ctx->p.gla_chunk,
                                     ctx->p.gla_scale, workspace, need_gla, ctx->p.gla_form);
-        g.out_f32 = 1;
         ring_into(g);
-        e = run_hybrid_fused(g, ring_launch(ctx, s, q, o, n), mid, partials_of(&s, wsb + need_gla),
-                             &ctx->p, sm);
+        e = run_hybrid(g, ring_launch(ctx, s, q, o, n), partials_of(&s, wsb + need_gla, o), &ctx->p,
+                           sm);
         if (e != hipSuccess) return hip_fail(e);
     } else {
         hta::GlaLaunch g = gla_base(&s, q, k, v, alpha, beta, ctx->state, o, ctx->p.gla_chunk,

@@ -49,19 +49,8 @@ struct WinLaunch {
                             //   branch; nbr 3: branch B's)
     float* park;            // nbr 3: scratch, win_attn_park_bytes(BH, Tq, P) bytes
     float* oa;              // nbr 3: fp32 [BH][Tq*P][dv] for branch A's output (may be o when
-                            //   o is fp32 and no partial is added)
-    const unsigned* add_ready;  // nbr 3, optional [BH]: `add` of head bh is complete once
-                            //   add_ready[bh] >= add_need, read once per wave, never waited
-                            //   on; a wave that finds it incomplete writes its rows without
-                            //   the add to `part` and flags them in `pend`
-    unsigned add_need;
-    float* part;            // with add_ready: fp32 [BH][Tq*P][dv] (may be o when o is fp32)
-    unsigned char* pend;    // with add_ready: one byte per (workgroup, wave), win_pend_bytes
+                            //   o is fp32 and no partial is added in place)
 };
-size_t win_pend_bytes(int BH, int Tq, int P);
-long long win_attn_workgroups(const WinLaunch& w);   // of launch_win_attn (bf16 inputs)
-// o = part + add for the rows a win_attn pass (nbr 3, add_ready set) flagged in pend.
-hipError_t launch_win_add_pending(const WinLaunch& w, hipStream_t stream);
 size_t win_attn_park_bytes(int BH, int Tq, int P);
 
 // dst = a + b elementwise (fp32), written as fp32 or rounded to bf16; n a multiple of 4.
@@ -89,7 +78,8 @@ struct BwdPrep {
     void* q16;
     void* k16;
     const void* v;          // v [rows][d] bf16: max |v| into gmax[1]
-    unsigned* gmax;         // max |dout| (as rounded) and max |v|, float bits, zeroed before
+    unsigned* gmax;         // float bits, zeroed before: max |dout| (as rounded), max |v|,
+                            //   and (with q16) max |q|, max |k| -- the copies' scales
 };
 hipError_t launch_win_bwd_prep(const BwdPrep& p, hipStream_t stream);
 
@@ -114,8 +104,8 @@ struct BwdLaunch {
     float scale;
     int ntaps;
     int off[kMaxTaps];      // ascending frame offsets: query frame f reads key frames f - off[j]
-    // bf16 path: fp16 copies of q and k (exact for |x| < 65504) and the maxima
-    // that fix the power-of-two scale of dS in its fp16 products
+    // bf16 path: fp16 copies 2^eq q and 2^ek k and the maxima that fix those
+    // powers of two and the one of dS in its fp16 products (gmax[0..3])
     const void* q16;
     const void* k16;
     const unsigned* gmax;
@@ -146,9 +136,10 @@ struct GlaLaunch {
     size_t ws_bytes;
     void* save_m;           // optional fp16 [BH][nch][d][d]: the state entering each chunk
     void* save_u;           // optional fp16 [BH][nch][64][d]: each chunk's U (bf16 path)
-    unsigned* done;         // optional [BH] (bf16 path): the prep zeroes it; each of a head's
-                            //   two scan workgroups adds 1 once its output rows are visible
-                            //   device-wide, so a head's output is complete at 2
+    const unsigned* vscale; // optional (saving scan): float bits of max(|v|, |state|); the scan
+                            //   runs on v and the state times the power of two that maps it
+                            //   into [1, 2) (saved M0, U carry the factor; o and the final
+                            //   state do not)
 };
 
 // Backward of the GLA branch over one sequence per (b,h): given dL/do and
@@ -204,6 +195,13 @@ hipError_t launch_gla_f32(const GlaLaunch& g, hipStream_t stream);
 constexpr int kGlaPrep = 1, kGlaScan = 2;
 hipError_t launch_gla_bf16(const GlaLaunch& g, hipStream_t stream, int parts = kGlaPrep | kGlaScan);
 size_t gla_bf16_workspace_bytes(int BH, long long L, int chunk);
+// The bf16 forward (prep with per-chunk power-of-two operand scales, then the
+// chunk scan); o may be NULL (state only). parts: kGlaPrep and / or one scan
+// shape, kGlaScan (the whole chip) or kGlaScanNarrow (few compute units, to run
+// beside other work).
+constexpr int kGlaScanNarrow = 4;
+hipError_t launch_gla_fwd(const GlaLaunch& g, hipStream_t stream, int parts = kGlaPrep | kGlaScan);
+size_t gla_fwd_workspace_bytes(int BH, long long L);
 // Chunk operand block of the bf16 path (bytes per 64-token chunk).
 size_t gla_bf16_chunk_bytes();
 

@@ -24,6 +24,7 @@
 
 #include "device_common.h"
 #include "hta_internal.h"
+#include "lds_dma.h"
 
 namespace hta {
 
@@ -45,23 +46,6 @@ constexpr int kYRow = kBN * 4 + 16;  // fp32 epilogue rows, padded against bank 
 __device__ __forceinline__ int swzx(int r) { return (r >> 1) & 7; }
 // W tile (256-byte rows): the same rotation as the attention K/V tiles.
 __device__ __forceinline__ int swzw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-__device__ __forceinline__ void dma16p(uint32_t voff, const void* sbase, uint32_t lds) {
-    // readfirstlane returns int: widen each half as uint32_t
-    const uint64_t b = (uint64_t)(uintptr_t)sbase;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds), "v"(voff), "s"(sb)
-                 : "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_p() {
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.f / (1.f + __expf(-z)); }
 
@@ -143,8 +127,8 @@ void project_kernel(ProjLaunch p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t off = 1024u * (4 * wave + i);
-            dma16p(xsrc[i], xs, lx + off);
-            dma16p(wsrc[i], ws, lw + off);
+            dma16(xsrc[i], xs, lx + off);
+            dma16(wsrc[i], ws, lw + off);
         }
     };
 
@@ -160,7 +144,7 @@ void project_kernel(ProjLaunch p) {
     issue(0, 0);
     auto step = [&](int kt, auto stage_tag) {
         constexpr int ST = decltype(stage_tag)::value;
-        wait_vmcnt_p<0>();   // this stage's loads have landed ...
+        wait_vmcnt<0>();   // this stage's loads have landed ...
         __syncthreads();     // ... for every wave; the other stage was read by all
         if (kt + 1 < nk) issue(kt + 1, ST ^ 1);
         typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;

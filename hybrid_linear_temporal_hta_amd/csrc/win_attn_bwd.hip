@@ -18,11 +18,14 @@
 //              S = Q K^T and dP = dO V^T, and accumulates dV^T += dO^T P and
 //              dK^T += Q^T dS (dK and dV in two launches, S computed by both).
 // dS enters its products (dQ = K^T dS, dK = Q^T dS) in fp16, against fp16
-// copies of K and Q (exact for |x| < 65504) made by the prep: a bf16 dS costs
-// about 1 % of RMS in dq and dk, because sum_s ds_s = 0 makes those sums
-// cancel; fp16 keeps 11 significant bits. dS is scaled by a power of two sigma
-// from max |dO| max |v| (found by the prep) so that it sits in fp16's normal
-// range whatever the gradient's magnitude; the results are scaled back exactly.
+// copies of K and Q made by the prep: a bf16 dS costs about 1 % of RMS in dq and
+// dk, because sum_s ds_s = 0 makes those sums cancel; fp16 keeps 11 significant
+// bits. Every fp16 operand carries a power of two (exact: it changes no
+// rounding): the copies are 2^eq q and 2^ek k, with max |2^eq q|, |2^ek k| in
+// [8, 16) (a max pass over q and k runs first), so any finite bf16 q and k fit;
+// the logits formed from them are scaled back inside the exponent. dS is scaled
+// by sigma from max |dO| max |v| (found by the prep) so that it sits in fp16's
+// normal range whatever the gradient's magnitude; dq, dk are scaled back exactly.
 // The bf16 kernels (d = 128) keep their own 32 rows (queries or keys) as MFMA B
 // fragments in registers and stream the other side through a two-stage LDS
 // ring with direct global->LDS loads, as the forward does; the logits' register
@@ -47,6 +50,43 @@ constexpr int kRows = 128;   // queries (query pass) or keys (key pass) per work
 // prep: stats[row] = {lse * log2(e), dO . o}; 16 lanes per row, 16 rows per
 // block, the blocks strided over the grid (so that the maxima take one atomic
 // pair per workgroup: same-address atomics serialise).
+
+// Exponent e of the power of two 2^e that maps a maximum |x| (float bits) into
+// [8, 16); 0 for a zero or non-finite maximum.
+__device__ __forceinline__ int qk_exp(unsigned bits) {
+    const float m = __uint_as_float(bits);
+    if (!(m > 0.f) || !(m < __builtin_huge_valf())) return 0;
+    return max(-120, min(120, 3 - (__builtin_amdgcn_frexp_expf(m) - 1)));
+}
+
+// gmax[2] = max |q|, gmax[3] = max |k| (bf16, 16 bytes per lane, one atomic pair per
+// workgroup): the scales of the fp16 copies the prep makes.
+__global__ __launch_bounds__(256) void win_bwd_qkmax_kernel(const bf16* q, const bf16* k, long long n8,
+                                                            unsigned* gmax) {
+    __shared__ float mx[2][4];
+    float mq = 0.f, mk = 0.f;
+    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n8; e += (long long)gridDim.x * 256) {
+        const bf16x8 a = reinterpret_cast<const bf16x8*>(q)[e];
+        const bf16x8 b = reinterpret_cast<const bf16x8*>(k)[e];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mq = fmaxf(mq, fabsf(bf2f(a[i])));
+            mk = fmaxf(mk, fabsf(bf2f(b[i])));
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        mq = fmaxf(mq, __shfl_xor(mq, m, 64));
+        mk = fmaxf(mk, __shfl_xor(mk, m, 64));
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) { mx[0][wave] = mq; mx[1][wave] = mk; }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+        const float* m4 = mx[threadIdx.x];
+        atomicMax(gmax + 2 + threadIdx.x, __float_as_uint(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))));
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
@@ -87,13 +127,17 @@ __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
 #pragma unroll
             for (int i = 0; i < E; ++i) dst[i] = f2bf(dov[i]);
         }
-        if (p.q16 && ok) {   // exact fp16 copies of q and k (D == 128 here: 8 per lane)
+        if (p.q16 && ok) {   // fp16 copies 2^eq q and 2^ek k (D == 128 here: 8 per lane)
             const bf16* qs = static_cast<const bf16*>(p.q) + base;
             const bf16* ks = static_cast<const bf16*>(p.k) + base;
             f16* qd = static_cast<f16*>(p.q16) + base;
             f16* kd = static_cast<f16*>(p.k16) + base;
+            const float sq = ldexpf(1.f, qk_exp(p.gmax[2])), sk = ldexpf(1.f, qk_exp(p.gmax[3]));
 #pragma unroll
-            for (int i = 0; i < E; ++i) { qd[i] = (f16)bf2f(qs[i]); kd[i] = (f16)bf2f(ks[i]); }
+            for (int i = 0; i < E; ++i) {
+                qd[i] = (f16)(bf2f(qs[i]) * sq);
+                kd[i] = (f16)(bf2f(ks[i]) * sk);
+            }
         }
         float acc = 0.f;
 #pragma unroll
@@ -251,7 +295,8 @@ void win_bwd_dq_bf16_kernel(BwdLaunch w) {
     const long long srow = (long long)bh * w.T * w.P + (long long)fq * w.P + qrow;
     const float lse2 = valid ? w.stats[2 * srow] : 0.f;
     const float Dq = valid ? w.stats[2 * srow + 1] : 0.f;
-    const float c = w.scale * kLog2e;
+    const int eq = qk_exp(w.gmax[2]), ek = qk_exp(w.gmax[3]);
+    const float c = ldexpf(w.scale * kLog2e, -(eq + ek));   // the logits come from 2^eq q, 2^ek k
     const float sig = ds_sigma(w.gmax);
 
     f32x16 acc[4];
@@ -309,7 +354,7 @@ void win_bwd_dq_bf16_kernel(BwdLaunch w) {
         if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     }
     if (!valid) return;
-    store_rows(acc, w.scale / sig, w.add_q, w.add2_q, w.dq, w.out_f32, rowoff, h);
+    store_rows(acc, ldexpf(w.scale / sig, -ek), w.add_q, w.add2_q, w.dq, w.out_f32, rowoff, h);
 }
 
 // ---------------------------------------------------------------------------------
@@ -378,7 +423,8 @@ void win_bwd_key_bf16_kernel(BwdLaunch w) {
     bf16x8 vf[DK ? 8 : 1];
     load_rows_h(kf, static_cast<const f16*>(w.k16) + rowoff, valid, h);
     if (DK) load_rows(reinterpret_cast<bf16x8(&)[8]>(vf), static_cast<const bf16*>(w.v) + rowoff, valid, h);
-    const float c = w.scale * kLog2e;
+    const int eq = qk_exp(w.gmax[2]), ek = qk_exp(w.gmax[3]);
+    const float c = ldexpf(w.scale * kLog2e, -(eq + ek));   // the logits come from 2^eq q, 2^ek k
     const float sig = ds_sigma(w.gmax);
 
     f32x16 acc[4];   // dK^T or dV^T
@@ -453,7 +499,7 @@ void win_bwd_key_bf16_kernel(BwdLaunch w) {
         if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
     }
     if (!valid) return;
-    if (DK) store_rows(acc, w.scale / sig, w.add_k, w.add2_k, w.dk, w.out_f32, rowoff, h);
+    if (DK) store_rows(acc, ldexpf(w.scale / sig, -eq), w.add_k, w.add2_k, w.dk, w.out_f32, rowoff, h);
     else store_rows(acc, 1.f, w.add_v, w.add2_v, w.dv, w.out_f32, rowoff, h);
 }
 
@@ -577,6 +623,15 @@ __global__ __launch_bounds__(256) void win_bwd_dkdv_f32_kernel(BwdLaunch w) {
 
 hipError_t launch_win_bwd_prep(const BwdPrep& p, hipStream_t stream) {
     if (p.rows == 0) return hipSuccess;
+    if (p.q16) {   // the copies' scales first (gmax[2], gmax[3], zeroed by the caller)
+        if (p.d != 128 || !p.gmax) return hipErrorInvalidValue;
+        const long long n8 = p.rows * 128 / 8;
+        const long long g = std::min((n8 + 255) / 256, 2048LL);
+        hipLaunchKernelGGL(win_bwd_qkmax_kernel, dim3((unsigned)g), dim3(256), 0, stream,
+                           static_cast<const bf16*>(p.q), static_cast<const bf16*>(p.k), n8, p.gmax);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const long long nwg = std::min((p.rows + 15) / 16, 4096LL);
     if (p.d == 128)
         hipLaunchKernelGGL((win_bwd_prep_kernel<128>), dim3((unsigned)nwg), dim3(256), 0, stream, p);

@@ -12,6 +12,7 @@
 
 #include "device_common.h"
 #include "hta_internal.h"
+#include "lds_dma.h"
 
 namespace hta {
 namespace tiles {
@@ -33,46 +34,6 @@ __device__ __forceinline__ int taps_present(const int* off, int n, long long fa)
     int c = 0;
     for (int j = 0; j < n; ++j) c += (off[j] <= fa) ? 1 : 0;
     return c;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// One global_load_lds_dwordx4: 16 bytes from sbase + voff (sbase wave-uniform,
-// voff per lane) into LDS at lds + 16 * lane (lds wave-uniform). Written as asm
-// so that the compiler does not serialise it against the LDS reads of the other
-// stage (it cannot tell the buffers apart); completion is tracked by wait_vmcnt.
-// It has no register outputs.
-__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-    // the bases are wave-uniform; readfirstlane pins them to SGPRs for the asm operands
-    // (readfirstlane returns int: widen each half as uint32_t, never sign-extended)
-    const uint64_t b = (uint64_t)(uintptr_t)sbase;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-    const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);   // uniform too
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(ls), "v"(voff), "s"(sb)
-                 : "m0");
-}
-
-// The same with 4 bytes per lane (global_load_lds_dword): LDS at lds + 4 * lane.
-// Needs only dword alignment of the source.
-__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t lds) {
-    const uint64_t b = (uint64_t)(uintptr_t)sbase;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-    const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
-                 :
-                 : "s"(ls), "v"(voff), "s"(sb)
-                 : "m0");
 }
 
 // Transposed LDS reads (ds_read_b64_tr_b16) of 16-bit elements, as bf16 or fp16.

@@ -14,8 +14,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# HTA_LIBRARY selects another build of the same library (tuning variants).
-LIB_PATH = os.environ.get("HTA_LIBRARY") or os.path.join(_HERE, "libhta.so")
+LIB_PATH = os.path.join(_HERE, "libhta.so")
 
 HTA_OK = 0
 HTA_ERR_NULL = -1
@@ -66,7 +65,20 @@ class Params(ctypes.Structure):
     _fields_ = [("swa_window", ctypes.c_int), ("dswa_taps", ctypes.c_int),
                 ("dswa_dilation", ctypes.c_int), ("gla_chunk", ctypes.c_int),
                 ("attn_scale", ctypes.c_float), ("gla_scale", ctypes.c_float),
-                ("gla_form", ctypes.c_int)]
+                ("gla_form", ctypes.c_int), ("side_stream", ctypes.c_void_p),
+                ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p)]
+
+
+class SideStream:
+    """A second stream on the current device and the two events hta_params needs
+    to run work on it (held here so that they outlive the calls using them)."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+        self.fork.record()          # torch creates an event on its first record
+        self.join.record()
 
 
 class StreamCtx(ctypes.Structure):
@@ -188,10 +200,17 @@ def make_shape(q: torch.Tensor, v: torch.Tensor, P: int, o: torch.Tensor | None 
 
 
 def make_params(window=3, taps=4, dilation=4, chunk=64, attn_scale=0.0, gla_scale=0.0,
-                gla_form=0) -> Params:
-    """gla_form: HTA_GLA_GATED_DELTA (0) or HTA_GLA_PRINTED (1)."""
-    return Params(int(window), int(taps), int(dilation), int(chunk), float(attn_scale),
-                  float(gla_scale), int(gla_form))
+                gla_form=0, side: SideStream | None = None) -> Params:
+    """gla_form: HTA_GLA_GATED_DELTA (0) or HTA_GLA_PRINTED (1); side: an optional
+    SideStream for the hybrid calls to run their attention work on."""
+    p = Params(int(window), int(taps), int(dilation), int(chunk), float(attn_scale),
+               float(gla_scale), int(gla_form), None, None, None)
+    if side is not None:
+        p.side_stream = side.stream.cuda_stream
+        p.fork_event = side.fork.cuda_event
+        p.join_event = side.join.cuda_event
+        p._side = side      # the handles are valid while the SideStream lives
+    return p
 
 
 def hta_workspace_bytes(op: int, shape: Shape, params: Params | None) -> int:
@@ -373,6 +392,7 @@ class Stream:
         code = HTA_BF16 if dtype == torch.bfloat16 else (HTA_F32 if dtype == torch.float32 else 99)
         ocode = HTA_BF16 if out_dtype == torch.bfloat16 else (HTA_F32 if out_dtype == torch.float32 else 99)
         self.out_dtype = out_dtype
+        self.params = params        # holds the side stream's handles alive, if any
         self.ctx = StreamCtx(Shape(B, H, 1, P, d, d, code, ocode), params, int(R),
                              self.ring_k.data_ptr(), self.ring_v.data_ptr(),
                              self.state.data_ptr(), 0)

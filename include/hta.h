@@ -22,11 +22,9 @@
  *   - alpha, beta: fp32 [B][H][L], per-token forget gate alpha in (0, 1] and write
  *     strength beta in [0, 1] (the pages: beta = sigmoid(.), alpha in (0,1)).
  *   - GLA state: fp32 [B][H][dk][dv] holding S^T (S is dv x dk: v_old = S k).
- *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
- *     caller. The library allocates no device memory. Its only global state:
- *     one auxiliary HIP stream (non-blocking, default priority) and two events
- *     per device, created on the first bf16 hybrid or stream step and kept
- *     until the process exits; see hta_hybrid_fwd.
+ *   - Every pointer argument except `stream` (and the optional side stream and
+ *     events in hta_params) is a DEVICE pointer owned by the caller. The library
+ *     allocates no device memory and keeps no global state.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
  *     the null stream). Results are valid once the stream has synchronised.
  *   - All arguments are checked before anything is enqueued. On a non-zero
@@ -92,6 +90,18 @@ typedef struct {
     float attn_scale;     /* softmax scale; 0 selects 1/sqrt(dk)            */
     float gla_scale;      /* GLA output scale; 0 selects 1                  */
     int   gla_form;       /* HTA_GLA_GATED_DELTA (0) or HTA_GLA_PRINTED (1) */
+    /* Optional execution resources of the caller (all NULL: every launch goes on
+     * the call's `stream`). side_stream: a second hipStream_t on the same device
+     * on which the bf16 hybrid forward (and stream step, and training pair) runs
+     * its attention work beside the GLA work on `stream`; fork_event, join_event:
+     * two hipEvent_t the call records (on `stream`, resp. side_stream) and waits on,
+     * both required with a side stream (HTA_ERR_NULL otherwise). The call orders
+     * everything it enqueues on side_stream after the work already on `stream`,
+     * and later work on `stream` after all of it. A call's use of the events must
+     * not overlap another call's. The results are the same bits either way. */
+    void* side_stream;
+    void* fork_event;
+    void* join_event;
 } hta_params;
 
 /*
@@ -254,17 +264,12 @@ int hta_gla_bwd(const hta_shape* shape, const hta_params* params,
  * hta_hybrid_fwd -- the whole layer (three-branch figure): o = o_swa + o_dswa + o_gla
  * with shared q, k, v; the GLA branch in params->gla_form. state as in hta_gla_fwd. workspace: >=
  * hta_workspace_bytes(HTA_OP_HYBRID, shape, params).
- * bf16 inputs: the GLA chunk scan (into an fp32 partial in the workspace) runs
- * on `stream` beside the attention, which runs on the library's auxiliary stream
- * (forked from `stream` by an event) as one pass over both windows (as in
- * hta_swa_dswa_fwd_ex). Where the scan has already finished a head when the pass
- * completes a block of its rows, the pass adds the GLA partial and writes o
- * itself; the other rows go to o (HTA_F32) or a second fp32 workspace partial,
- * and after `stream` waits for the pass, one more kernel adds the GLA partial to
- * those rows. Either way o is the same fp32 sum rounded once, independent of the
- * timing. Everything the call enqueues is ordered
- * after the work already on `stream`, and later work on `stream` is ordered
- * after all of it. The fork/join is serialised across host threads.
+ * bf16 inputs: the GLA branch goes into an fp32 partial in the workspace; one
+ * attention pass runs both windows (as in hta_swa_dswa_fwd_ex). Without a side
+ * stream in params, the GLA branch runs first and the pass adds its partial in
+ * its epilogue. With one, the pass runs on the side stream beside the GLA chunk
+ * scan on `stream`, and after the join one elementwise kernel adds the partial.
+ * Either way o is (DSWA + SWA) + GLA in fp32, rounded once: the same bits.
  * fp32 inputs: GLA into o, then SWA + DSWA adding it, all on `stream`.
  */
 int hta_hybrid_fwd(const hta_shape* shape, const hta_params* params,
@@ -338,9 +343,9 @@ int hta_stream_init(hta_stream_ctx* ctx, const void* k_prefix, const void* v_pre
  * q, k, v: [B][H][P][d]; alpha, beta: [B][H][P]; o: [B][H][P][dv] or NULL
  * (commit only). workspace: >= hta_workspace_bytes(HTA_OP_STREAM_STEP,
  * &ctx->s with T = 1, &ctx->p). With bf16 inputs and o != NULL, steps 2 and 3
- * overlap as in hta_hybrid_fwd (GLA on the auxiliary stream). ctx->n_frames
- * is incremented after a successful enqueue. A context must not be used by
- * two threads at once.
+ * run as in hta_hybrid_fwd (beside each other when ctx->p carries a side
+ * stream). ctx->n_frames is incremented after a successful enqueue. A context
+ * must not be used by two threads at once.
  */
 int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, void* o,

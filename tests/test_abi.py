@@ -137,21 +137,21 @@ def test_workspace_bytes_rules():
     assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, s, prm) == 0     # T must be 1
     s1 = shape(T=1)
     assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, s1, prm) > 0
-    # bf16 inputs: the GLA branch runs beside the SWA pass with an fp32 partial of
-    # its own; a bf16 o also needs an fp32 buffer for the SWA pass.
-    # The one-pass attention parks each wave's own-frame softmax state: 68 floats
-    # per lane, 4 waves of 64 lanes per workgroup of 128 query rows.
+    # bf16 inputs: the GLA branch runs first into an fp32 partial of its own; a bf16
+    # o also needs an fp32 buffer for the SWA branch's output. The one-pass
+    # attention parks each wave's own-frame softmax state: 68 floats per lane,
+    # 4 waves of 64 lanes per workgroup of 128 query rows.
     so = shape(out=hta.HTA_F32)
     part = so.B * so.H * so.T * so.P * so.dv * 4
     part = (part + 255) // 256 * 256
     park = so.B * so.H * so.T * ((so.P + 127) // 128) * 4 * 64 * 68 * 4
     park = (park + 255) // 256 * 256
-    # the hybrid's hand-off: a scan counter per head, a pending flag per attention wave
+    # the GLA branch's operand blocks: 42496 bytes per 64-token chunk and head
     up = lambda n: (n + 255) // 256 * 256
-    sync = up(so.B * so.H * 4) + up(so.B * so.H * so.T * ((so.P + 127) // 128) * 4)
     gla = hta.hta_workspace_bytes(hta.HTA_OP_GLA, so, prm)
-    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, so, prm) == gla + part + park + sync
-    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape(), prm) == gla + 2 * part + park + sync
+    assert gla == up(so.B * so.H * ((so.T * so.P + 63) // 64) * 42496)
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, so, prm) == gla + part + park
+    assert hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, shape(), prm) == gla + 2 * part + park
     assert hta.hta_workspace_bytes(hta.HTA_OP_SWA_DSWA, so, None) == park + part
     # fp32 inputs run the branches in sequence with the GLA partial in o
     f32 = shape(dtype=hta.HTA_F32, d=64)

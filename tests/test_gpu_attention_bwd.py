@@ -42,11 +42,9 @@ def _case(base, kind, out_dtype, seed, **kw):
     print(f"[case] attn bwd {kind} {w.name} B{w.B} H{w.H} T{w.T} P{w.P} d{w.dk} "
           f"W{w.window} taps{w.taps} dil{w.dilation} out {out_dtype}", flush=True)
     x = make_inputs(w, device="cuda", frames=w.T)
-    dout = make_output_grad(w, device="cuda").to(out_dtype)
+    dout = make_output_grad(w.replace(dtype=out_dtype), device="cuda")   # fp32: unrounded
     o, lse, dq, dk, dv = _run(kind, x, dout, w, out_dtype)
-    q, k, v, do = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(dout)
-    if w.dtype == torch.bfloat16:
-        do = f64(dout.to(torch.bfloat16))   # the bf16 path multiplies the rounded gradient
+    q, k, v, do = f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(dout)   # the exact gradient
     if kind == "swa":
         ref = oracle.swa_bwd(q, k, v, do, w.T, w.P, w.window)
         lse_ref, _ = oracle.window_stats("swa", q, k, v, do, w.T, w.P, w.window, 0,

@@ -48,8 +48,10 @@ def _run(w, x, dout, s0, dsf, prm, out_dtype):
 
 
 def _inputs(w, out_dtype):
+    """dL/do in the output dtype: an fp32 one is drawn unrounded (the bf16 kernels
+    round it themselves; the oracle differentiates the exact values)."""
     x = make_inputs(w, device="cuda", frames=w.T)
-    dout = make_output_grad(w, device="cuda").to(out_dtype)
+    dout = make_output_grad(w.replace(dtype=out_dtype), device="cuda")
     g = torch.Generator(device="cuda")
     g.manual_seed(w.seed + 77)
     s0 = 0.3 * torch.randn(w.B, w.H, w.dk, w.dv, generator=g, device="cuda")
@@ -67,16 +69,21 @@ def _check(got, ref, dtype, what):
         assert_parity(got[name], ref[name], dtype, f"{what} {name}")
 
 
+@pytest.mark.parametrize("side", [False, True])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("form", [0, 1])
-def test_hybrid_bwd_bf16(out_dtype, form):
+def test_hybrid_bwd_bf16(out_dtype, form, side):
+    """side: the caller's side stream in params (the attention work beside the GLA
+    work), which must give the same results."""
     w = WORKLOADS["hybrid_stream"].replace(B=1, H=2, T=9, P=70, stream_frames=0, dilation=2,
                                            seed=41)
-    print(f"[case] hybrid bwd B{w.B} H{w.H} T{w.T} P{w.P} form{form} out {out_dtype}", flush=True)
+    print(f"[case] hybrid bwd B{w.B} H{w.H} T{w.T} P{w.P} form{form} out {out_dtype} side {side}",
+          flush=True)
     x, dout, s0, dsf = _inputs(w, out_dtype)
-    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, gla_form=form)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, gla_form=form,
+                          side=hta.SideStream() if side else None)
     got = _run(w, x, dout, s0, dsf, prm, out_dtype)
-    do = f64(dout.to(torch.bfloat16))
+    do = f64(dout)
     ref = oracle.hybrid_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["alpha"]),
                             f64(x["beta"]), do, w.T, w.P, w.window, w.taps, w.dilation,
                             f64(s0), f64(dsf), form=form)
@@ -107,7 +114,7 @@ def test_hybrid_bwd_full_size_sampled():
     prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
     got = _run(w, x, dout, s0, dsf, prm, torch.float32)
     q, k, v = x["q"].cpu(), x["k"].cpu(), x["v"].cpu()
-    do = f64(dout.to(torch.bfloat16))
+    do = f64(dout)
     L = w.L
     rng = np.random.default_rng(3)
     for b_, h_ in ((0, 3), (1, 14)):
