@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/hta.h"
 #include "hta_internal.h"
 
@@ -495,6 +497,9 @@ const char* hta_status_string(int status) {
         case HTA_ERR_HIP: return "HTA_ERR_HIP: a HIP runtime call failed";
         case HTA_ERR_ALIAS: return "HTA_ERR_ALIAS: an output overlaps an input";
         case HTA_ERR_ALIGN: return "HTA_ERR_ALIGN: a device pointer is not aligned as required";
+        case HTA_ERR_SCRATCH:
+            return "HTA_ERR_SCRATCH: the step needs more than the library's fixed scratch "
+                   "(HTA_NOALLOC_SCRATCH_BYTES); use hta_stream_step with a workspace";
         default: return "unknown hta status";
     }
 }
@@ -1126,6 +1131,23 @@ static hta::WinLaunch ring_launch(const hta_stream_ctx* ctx, const hta_shape& s,
     return w;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of one stream step (the frame's GLA blocks, then with o the fp32
+// partials of the sum); the context must have passed check_ctx.
+size_t stream_step_ws(const hta_stream_ctx* ctx, bool with_o, size_t* need_gla) {
+    hta_shape s = ctx->s;
+    s.T = 1;
+    *need_gla = gla_ws(&s, ctx->p.gla_chunk);
+    return *need_gla + (with_o ? partial_ws(&s) : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
 int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, void* o, void* workspace,
                     size_t workspace_bytes, void* stream) {
@@ -1134,8 +1156,8 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
     hta_shape s = ctx->s;
     s.T = 1;
     if (!q || !k || !v || !alpha || !beta) return HTA_ERR_NULL;
-    const size_t need_gla = gla_ws(&s, ctx->p.gla_chunk);
-    const size_t need = need_gla + (o ? partial_ws(&s) : 0);
+    size_t need_gla = 0;
+    const size_t need = stream_step_ws(ctx, o != nullptr, &need_gla);
     if (!workspace || workspace_bytes < need) return HTA_ERR_WORKSPACE;
     if ((st = check_align(15, q, k, v, o, workspace)) != HTA_OK ||
         (st = check_align(3, alpha, beta)) != HTA_OK)
@@ -1204,6 +1226,64 @@ int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const voi
     }
     ctx->n_frames = n + 1;
     return HTA_OK;
+}
+
+}  // extern "C"
+
+// Scratch of hta_stream_step_noalloc: a fixed array in the library's code
+// object, one copy per GPU (allocated when the code object loads on that GPU,
+// held until the process ends). In host code `scratch` only stands in for the
+// symbol; its device address on each GPU comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[HTA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each GPU (set once)
+
+// The scratch address on `dev`, which must be the current device. The first
+// call on a device looks the symbol up; the address never changes after.
+int scratch_on(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return HTA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return HTA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hta_stream_step_noalloc(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, void* o, void* stream) {
+    int st;
+    if ((st = check_ctx(ctx)) != HTA_OK) return st;
+    size_t need_gla = 0;
+    if (stream_step_ws(ctx, o != nullptr, &need_gla) > (size_t)HTA_NOALLOC_SCRATCH_BYTES)
+        return HTA_ERR_SCRATCH;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (stream) {   // the scratch used must be the copy on the stream's GPU
+        hipDevice_t sdev = 0;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) return hip_fail(e);
+        if (sdev != dev) return HTA_ERR_UNSUPPORTED;
+    }
+    void* ws = nullptr;
+    if ((st = scratch_on(dev, &ws)) != HTA_OK) return st;
+    // Every scratch byte this step reads it has written first in the same call,
+    // so nothing needs clearing between calls.
+    return hta_stream_step(ctx, q, k, v, alpha, beta, o, ws, (size_t)HTA_NOALLOC_SCRATCH_BYTES,
+                           stream);
 }
 
 }  // extern "C"

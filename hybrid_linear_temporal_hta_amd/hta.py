@@ -27,6 +27,8 @@ HTA_ERR_RING = -7
 HTA_ERR_HIP = -8
 HTA_ERR_ALIAS = -9
 HTA_ERR_ALIGN = -10
+HTA_ERR_SCRATCH = -11
+HTA_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 HTA_F32 = 0
 HTA_BF16 = 1
@@ -50,7 +52,7 @@ EXPORTED = (
     "hta_swa_bwd", "hta_dswa_bwd", "hta_swa_dswa_fwd", "hta_swa_dswa_fwd_ex", "hta_gla_fwd",
     "hta_gla_fwd_ex", "hta_gla_bwd", "hta_hybrid_fwd", "hta_hybrid_saved_bytes",
     "hta_hybrid_fwd_train", "hta_hybrid_bwd", "hta_project_fwd",
-    "hta_stream_init", "hta_stream_step", "hta_status_string", "hta_last_hip_error",
+    "hta_stream_init", "hta_stream_step", "hta_stream_step_noalloc", "hta_status_string", "hta_last_hip_error",
     "hta_version",
 )
 
@@ -148,6 +150,8 @@ def lib() -> ctypes.CDLL:
     L.hta_stream_init.argtypes = [ctypes.POINTER(StreamCtx), vp, vp, i, vp, vp]
     L.hta_stream_step.restype = i
     L.hta_stream_step.argtypes = [ctypes.POINTER(StreamCtx), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.hta_stream_step_noalloc.restype = i
+    L.hta_stream_step_noalloc.argtypes = [ctypes.POINTER(StreamCtx), vp, vp, vp, vp, vp, vp, vp]
     L.hta_status_string.restype = ctypes.c_char_p
     L.hta_status_string.argtypes = [i]
     L.hta_last_hip_error.restype = i
@@ -414,3 +418,10 @@ def hta_stream_step(st: Stream, q, k, v, alpha, beta, o=None, stream=None):
     _check(lib().hta_stream_step(ctypes.byref(st.ctx), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                  _ptr(beta), _ptr(o), _ptr(st.workspace), st.workspace.numel(),
                                  _stream(stream)), "hta_stream_step")
+
+
+def hta_stream_step_noalloc(st: Stream, q, k, v, alpha, beta, o=None, stream=None):
+    """hta_stream_step on the library's fixed per-GPU scratch (no workspace)."""
+    _check(lib().hta_stream_step_noalloc(ctypes.byref(st.ctx), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(alpha), _ptr(beta), _ptr(o), _stream(stream)),
+           "hta_stream_step_noalloc")

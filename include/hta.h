@@ -24,7 +24,8 @@
  *   - GLA state: fp32 [B][H][dk][dv] holding S^T (S is dv x dk: v_old = S k).
  *   - Every pointer argument except `stream` (and the optional side stream and
  *     events in hta_params) is a DEVICE pointer owned by the caller. The library
- *     allocates no device memory and keeps no global state.
+ *     allocates no device memory and keeps no global state, with one exception:
+ *     hta_stream_step_noalloc's fixed scratch array on each GPU and its address.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
  *     the null stream). Results are valid once the stream has synchronised.
  *   - All arguments are checked before anything is enqueued. On a non-zero
@@ -68,6 +69,7 @@ extern "C" {
 #define HTA_ERR_HIP         (-8)  /* a HIP call failed; see hta_last_hip_error()       */
 #define HTA_ERR_ALIAS       (-9)  /* an output overlaps an input                       */
 #define HTA_ERR_ALIGN      (-10)  /* a device pointer is not aligned as required        */
+#define HTA_ERR_SCRATCH    (-11)  /* needs more than HTA_NOALLOC_SCRATCH_BYTES          */
 
 typedef enum { HTA_F32 = 0, HTA_BF16 = 1 } hta_dtype;
 
@@ -350,6 +352,31 @@ int hta_stream_init(hta_stream_ctx* ctx, const void* k_prefix, const void* v_pre
 int hta_stream_step(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
                     const float* alpha, const float* beta, void* o,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hta_stream_step_noalloc -- hta_stream_step without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * results (the same kernels, bit for bit), context update and error behaviour
+ * as hta_stream_step, which it calls with the library's scratch instead of a
+ * caller workspace. The scratch is one fixed array of HTA_NOALLOC_SCRATCH_BYTES
+ * per GPU inside the library, allocated when the library's code loads on that
+ * GPU and held until the process ends; this call allocates and frees nothing.
+ *   - Returns HTA_ERR_SCRATCH (nothing enqueued) when the step needs more than
+ *     HTA_NOALLOC_SCRATCH_BYTES, i.e. when hta_workspace_bytes(HTA_OP_STREAM_STEP,
+ *     ...) (or its commit-only share) exceeds it. 128 MiB holds B*H = 32 heads
+ *     of P = 1560 tokens with bf16 inputs and either output dtype.
+ *   - `stream` must belong to the current device (HTA_ERR_UNSUPPORTED otherwise).
+ *   - Every call on a GPU uses that GPU's one array: calls whose work overlaps
+ *     on one GPU (other streams, other threads, other contexts) race and give
+ *     undefined results. Serialise them, e.g. on one stream. The array keeps the
+ *     last call's contents; the step writes each scratch byte before reading it.
+ *   - The first call on a device looks up the array's address there (a HIP
+ *     symbol query, no allocation); later calls reuse it.
+ */
+#define HTA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int hta_stream_step_noalloc(hta_stream_ctx* ctx, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, void* o, void* stream);
 
 /*
  * hta_project_fwd -- the input side of the GLA branch (GLA paragraph: q = W_Q x,

@@ -174,6 +174,28 @@ def test_stream_ring_too_small():
     assert ctx.n_frames == 0
 
 
+def test_stream_step_noalloc_rejects_oversized_steps():
+    """The no-allocation step refuses a step whose workspace exceeds the fixed
+    scratch (before any HIP call), and passes the context checks through."""
+    lib = hta.lib()
+    prm = hta.make_params(3, 4, 4, 64)
+    big = hta.Shape(4, 16, 1, 4096, 128, 128, hta.HTA_BF16, hta.HTA_BF16)
+    assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, big, prm) > hta.HTA_NOALLOC_SCRATCH_BYTES
+    ctx = hta.StreamCtx(big, prm, 13, F.value, G.value, S.value, 5)
+    assert lib.hta_stream_step_noalloc(ctypes.byref(ctx), F, G, Hh, A, Bt, O, None) == \
+        hta.HTA_ERR_SCRATCH
+    assert ctx.n_frames == 5
+    ctx.R = 12                                   # the ring check comes first
+    assert lib.hta_stream_step_noalloc(ctypes.byref(ctx), F, G, Hh, A, Bt, O, None) == \
+        hta.HTA_ERR_RING
+    assert "HTA_ERR_SCRATCH" in lib.hta_status_string(hta.HTA_ERR_SCRATCH).decode()
+    # the serving workload (B2 H16, 1560 tokens per frame) fits, with either output dtype
+    for out in (hta.HTA_F32, hta.HTA_BF16):
+        s = hta.Shape(2, 16, 1, 1560, 128, 128, hta.HTA_BF16, out)
+        assert hta.hta_workspace_bytes(hta.HTA_OP_STREAM_STEP, s, prm) <= \
+            hta.HTA_NOALLOC_SCRATCH_BYTES
+
+
 def test_gla_form_validation():
     """gla_form must be one of the two update forms; hta_gla_fwd_ex checks it
     before anything else touches the buffers."""
