@@ -2,15 +2,16 @@
 
 One step = one hta_hybrid_fwd call over one batch of the workload B=2, H=16,
 d=128, T=21 frames x P=1560 tokens (L=32760), bf16 q/k/v, fp32 accumulation
-and output, inputs resident in HBM. Inside the call the GLA chunk scan runs
-beside one attention pass over both windows (on the library's auxiliary
-stream); an elementwise pass then adds the GLA partial. The dominant kernel's
-roofline is timed on that attention pass run alone (hta_swa_dswa_fwd_ex); the
-GLA branch is timed alone as well. After the forward
-steps the 64-frame streaming continuation of the same workload is timed
-(reported under "stream"), then the training pair on the same batch (forward
-that saves activations + backward, under "train"), the 336-frame long-horizon
-workload and the input-side projection.
+and output, inputs resident in HBM. The call gets a side stream from the
+caller (hta_params): the GLA prep runs first, then the GLA chunk scan on the
+call's stream beside one attention pass over both windows on the side stream,
+then one elementwise pass adds the two partials. The dominant kernel's roofline
+is timed on that attention pass run alone (hta_swa_dswa_fwd_ex); the GLA branch
+is timed alone as well. Then: the 64-frame streaming continuation of the same
+workload ("stream"), the training pair on the same batch ("train"), the
+336-frame long-horizon workload, the 61-frame workloads at DSWA dilations 6 and
+12 ("dilated"), the attention pass at unscaled logits ("attn_unscaled"), the
+input-side projection, and the chip's measured MFMA and HBM ceilings ("peaks").
 
 Prints ONE JSON line. With --gpus above 1 it exits: this build runs on a single
 GPU (sharding is described in the design notes, not measured).
@@ -35,20 +36,35 @@ ATTN_KERNEL = "win_attn_bf16_kernel<3>"   # both windows in one pass (own frame 
 PMC_FILE = os.path.join(ROOT, "profiles", "win_attn_bf16_onepass_hybrid_fwd_B2H16L32760_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "hybrid_linear_temporal_hta_amd", "csrc", "win_attn.hip")
 ATTN_LAUNCHES = 1                   # one SWA+DSWA pass per step
+GLA_SRC = os.path.join(ROOT, "hybrid_linear_temporal_hta_amd", "csrc", "gla_fwd.hip")
+GLA_PREP_PMC = os.path.join(ROOT, "profiles", "gla_prep2_gla_fwd_B2H16L32760_traffic.json")
+GLA_SCAN_PMC = os.path.join(ROOT, "profiles", "gla_scan3_gla_fwd_B2H16L32760_traffic.json")
+
+
+def attn_pairs(w) -> int:
+    """Distinct (query frame, key frame) pairs of SWA and DSWA together: the key
+    frames of frame f are the union of the two windows, the own frame once."""
+    n = 0
+    for f in range(w.T):
+        keys = {f - j for j in range(w.window) if f - j >= 0}
+        keys |= {f - j * w.dilation for j in range(w.taps) if f - j * w.dilation >= 0}
+        n += len(keys)
+    return n
 
 
 def attn_flops(w) -> float:
-    """Algorithmic FLOPs of SWA + DSWA: 4 d P^2 per (query frame, tap frame) pair,
-    each branch counted in full (its own frame included)."""
+    """Algorithmic FLOPs of SWA + DSWA: 4 d P^2 (QK^T and PV) per distinct (query
+    frame, key frame) pair. A frame in both windows (the own frame; with W > dil
+    others too) has one set of logits and weights, so it is counted once."""
+    return 4.0 * w.dk * w.P * w.P * attn_pairs(w) * w.B * w.H
+
+
+def attn_flops_double_counted(w) -> float:
+    """SWA and DSWA each counted in full (a frame in both windows twice): what two
+    separate branch passes would execute."""
     n_swa = sum(min(w.window, f + 1) for f in range(w.T))
     n_dswa = sum(sum(1 for j in range(w.taps) if f - j * w.dilation >= 0) for f in range(w.T))
     return 4.0 * w.dk * w.P * w.P * (n_swa + n_dswa) * w.B * w.H
-
-
-def attn_flops_executed(w) -> float:
-    """MFMA work the one-pass kernel executes: the query's own frame, common to
-    both windows, is attended once."""
-    return attn_flops(w) - 4.0 * w.dk * w.P * w.P * w.T * w.B * w.H
 
 
 def gla_flops(w) -> float:
@@ -57,45 +73,77 @@ def gla_flops(w) -> float:
     return (5 * C * d + 6 * d * d + C * C / 3.0) * w.B * w.H * w.L
 
 
+def cpu_info():
+    """Host CPU model and logical CPU count (what the CPU baseline ran on)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
 def gla_bytes(w, out_bytes=4) -> float:
     """Algorithmic HBM bytes of the GLA branch: q, k, v (bf16), alpha, beta, o."""
     return (3 * w.dk * 2 + 8 + w.dv * out_bytes) * w.B * w.H * w.L
 
 
-def pmc_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs
+def pmc_traffic(path: str, src: str):
+    """HBM bytes per launch of one kernel from committed rocprofv3 counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), valid only
-    while the kernel source is the one they were taken on."""
+    while the kernel source is the one they were taken on (else None)."""
     try:
         from hybrid_linear_temporal_hta_amd.profiling import source_digest
-        rec = json.load(open(PMC_FILE))
-        if rec.get("source_digest") != source_digest(ATTN_SRC):
+        rec = json.load(open(path))
+        if rec.get("source_digest") != source_digest(src):
             return None
         return float(rec["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
         return None
 
 
+COPY_BYTES = 1 << 30        # the calibration and measured-peak copy: 1 GiB read, 1 GiB written
+
+
 def copy_calibration(steps: int):
-    """A plain copy of known size for counter calibration: hta_stream_init
-    filling a 13-frame ring from 13 frames of K and of V (B2 H16 P1560 d128
-    bf16), one copy_frames_kernel launch per frame and tensor, each reading and
-    writing B*H*P*d*2 bytes."""
+    """A plain copy of known size for counter calibration: hbm_copy_kernel
+    (libhta_peaks) copying COPY_BYTES, `steps` launches."""
     import torch
-    from hybrid_linear_temporal_hta_amd import hta
-    from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS
-    w = WORKLOADS["hybrid_stream"]
+    from hybrid_linear_temporal_hta_amd import peaks
     dev = torch.device("cuda:0")
-    k = torch.randn(w.B, w.H, w.ring * w.P, w.dk, device=dev).to(w.dtype)
-    v = torch.randn(w.B, w.H, w.ring * w.P, w.dv, device=dev).to(w.dtype)
-    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
-    st = hta.Stream(w.B, w.H, w.P, w.dk, w.dtype, prm, w.ring, device=dev)
+    src = torch.ones(COPY_BYTES // 4, device=dev)
+    dst = torch.empty_like(src)
     for _ in range(steps):
-        hta.hta_stream_init(st, k, v, w.ring, None)
+        peaks.copy(src, dst)
     torch.cuda.synchronize()
-    nbytes = w.B * w.H * w.P * w.dk * 2
-    print(json.dumps({"copy_kernel": "copy_frames_kernel", "launches": 2 * w.ring * steps,
-                      "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes}))
+    print(json.dumps({"copy_kernel": "hbm_copy_kernel", "launches": steps,
+                      "bytes_read_per_launch": COPY_BYTES, "bytes_written_per_launch": COPY_BYTES}))
+
+
+def measured_peaks(dev, stream):
+    """The chip's ceilings as plain kernels reach them (libhta_peaks): an MFMA
+    issue loop (bf16 32x32x16, register operands, 4 workgroups of 4 waves per
+    CU) and a 1 GiB HBM copy, both timed with HIP events on `stream`."""
+    import torch
+    from hybrid_linear_temporal_hta_amd import peaks
+    blocks, iters = 1024, 8000
+    sink = torch.empty(blocks * 256, device=dev)
+    mfma_ms = timed_events(lambda: peaks.mfma(blocks, iters, sink, stream), 5, 2, stream)
+    fl = peaks.mfma_flop(blocks, iters)
+    src = torch.ones(COPY_BYTES // 4, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = timed_events(lambda: peaks.copy(src, dst, stream), 10, 2, stream)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_kernel": "mfma_loop_kernel (v_mfma_f32_32x32x16_bf16)",
+            "mfma_TFLOPs": round(fl / (mfma_ms / 1e3) / 1e12, 1),
+            "mfma_frac_of_spec": round(fl / (mfma_ms / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+            "copy_kernel": "hbm_copy_kernel", "copy_bytes_moved": 2 * COPY_BYTES,
+            "hbm_copy_GBps": round(2 * COPY_BYTES / (copy_ms / 1e3) / 1e9, 1),
+            "hbm_frac_of_spec": round(2 * COPY_BYTES / (copy_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
 def cpu_baseline(w, x, heads: int):
@@ -117,16 +165,17 @@ def cpu_baseline(w, x, heads: int):
     oracle.gla(q, k, v, a, b)
     dt = time.perf_counter() - t0
     tokens = w.L * heads / w.H
+    model, nproc = cpu_info()
     return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": f"{heads} of {w.H} heads of batch 0: SWA + DSWA for all {w.L} query rows "
                       f"and the GLA recurrence over all {w.L} tokens of each head "
                       f"(= {tokens:.0f} tokens of {w.H} heads), {dt:.1f} s wall"}
 
 
-def setup(hta, w, x, dev):
+def setup(hta, w, x, dev, side=None):
     import torch
-    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, side=side)
     state = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
     o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device=dev)
     nws = hta.hta_workspace_bytes(hta.HTA_OP_HYBRID, hta.make_shape(x["q"], x["v"], w.P, o), prm)
@@ -183,7 +232,7 @@ def long_horizon(hta, dev, steps):
     from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, make_inputs
     w = WORKLOADS["long_horizon"]
     x = make_inputs(w, device=dev)
-    prm, state, o, ws = setup(hta, w, x, dev)
+    prm, state, o, ws = setup(hta, w, x, dev, side=hta.SideStream(dev))
     stream = torch.cuda.current_stream()
     ms = timed_wall(hybrid_call(hta, w, x, state, o, ws, prm, stream), steps, 1)
     wsa = attn_ws(hta, w, x, o, prm, dev)
@@ -200,6 +249,65 @@ def long_horizon(hta, dev, steps):
            "attn_tflops": round(fl / (attn_ms / 1e3) / 1e12, 1),
            "attn_tap_frames_per_token": round(fl / (4.0 * w.dk * w.P * w.B * w.H * w.L), 3)}
     del x, o, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def dilated(hta, dev, steps):
+    """The 61-frame workloads at the pages' DSWA dilations 6 and 12 (B1 H16,
+    P=1560, L=95160, W=3, 4 taps): the hybrid forward (side stream) and the
+    attention pass alone, with its MFMA fraction."""
+    import torch
+    from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, make_inputs
+    out = []
+    stream = torch.cuda.current_stream()
+    for name in ("dilated_d6", "dilated_d12"):
+        w = WORKLOADS[name]
+        x = make_inputs(w, device=dev)
+        prm, state, o, ws = setup(hta, w, x, dev, side=hta.SideStream(dev))
+        ms = timed_wall(hybrid_call(hta, w, x, state, o, ws, prm, stream), steps, 1)
+        wsa = attn_ws(hta, w, x, o, prm, dev)
+        attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, w.P,
+                                                               prm, workspace=wsa, stream=stream),
+                               steps, 1, stream)
+        fl = attn_flops(w)
+        out.append({"workload": f"B{w.B} H{w.H} T{w.T} P{w.P} d{w.dk} (L={w.L}), W={w.window}, "
+                                f"{w.taps} taps dil {w.dilation}",
+                    "steps": steps, "ms_per_step": round(ms, 3),
+                    "tokens_per_s": round(w.B * w.L / (ms / 1e3), 1),
+                    "attn_ms": round(attn_ms, 3), "attn_flop": fl,
+                    "attn_frac_mfma": round(fl / (attn_ms / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+                    "hybrid_frac_mfma": round((fl + gla_flops(w)) / (ms / 1e3) / 1e12
+                                              / PEAK_MFMA_BF16_TFLOPS, 4)})
+        del x, o, ws, wsa
+        torch.cuda.empty_cache()
+    return out
+
+
+def attn_unscaled(hta, dev, steps):
+    """The attention pass of the metric workload with q, k ~ N(0, 1) (no data
+    scaling; logits of std 1 after the 1/sqrt(d) softmax scale), so the online
+    softmax's running maximum moves and its rescale runs; beside the same pass
+    on the metric's inputs (logits of std 1/sqrt(d))."""
+    import torch
+    from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["hybrid_stream"].replace(qv_std=1.0, k_std=1.0, k_unit=False,
+                                           stream_frames=0, seed=7)
+    x = make_inputs(w, device=dev)
+    stream = torch.cuda.current_stream()
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device=dev)
+    wsa = attn_ws(hta, w, x, o, prm, dev)
+    ms = timed_events(lambda: hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, w.P, prm,
+                                                      workspace=wsa, stream=stream),
+                      steps, 1, stream)
+    fl = attn_flops(w)
+    qk = (x["q"][0, 0, :4096].float() @ x["k"][0, 0, :4096].float().T) / w.dk ** 0.5
+    res = {"workload": "B2 H16 T21 P1560 d128, q, k, v ~ N(0, 1)", "avg_launch_ms": round(ms, 4),
+           "achieved_TFLOPs": round(fl / (ms / 1e3) / 1e12, 1),
+           "frac": round(fl / (ms / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+           "logit_std_sample": round(float(qk.std()), 3)}
+    del x, o, wsa
     torch.cuda.empty_cache()
     return res
 
@@ -273,7 +381,7 @@ def train(hta, w, x, dev, steps, warmup, cpu_heads):
     dswa_ms = timed_events(lambda: hta.hta_dswa_bwd(q, k, v, ob, lse, dout, dq, dk, dv, w.P,
                                                     w.taps, w.dilation, workspace=wsa,
                                                     stream=stream), steps, 1, stream)
-    fl_branch = attn_flops(w) / 2          # SWA and DSWA have equal tap-frame counts here
+    fl_branch = attn_flops_double_counted(w) / 2   # SWA and DSWA: equal tap-frame counts here
     fl_bwd = 2.5 * fl_branch
     att_ms = (swa_ms + dswa_ms) / 2
     achieved = fl_bwd / (att_ms / 1e3) / 1e12
@@ -309,8 +417,9 @@ def cpu_baseline_bwd(w, x, dout, heads: int, frames: int = 2):
     oracle.hybrid_bwd(q, k, v, a, b, do, frames, w.P, w.window, w.taps, w.dilation)
     dt = time.perf_counter() - t0
     tokens = n * heads / w.H
+    model, nproc = cpu_info()
     return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "nproc": nproc,
             "sample": f"hybrid backward of {heads} of {w.H} heads of batch 0 over the first "
                       f"{frames} frames ({n} tokens each; = {tokens:.0f} tokens of {w.H} heads), "
                       f"{dt:.1f} s wall"}
@@ -323,12 +432,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--stream-steps", type=int, default=64)
     ap.add_argument("--long-horizon-steps", type=int, default=2)
+    ap.add_argument("--dilated-steps", type=int, default=3)
+    ap.add_argument("--unscaled-steps", type=int, default=5)
     ap.add_argument("--project-steps", type=int, default=10)
     ap.add_argument("--train-steps", type=int, default=10)
+    ap.add_argument("--peaks", type=int, default=1, help="measure the MFMA and HBM ceilings (0: skip)")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU oracle baseline runs (0: skip it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="CALLS",
-                    help="only run CALLS ring fills (copy kernel of known size) and exit")
+                    help="only run CALLS copies of known size (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
@@ -349,17 +461,21 @@ def main():
     nP = w.T * w.P
     x = {k: (t[:, :, :nP].contiguous() if k in ("q", "k", "v", "alpha", "beta") else t)
          for k, t in full.items()}
-    prm, state, o, ws = setup(hta, w, x, dev)
+    side = hta.SideStream(dev)
+    prm, state, o, ws = setup(hta, w, x, dev, side=side)
     stream = torch.cuda.current_stream()
-    # The metric: the library's hybrid forward (GLA beside the SWA pass, then DSWA).
+    # The metric: the library's hybrid forward, the attention pass on the side stream.
     ms_per_step = timed_wall(hybrid_call(hta, w, x, state, o, ws, prm, stream), args.steps,
                              args.warmup)
     tokens = w.B * w.L
     value = tokens / (ms_per_step / 1e3)
+    # The same call with every launch on one stream (no side stream), for context.
+    prm1 = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    ms_single = timed_wall(hybrid_call(hta, w, x, state, o, ws, prm1, stream), args.steps, 1)
     # Roofline of the dominant kernel: the hybrid's attention pass (both windows in
     # one launch), alone on the stream, timed with HIP events on that stream.
-    wsa = attn_ws(hta, w, x, o, prm, dev)
-    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, w.P, prm,
+    wsa = attn_ws(hta, w, x, o, prm1, dev)
+    attn_ms = timed_events(lambda: hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, w.P, prm1,
                                                            workspace=wsa, stream=stream),
                            args.steps, 1, stream)
     # The GLA branch alone (prep + scan), for its own HBM fraction.
@@ -371,20 +487,23 @@ def main():
     launch_ms = attn_ms / ATTN_LAUNCHES
     fl_launch = fl / ATTN_LAUNCHES
     achieved = fl_launch / (launch_ms / 1e3) / 1e12
-    executed = attn_flops_executed(w) / ATTN_LAUNCHES / (launch_ms / 1e3) / 1e12
+    dbl = attn_flops_double_counted(w) / ATTN_LAUNCHES / (launch_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
-                "traffic": pmc_traffic(), "kernel": ATTN_KERNEL,
+                "traffic": pmc_traffic(PMC_FILE, ATTN_SRC), "kernel": ATTN_KERNEL,
                 "launches_per_step": ATTN_LAUNCHES, "flop_per_launch": fl_launch,
                 "avg_launch_ms": round(launch_ms, 4),
-                "executed_mfma_TFLOPs": round(executed, 2),
-                "executed_frac": round(executed / PEAK_MFMA_BF16_TFLOPS, 4)}
+                "double_counted_TFLOPs": round(dbl, 2),
+                "double_counted_frac": round(dbl / PEAK_MFMA_BF16_TFLOPS, 4)}
     gb = gla_bytes(w)
-    gla = {"kernels": "gla_prep_bf16_kernel + gla_scan_bf16_kernel", "avg_ms": round(gla_ms, 4),
+    gla = {"kernels": "gla_prep2_kernel + gla_scan3_kernel", "avg_ms": round(gla_ms, 4),
            "algorithmic_bytes": gb, "achieved_GBps": round(gb / (gla_ms / 1e3) / 1e9, 1),
            "frac_hbm": round(gb / (gla_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
            "flop": gla_flops(w),
-           "frac_mfma": round(gla_flops(w) / (gla_ms / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)}
+           "frac_mfma": round(gla_flops(w) / (gla_ms / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
+           "traffic_prep": pmc_traffic(GLA_PREP_PMC, GLA_SRC),
+           "traffic_scan": pmc_traffic(GLA_SCAN_PMC, GLA_SRC)}
+    hybrid_frac = (fl + gla_flops(w)) / (ms_per_step / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS
 
     # Streaming continuation: prefix = the 21 frames above, then one frame per step.
     sres = None
@@ -421,7 +540,13 @@ def main():
 
     tr = train(hta, w, x, dev, args.train_steps, 2, args.cpu_heads) if args.train_steps > 0 else None
     lh = long_horizon(hta, dev, args.long_horizon_steps) if args.long_horizon_steps > 0 else None
+    dl = dilated(hta, dev, args.dilated_steps) if args.dilated_steps > 0 else None
+    un = attn_unscaled(hta, dev, args.unscaled_steps) if args.unscaled_steps > 0 else None
     proj = projection(hta, dev, args.project_steps) if args.project_steps > 0 else None
+    pk = measured_peaks(dev, stream) if args.peaks else None
+    if pk:
+        roofline["frac_of_measured_mfma"] = round(achieved / pk["mfma_TFLOPs"], 4)
+        gla["frac_of_measured_hbm"] = round(gb / (gla_ms / 1e3) / 1e9 / pk["hbm_copy_GBps"], 4)
     cpu = cpu_baseline(w, x, args.cpu_heads) if args.cpu_heads > 0 else None
 
     out = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -432,8 +557,10 @@ def main():
                                   "SWA W=3, DSWA 4 taps dil 4, GLA chunk 64",
                       "global_batch": w.B, "seq_len": w.L, "heads": w.H, "head_dim": w.dk,
                       "parallelism": "single GPU"},
-           "roofline": roofline, "gla": gla, "stream": sres, "long_horizon": lh, "project": proj,
-           "train": tr, "cpu_baseline": cpu}
+           "roofline": roofline, "hybrid_frac_mfma": round(hybrid_frac, 4),
+           "hybrid_flop": fl + gla_flops(w), "ms_per_step_single_stream": round(ms_single, 4),
+           "gla": gla, "stream": sres, "long_horizon": lh, "dilated": dl, "attn_unscaled": un,
+           "project": proj, "train": tr, "peaks": pk, "cpu_baseline": cpu}
     print(json.dumps(out))
 
 

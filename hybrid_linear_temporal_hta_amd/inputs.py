@@ -11,10 +11,13 @@ Workloads (frame-major token order, token t in frame t // P):
   gla_bf16       B1 H16 d128 T21  P1560 bf16, q,k unit-norm, v ~ N(0,1), chunk 64
   hybrid_stream  B2 H16 d128 T21  P1560 bf16 (+64 streamed frames, ring of 13)
   long_horizon   B1 H16 d128 T336 P1560 bf16
+  dilated_d6     B1 H16 d128 T61  P1560 bf16, W=3, 4 taps dil 6 (the pages' dilation 6)
+  dilated_d12    B1 H16 d128 T61  P1560 bf16, W=3, 4 taps dil 12 (the pages' dilation 12)
 Gates: alpha = sigmoid(N(mu_a, 1)), beta = sigmoid(N(0, 1)), per token and head.
 The 21 x 1560 shape stands for 81-frame clips after 4x temporal and a 30x52
 patch grid after 16x spatial compression; the long horizon for multi-minute
-rollouts. No dataset is read: these synthetic draws stand in for video latents.
+rollouts. At 61 frames, the queries of frames 36 to 60 reach all four taps of
+dilation 12 ((4 - 1) * 12 + 1 = 37 frames). No dataset is read: these synthetic draws stand in for video latents.
 """
 from __future__ import annotations
 
@@ -74,6 +77,12 @@ WORKLOADS = {
     "long_horizon": Workload("long_horizon", 1, 16, 336, 1560, 128, 128, torch.bfloat16,
                              window=3, taps=4, dilation=4, chunk=64,
                              qv_std=_INV_SQRT128, k_unit=True, alpha_mu=4.0, seed=4),
+    "dilated_d6": Workload("dilated_d6", 1, 16, 61, 1560, 128, 128, torch.bfloat16,
+                           window=3, taps=4, dilation=6, chunk=64,
+                           qv_std=_INV_SQRT128, k_unit=True, alpha_mu=4.0, seed=5),
+    "dilated_d12": Workload("dilated_d12", 1, 16, 61, 1560, 128, 128, torch.bfloat16,
+                            window=3, taps=4, dilation=12, chunk=64,
+                            qv_std=_INV_SQRT128, k_unit=True, alpha_mu=4.0, seed=6),
 }
 
 

@@ -1,0 +1,60 @@
+"""ctypes binding of libhta_peaks.so (include/hta_peaks.h): the MFMA issue loop
+and the HBM copy whose rates the benchmark reports beside the published peaks.
+Argument marshalling only; the library must be built (it raises otherwise)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhta_peaks.so")
+EXPORTED = ("hta_peak_mfma", "hta_peak_mfma_chains", "hta_peak_copy")
+MFMA_FLOP = 2 * 32 * 32 * 16          # one v_mfma_f32_32x32x16_bf16 per wave
+WAVES_PER_BLOCK = 4
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m "
+                               "hybrid_linear_temporal_hta_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i = ctypes.c_void_p, ctypes.c_int
+        L.hta_peak_mfma.restype = i
+        L.hta_peak_mfma.argtypes = [i, i, vp, vp]
+        L.hta_peak_mfma_chains.restype = i
+        L.hta_peak_mfma_chains.argtypes = []
+        L.hta_peak_copy.restype = i
+        L.hta_peak_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        _lib = L
+    return _lib
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def mfma_flop(blocks: int, iters: int) -> float:
+    return float(blocks) * WAVES_PER_BLOCK * iters * lib().hta_peak_mfma_chains() * MFMA_FLOP
+
+
+def mfma(blocks: int, iters: int, sink, stream=None) -> None:
+    st = lib().hta_peak_mfma(int(blocks), int(iters), ctypes.c_void_p(sink.data_ptr()),
+                             _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"hta_peak_mfma: status {st}")
+
+
+def copy(src, dst, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    st = lib().hta_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n,
+                             _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"hta_peak_copy: status {st}")

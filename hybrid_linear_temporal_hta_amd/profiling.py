@@ -7,7 +7,7 @@ Two subcommands, both reading what ``rocprofv3 --output-format csv`` writes:
   traffic  HBM bytes per dispatch of one kernel from two ``--pmc`` runs
            (``FETCH_SIZE``, then ``WRITE_SIZE``; KiB per dispatch), each scaled
            by the same counter's reading on a plain copy kernel whose bytes are
-           known (``copy_frames_kernel`` under ``bench.py --copy-calibration``).
+           known (``hbm_copy_kernel`` under ``bench.py --copy-calibration``).
            The result is JSON keyed to a digest of the kernel's source file
            (comments excluded), so a reader can tell when the kernel changed
            after the counters were taken.
@@ -29,7 +29,7 @@ import os
 import re
 import sys
 
-COPY_KERNEL = "copy_frames_kernel"
+COPY_KERNEL = "hbm_copy_kernel"
 
 
 def source_digest(path: str) -> str:

@@ -42,6 +42,32 @@ def test_header_declarations_are_exported():
     assert set(names) <= exported, set(names) - exported
 
 
+def test_peaks_header_declarations_are_exported():
+    from hybrid_linear_temporal_hta_amd import peaks
+    text = open(os.path.join(ROOT, "include", "hta_peaks.h")).read()
+    names = sorted(set(re.findall(r"^\s*[a-z_]+\*?\s+\**(hta_[a-z0-9_]+)\s*\(", text, flags=re.M)))
+    assert set(names) == set(peaks.EXPORTED), names
+    out = subprocess.run(["nm", "-D", "--defined-only", peaks.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (hta_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_peaks_argument_errors():
+    """The microbenchmarks check their arguments before launching (fake pointers)."""
+    from hybrid_linear_temporal_hta_amd import peaks
+    L = peaks.lib()
+    assert L.hta_peak_mfma_chains() == 4
+    assert L.hta_peak_mfma(1, 1, None, None) == -1
+    assert L.hta_peak_mfma(0, 1, F, None) == -2
+    assert L.hta_peak_mfma(1, 0, F, None) == -2
+    assert L.hta_peak_copy(None, G, 16384, None) == -1
+    assert L.hta_peak_copy(F, G, 0, None) == -2
+    assert L.hta_peak_copy(F, G, 16384 + 64, None) == -2
+    assert L.hta_peak_copy(ctypes.c_void_p(F.value + 8), G, 16384, None) == -10
+    assert L.hta_peak_copy(F, ctypes.c_void_p(F.value + 16384), 32768, None) == -9
+
+
 def test_version_and_status_strings():
     lib = hta.lib()
     assert b"gfx950" in lib.hta_version()
