@@ -358,6 +358,9 @@ hipError_t run_hybrid(hta::GlaLaunch g, const hta::WinLaunch& w, const Partials&
     f.o = att;
     f.out_f32 = 1;
     f.add = nullptr;
+    // prep first (it needs the whole chip briefly), then the scan on a few CUs
+    // beside the attention pass (started at once, the attention holds every
+    // CU's LDS and the scan's workgroups could not be placed until it drained)
     if ((e = hta::launch_gla_fwd(g, sm, hta::kGlaPrep)) != hipSuccess) return e;
     if ((e = fork(d, sm)) != hipSuccess) return e;
     if ((e = hta::launch_gla_fwd(g, sm, hta::kGlaScanNarrow)) != hipSuccess) return e;

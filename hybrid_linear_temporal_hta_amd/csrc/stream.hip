@@ -31,31 +31,37 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* __restrict__ dst,
 
 // dst = a + b over n4 groups of 4 floats; each thread takes 4 groups 256 apart
 // per pass, all loads issued before the stores (more bytes in flight per lane).
+// dst = a + b over n4 float4 elements (dst may be a). Grid-stride rounds of 1024
+// elements per block, eight loads in flight per thread; streaming (nontemporal)
+// accesses, since nothing reads these arrays again soon.
 __global__ __launch_bounds__(256) void add_f32_kernel(void* __restrict__ dst, int dst_bf16,
                                                       const float* a, const float* b, long long n4) {
     const long long step = (long long)gridDim.x * 1024;
+    const f32x4* av = reinterpret_cast<const f32x4*>(a);
+    const f32x4* bv = reinterpret_cast<const f32x4*>(b);
     for (long long base = (long long)blockIdx.x * 1024 + threadIdx.x; base < n4; base += step) {
-        f32x4 r[4];
+        f32x4 x[4], y[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const long long i = base + 256 * u;
             if (i < n4) {
-                const f32x4 x = reinterpret_cast<const f32x4*>(a)[i];
-                const f32x4 y = reinterpret_cast<const f32x4*>(b)[i];
-                r[u] = f32x4{x[0] + y[0], x[1] + y[1], x[2] + y[2], x[3] + y[3]};
+                x[u] = __builtin_nontemporal_load(av + i);
+                y[u] = __builtin_nontemporal_load(bv + i);
             }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const long long i = base + 256 * u;
             if (i >= n4) break;
+            const f32x4 r = f32x4{x[u][0] + y[u][0], x[u][1] + y[u][1], x[u][2] + y[u][2],
+                                  x[u][3] + y[u][3]};
             if (dst_bf16) {
                 bf16x4 o;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) o[j] = f2bf(r[u][j]);
-                reinterpret_cast<bf16x4*>(dst)[i] = o;
+                for (int k = 0; k < 4; ++k) o[k] = f2bf(r[k]);
+                __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(dst) + i);
             } else {
-                reinterpret_cast<f32x4*>(dst)[i] = r[u];
+                __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(dst) + i);
             }
         }
     }
@@ -91,7 +97,7 @@ hipError_t launch_add_f32(void* dst, int dst_bf16, const float* a, const float* 
     if (n == 0) return hipSuccess;
     if (n & 3) return hipErrorInvalidValue;
     long long g = (n / 4 + 1023) / 1024;
-    if (g > 16384) g = 16384;
+    if (g > 4096) g = 4096;   // 16 workgroups per CU, then grid-stride
     hipLaunchKernelGGL(add_f32_kernel, dim3((unsigned)(g < 1 ? 1 : g)), dim3(256), 0, stream, dst,
                        dst_bf16, a, b, n / 4);
     return hipGetLastError();
