@@ -612,7 +612,11 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
     __shared__ __attribute__((aligned(16))) f16 Ur[kC * kLd];     // U   [64][128]
     __shared__ __attribute__((aligned(16))) f16 Mb[kD * kLd];     // M0, then dM_C; then 3 [64][64]
     __shared__ float gs[kC], gps[kC], Es[kC], Dn[kC], bs[kC], Eps[kC], als[kC];
-    __shared__ float dg[kC], dgp[kC], dbt[kC];
+    // per-wave partial row sums of dL/dg, dL/dgp and dL/dbeta: each wave adds
+    // only to its own slice (one lane per row per instruction), and the slices
+    // are summed in wave order at the end, so the result does not depend on
+    // timing (no float atomics)
+    __shared__ float pdg[kGradThreads / 64][kC], pdgp[kGradThreads / 64][kC], pdbt[kGradThreads / 64][kC];
     __shared__ float red[kGradThreads / 64];
 
     const long long nch = (b.L + kC - 1) / kC;
@@ -685,10 +689,10 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
         Eps[lane] = __expf(gp);
         bs[lane] = lane < n ? b.beta[tok0 + lane] : 0.f;
         als[lane] = a;
-        dg[lane] = 0.f;
-        dgp[lane] = 0.f;
-        dbt[lane] = 0.f;
     }
+    pdg[wave][lane] = 0.f;
+    pdgp[wave][lane] = 0.f;
+    pdbt[wave][lane] = 0.f;
     // (the chunk's global operands were all requested at the top: see phase 0)
 #pragma unroll
     for (int it = 0; it < 2; ++it) {   // 16-byte pieces of 64 rows x 128
@@ -729,7 +733,7 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
         float t = 0.f;
 #pragma unroll
         for (int i = 0; i < kGradThreads / 64; ++i) t += red[i];
-        atomicAdd(&dg[kC - 1], Es[kC - 1] * t);
+        pdg[0][kC - 1] += Es[kC - 1] * t;
     }
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -750,7 +754,7 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
             accQ[mt][i] = Es[row] * X[mt][i];
             float s = (float)QT[col * kLc + row] * X[mt][i];
             s = group16_sum(s);
-            if (m == 0) atomicAdd(&dg[row], Es[row] * s);
+            if (m == 0) pdg[wave][row] += Es[row] * s;
         }
     // ---- phase 2: dR M0^T -> dK (-diag(beta Ep)); dgp, dbeta
 #pragma unroll
@@ -766,8 +770,8 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
             float s = (float)Kr[row * kLd + col] * X[mt][i];
             s = group16_sum(s);
             if (m == 0) {
-                atomicAdd(&dgp[row], -bs[row] * Eps[row] * s);
-                atomicAdd(&dbt[row], -Eps[row] * s);
+                pdgp[wave][row] += -bs[row] * Eps[row] * s;
+                pdbt[wave][row] += -Eps[row] * s;
             }
         }
     __syncthreads();   // every wave is done with M0
@@ -792,11 +796,13 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
             float s = (float)Kr[row * kLd + col] * X[mt][i];
             s = group16_sum(s) * Dn[row];
             if (m == 0) {
-                atomicAdd(&dg[row], -s);
+                pdg[wave][row] -= s;
                 slast += s;
             }
         }
-    if (m == 0) atomicAdd(&dg[kC - 1], slast);
+    slast += __shfl_xor(slast, 16, 64);   // the four m == 0 lanes, summed in one lane
+    slast += __shfl_xor(slast, 32, 64);
+    if (lane == 0) pdg[wave][kC - 1] += slast;
     __syncthreads();   // Mb free: three 64 x 64 buffers
     f16* D1 = Mb;
     f16* D1T = Mb + kC * kLc;
@@ -816,7 +822,7 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
                 const float pm = (float)pmv[4 * h + i];
                 const float y = x * pm;
                 const float rs = group16_sum(y);
-                if (m == 0) atomicAdd(&dg[row], rs);
+                if (m == 0) pdg[wave][row] += rs;
                 colsum += y;
                 const float d1 = j <= row ? x * __expf(gs[row] - gs[j]) : 0.f;
                 D1[row * kLc + j] = (f16)d1;
@@ -824,7 +830,7 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
             }
         colsum += __shfl_xor(colsum, 16, 64);
         colsum += __shfl_xor(colsum, 32, 64);
-        if (G == 0) atomicAdd(&dg[j], -colsum);
+        if (G == 0) pdg[wave][j] -= colsum;
     }
     // ---- phase 5: dA = -strictly-lower(dR U^T), K K^T -> dbeta, dgp, dg, Bs
     {
@@ -848,14 +854,14 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
                     bm = bs[row] * z;
                 }
                 const float r1 = group16_sum(zk), r2 = group16_sum(da_a);
-                if (m == 0) { atomicAdd(&dbt[row], r1); atomicAdd(&dgp[row], r2); }
+                if (m == 0) { pdbt[wave][row] += r1; pdgp[wave][row] += r2; }
                 colsum += da_a;
                 if (j < row) { Bs[row * kLc + j] = (f16)bm; Bs[j * kLc + row] = (f16)bm; }
                 else if (j == row) Bs[row * kLc + j] = (f16)0.f;
             }
         colsum += __shfl_xor(colsum, 16, 64);
         colsum += __shfl_xor(colsum, 32, 64);
-        if (G == 0) atomicAdd(&dg[j], -colsum);
+        if (G == 0) pdg[wave][j] -= colsum;
     }
     __syncthreads();
     // ---- phase 6: dQ += D1 K, dK += D1^T Q + Bs K
@@ -909,13 +915,18 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
             }
         }
         s = group16_sum(s);
-        if ((e & 15) == 0 && row < n) atomicAdd(&dbt[row], s);
+        if ((e & 15) == 0 && row < n) pdbt[wave][row] += s;
     }
     __syncthreads();
     if (wave == 0) {
         // dlog(alpha)_r = sum_{i >= r} dg_i + sum_{i >= r} dgp_i (form 0) or sum_{i > r} dgp_i
-        const float x = dg[lane];
-        const float y = dgp[lane];
+        float x = 0.f, y = 0.f, zb = 0.f;
+#pragma unroll
+        for (int v8 = 0; v8 < kGradThreads / 64; ++v8) {
+            x += pdg[v8][lane];
+            y += pdgp[v8][lane];
+            zb += pdbt[v8][lane];
+        }
         float sx = x, sy = y;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -925,7 +936,7 @@ __global__ __launch_bounds__(kGradThreads) void gla_grad_kernel(GlaBwdLaunch b, 
         const float dla = sx + (b.form ? sy - y : sy);
         if (lane < n) {
             b.dalpha[tok0 + lane] = dla / als[lane] * invv;
-            b.dbeta[tok0 + lane] = dbt[lane] * invv;
+            b.dbeta[tok0 + lane] = zb * invv;
         }
     }
 }

@@ -122,7 +122,9 @@ __device__ __forceinline__ f32x4 mm16f(const float* X, int xld, const float* Y, 
 
 // Power of two sigma with max * sigma in [1, 2) (1 when the max is 0).
 __device__ __forceinline__ float sigma_of(unsigned bits) {
-    if (bits == 0u) return 1.f;
+    // zero, or an inf / NaN maximum (a non-finite input): no scaling, so finite
+    // operands keep their values and the non-finite one propagates
+    if (bits == 0u || bits >= 0x7f800000u) return 1.f;
     const int e = (int)((bits >> 23) & 0xffu) - 127;
     return ldexpf(1.f, -max(-126, min(e, 126)));
 }

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void win_bwd_prep_kernel(BwdPrep p) {
 // below 2 d while typical values stay in fp16's normal range (1 when m = 0).
 __device__ __forceinline__ float ds_sigma(const unsigned* gmax) {
     const float m = __uint_as_float(gmax[0]) * __uint_as_float(gmax[1]);
-    if (!(m > 0.f)) return 1.f;
+    if (!(m > 0.f) || !(m < __builtin_huge_valf())) return 1.f;   // zero, inf or NaN: no scaling
     const int e = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
     return ldexpf(1.f, -max(-100, min(e, 100)));
 }

@@ -14,7 +14,7 @@ import torch
 import oracle
 from helpers import TOL, assert_parity, assert_parity_rounded, f64
 from hybrid_linear_temporal_hta_amd import hta
-from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, make_inputs, make_output_grad
+from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, Workload, make_inputs, make_output_grad
 
 pytestmark = pytest.mark.gpu
 
@@ -72,3 +72,30 @@ def test_gla_bwd_bf16_long(form):
     GLA workload (alpha = sigmoid(N(4, 1)))."""
     w = WORKLOADS["gla_bf16"].replace(B=2, H=4, T=13, P=151, seed=9)   # L = 1963
     _case(w, form, torch.float32)
+
+
+@pytest.mark.parametrize("form", [0, 1])
+def test_gla_bwd_deterministic(form):
+    """hta_gla_bwd is bitwise reproducible (per-wave partial row sums in a fixed
+    order; no float atomics)."""
+    w = Workload("det", 1, 2, 3, 150, 128, 128, torch.bfloat16, chunk=64, k_unit=True,
+                 alpha_mu=3.0, seed=48)
+    print(f"[case] gla bwd determinism form {form}", flush=True)
+    x = make_inputs(w, device="cuda", frames=w.T)
+    q, k, v, a, b = x["q"], x["k"], x["v"], x["alpha"], x["beta"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    s0 = 0.5 * torch.randn(w.B, w.H, 128, 128, generator=g, device="cuda")
+    dsf = torch.randn(w.B, w.H, 128, 128, generator=g, device="cuda")
+    dout = make_output_grad(w.replace(dtype=torch.float32), device="cuda")
+    prm = hta.make_params(chunk=64, gla_form=form)
+    runs = []
+    for _ in range(3):
+        gr = [torch.empty_like(t) for t in (q, k, v, a, b)]
+        dst = dsf.clone()
+        hta.hta_gla_bwd(q, k, v, a, b, s0, dout, dst, *gr, w.P, prm)
+        runs.append(gr + [dst])
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for name, x0, x1 in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dstate0"), runs[0], r):
+            assert torch.equal(x0, x1), f"{name} differs between identical calls"

@@ -136,3 +136,31 @@ def test_hybrid_bwd_full_size_sampled():
             ref = att + g[name][0, 0, pos]
             assert_parity_rounded(got[name][b_, h_, torch.from_numpy(pos).cuda()], ref,
                                   TOL[w.dtype], f"full-size {name} sampled rows (b,h)=({b_},{h_})")
+
+
+@pytest.mark.parametrize("side", [False, True])
+def test_hybrid_bwd_deterministic(side):
+    """The training pair is bitwise reproducible: two backward calls on the same
+    saved activations give identical gradients (no order-dependent reductions:
+    the GLA gradient's row sums are per-wave partials summed in a fixed order)."""
+    w = WORKLOADS["hybrid_stream"].replace(B=1, H=2, T=7, P=130, stream_frames=0, seed=46)
+    print(f"[case] hybrid bwd determinism B{w.B} H{w.H} T{w.T} P{w.P} side {side}", flush=True)
+    x, dout, s0, dsf = _inputs(w, torch.float32)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk,
+                          side=hta.SideStream() if side else None)
+    q, k, v, a, b = x["q"], x["k"], x["v"], x["alpha"], x["beta"]
+    o = torch.empty(w.B, w.H, w.L, w.dv, device="cuda")
+    st = s0.clone()
+    shape = hta.make_shape(q, v, w.P, o)
+    saved = torch.empty(hta.hta_hybrid_saved_bytes(shape), dtype=torch.uint8, device="cuda")
+    hta.hta_hybrid_fwd_train(q, k, v, a, b, st, o, saved, w.P, prm)
+    runs = []
+    for _ in range(3):
+        g = [torch.empty_like(t) for t in (q, k, v, a, b)]
+        dst = dsf.clone()
+        hta.hta_hybrid_bwd(q, k, v, a, b, saved, dout, dst, *g, w.P, prm)
+        runs.append(g + [dst])
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for name, x0, x1 in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dstate0"), runs[0], r):
+            assert torch.equal(x0, x1), f"{name} differs between identical calls"

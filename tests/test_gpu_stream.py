@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import TOL, assert_parity, f64
+from helpers import TOL, assert_parity, assert_parity_rounded, f64
 from hybrid_linear_temporal_hta_amd import hta
 from hybrid_linear_temporal_hta_amd.inputs import WORKLOADS, Workload, make_inputs
 
@@ -37,14 +37,18 @@ def _start_stream(w, full, T0, prm, out_dtype=torch.float32):
     return s, o
 
 
-def _run_and_check(w, T0, N, check_steps=None, rows=None, form=0):
-    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, gla_form=form)
+def _run_and_check(w, T0, N, check_steps=None, rows=None, form=0, out_dtype=torch.float32,
+                   side=False):
+    """out_dtype: the steps' output dtype (bf16: the fp32 sum rounded once);
+    side: a caller side stream in the context's params."""
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, gla_form=form,
+                          side=hta.SideStream() if side else None)
     full = make_inputs(w, device="cuda", frames=T0 + N)
-    s, _ = _start_stream(w, full, T0, prm)
+    s, _ = _start_stream(w, full, T0, prm, out_dtype)
     outs = {}
     for n in range(N):
         f = _frames(full, w.P, T0 + n)
-        o = torch.empty(w.B, w.H, w.P, w.dv, dtype=torch.float32, device="cuda")
+        o = torch.empty(w.B, w.H, w.P, w.dv, dtype=out_dtype, device="cuda")
         hta.hta_stream_step(s, f["q"], f["k"], f["v"], f["alpha"], f["beta"], o)
         if check_steps is None or (n + 1) in check_steps:
             outs[n] = o
@@ -62,7 +66,11 @@ def _run_and_check(w, T0, N, check_steps=None, rows=None, form=0):
                                       q[:, :, fr * w.P:(fr + 1) * w.P], w.P, w.window, w.taps,
                                       w.dilation, rows=pos)
         ref = ref_att + ref_g[:, :, fr * w.P + pos]
-        assert_parity(f64(o)[:, :, pos], ref, w.dtype, f"stream step {n + 1} (frame {fr})")
+        if out_dtype == torch.bfloat16:
+            assert_parity_rounded(f64(o)[:, :, pos], ref, TOL[w.dtype],
+                                  f"stream step {n + 1} (frame {fr}), bf16 out")
+        else:
+            assert_parity(f64(o)[:, :, pos], ref, w.dtype, f"stream step {n + 1} (frame {fr})")
     # ring holds exact copies of the last R frames
     last = T0 + N
     for fr in range(max(0, last - w.ring), last):
@@ -72,12 +80,14 @@ def _run_and_check(w, T0, N, check_steps=None, rows=None, form=0):
     return s
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_stream_small(dtype):
-    print(f"[case] stream small {dtype}", flush=True)
+@pytest.mark.parametrize("dtype,out_dtype", [(torch.bfloat16, torch.float32),
+                                             (torch.bfloat16, torch.bfloat16),
+                                             (torch.float32, torch.float32)])
+def test_stream_small(dtype, out_dtype):
+    print(f"[case] stream small {dtype} out {out_dtype}", flush=True)
     w = Workload("case", 1, 2, 5, 150, 128, 128, dtype, window=3, taps=4, dilation=4, chunk=64,
                  k_unit=True, alpha_mu=3.0, ring=13, seed=41)
-    _run_and_check(w, T0=5, N=14)
+    _run_and_check(w, T0=5, N=14, out_dtype=out_dtype)
 
 
 def test_stream_dilation_12_printed_form():
@@ -114,19 +124,21 @@ def test_stream_from_empty_prefix():
     assert_parity(s.state, ref_st, w.dtype, "stream from empty state")
 
 
-def test_stream_step_wide_grid():
+@pytest.mark.parametrize("out_dtype,side", [(torch.float32, False), (torch.bfloat16, False),
+                                           (torch.bfloat16, True)])
+def test_stream_step_wide_grid(out_dtype, side):
     """A stream step whose attention grid spans more than one wave of workgroups
     (B4 H16 P1040: 64 heads x 9 query tiles = 576 workgroups, over two per CU on
-    256 CUs), where the attention pass adds the GLA partial itself for heads whose
-    scan has finished and flags the rest: sampled rows of two steps against the
-    oracle on the whole history, the final state and the ring."""
-    print("[case] stream step, wide grid B4 H16 P1040", flush=True)
+    256 CUs), with fp32 or bf16 output, on one stream or with the attention on a
+    caller side stream: sampled rows of two steps against the oracle on the whole
+    history, the final state and the ring."""
+    print(f"[case] stream step, wide grid B4 H16 P1040, out {out_dtype}, side {side}", flush=True)
     w = Workload("case", 4, 16, 4, 1040, 128, 128, torch.bfloat16, window=3, taps=4, dilation=4,
                  k_unit=True, alpha_mu=3.0, ring=13, seed=47)
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([np.array([0, 1, 127, 128, 1023, 1024, 1039]),
                                      rng.integers(0, w.P, 40)]))
-    _run_and_check(w, 4, 2, rows=rows)
+    _run_and_check(w, 4, 2, rows=rows, out_dtype=out_dtype, side=side)
 
 
 def test_stream_equals_batch_and_commit_only():

@@ -43,7 +43,7 @@ def test_counter_per_dispatch_sums_rows_and_takes_last(tmp_path):
 
 def test_traffic_scales_by_the_copy_kernel(tmp_path):
     k = "hta::win_attn_bf16_kernel<3>(hta::WinLaunch)"
-    cp = "hta::copy_frames_kernel(x)"
+    cp = "(anonymous namespace)::hbm_copy_kernel(x)"
     for name, counter, kv, cv in (("f", "FETCH_SIZE", 2000.0, 500.0), ("w", "WRITE_SIZE", 300.0, 1000.0)):
         (tmp_path / name).mkdir()
         (tmp_path / ("c" + name)).mkdir()
