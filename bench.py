@@ -39,6 +39,9 @@ ATTN_LAUNCHES = 1                   # one SWA+DSWA pass per step
 GLA_SRC = os.path.join(ROOT, "hybrid_linear_temporal_hta_amd", "csrc", "gla_fwd.hip")
 GLA_PREP_PMC = os.path.join(ROOT, "profiles", "gla_prep2_gla_fwd_B2H16L32760_traffic.json")
 GLA_SCAN_PMC = os.path.join(ROOT, "profiles", "gla_scan3_gla_fwd_B2H16L32760_traffic.json")
+ATTN_MFMA = os.path.join(ROOT, "profiles", "win_attn_bf16_onepass_hybrid_fwd_B2H16L32760_mfma.json")
+GLA_PREP_MFMA = os.path.join(ROOT, "profiles", "gla_prep2_gla_fwd_B2H16L32760_mfma.json")
+GLA_SCAN_MFMA = os.path.join(ROOT, "profiles", "gla_scan3_gla_fwd_B2H16L32760_mfma.json")
 
 
 def attn_pairs(w) -> int:
@@ -102,6 +105,20 @@ def pmc_traffic(path: str, src: str):
             return None
         return float(rec["hbm_bytes_per_launch"])
     except (OSError, ValueError, KeyError):
+        return None
+
+
+def profiled_mfma_busy(path: str, src: str):
+    """MFMA busy fraction of a kernel from a committed rocprofv3 counter summary
+    (busy cycles per SIMD over the kernel's active cycles), valid only while the
+    kernel source is the one it was taken on (else None)."""
+    try:
+        from hybrid_linear_temporal_hta_amd.profiling import source_digest
+        rec = json.load(open(path))
+        if rec.get("source_digest") != source_digest(src):
+            return None
+        return round(float(rec["mfma_busy_frac"]), 4)
+    except (OSError, ValueError, KeyError, TypeError):
         return None
 
 
@@ -494,7 +511,8 @@ def main():
                 "launches_per_step": ATTN_LAUNCHES, "flop_per_launch": fl_launch,
                 "avg_launch_ms": round(launch_ms, 4),
                 "double_counted_TFLOPs": round(dbl, 2),
-                "double_counted_frac": round(dbl / PEAK_MFMA_BF16_TFLOPS, 4)}
+                "double_counted_frac": round(dbl / PEAK_MFMA_BF16_TFLOPS, 4),
+                "mfma_busy_frac_profiled": profiled_mfma_busy(ATTN_MFMA, ATTN_SRC)}
     gb = gla_bytes(w)
     gla = {"kernels": "gla_prep2_kernel + gla_scan3_kernel", "avg_ms": round(gla_ms, 4),
            "algorithmic_bytes": gb, "achieved_GBps": round(gb / (gla_ms / 1e3) / 1e9, 1),
@@ -502,7 +520,9 @@ def main():
            "flop": gla_flops(w),
            "frac_mfma": round(gla_flops(w) / (gla_ms / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
            "traffic_prep": pmc_traffic(GLA_PREP_PMC, GLA_SRC),
-           "traffic_scan": pmc_traffic(GLA_SCAN_PMC, GLA_SRC)}
+           "traffic_scan": pmc_traffic(GLA_SCAN_PMC, GLA_SRC),
+           "mfma_busy_frac_profiled": {"prep": profiled_mfma_busy(GLA_PREP_MFMA, GLA_SRC),
+                                       "scan": profiled_mfma_busy(GLA_SCAN_MFMA, GLA_SRC)}}
     hybrid_frac = (fl + gla_flops(w)) / (ms_per_step / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS
 
     # Streaming continuation: prefix = the 21 frames above, then one frame per step.

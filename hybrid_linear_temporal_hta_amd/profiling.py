@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 CSV output for the HTA kernels.
 
-Two subcommands, both reading what ``rocprofv3 --output-format csv`` writes:
+Three subcommands, all reading what ``rocprofv3 --output-format csv`` writes:
 
   stats    per-kernel call count and durations from ``*_kernel_stats.csv``,
            written as a short text table with the command that produced it.
@@ -11,12 +11,18 @@ Two subcommands, both reading what ``rocprofv3 --output-format csv`` writes:
            The result is JSON keyed to a digest of the kernel's source file
            (comments excluded), so a reader can tell when the kernel changed
            after the counters were taken.
+  mfma     MFMA utilisation of one kernel from a ``--pmc`` run of
+           SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, SQ_INSTS_MFMA and the MFMA
+           op counters: busy cycles per SIMD over the kernel's active cycles
+           per shader engine (MI355X: 1024 SIMDs in 32 shader engines).
 
 Usage:
   python -m hybrid_linear_temporal_hta_amd.profiling stats CSV --out FILE --command CMD
   python -m hybrid_linear_temporal_hta_amd.profiling traffic --kernel SUBSTR \\
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N \\
-      --source FILE --out FILE --command CMD [--last N]
+      --source FILE --out FILE --command CMD [--last N | --first N] [--grid N]
+  python -m hybrid_linear_temporal_hta_amd.profiling mfma --kernel SUBSTR --pmc DIR \\
+      --source FILE --out FILE --command CMD [--last N | --first N] [--grid N]
 """
 from __future__ import annotations
 
@@ -107,24 +113,31 @@ def trace_by_grid(path: str, prefix: str = "hta::"):
     return out
 
 
-def counter_per_dispatch(path: str, counter: str, kernel: str, last: int = 0):
+def counter_per_dispatch(path: str, counter: str, kernel: str, last: int = 0, grid: int = 0,
+                         first: int = 0):
     """Mean over dispatches of `kernel` (substring) of one counter's value, and
-    the dispatch count; with `last`, over the last that many dispatches only.
-    Values of one dispatch spread over several rows (one per counter dimension)
-    are summed first."""
+    the dispatch count; with `last` (`first`), over the last (first) that many
+    dispatches only;
+    with `grid`, over dispatches of that grid size (work-items) only. Values of
+    one dispatch spread over several rows (one per counter dimension) are
+    summed first."""
     per = {}
     with open(_find(path, "counter_collection.csv")) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter or kernel not in r["Kernel_Name"]:
                 continue
+            if grid and int(r["Grid_Size"]) != grid:
+                continue
             d = int(r["Dispatch_Id"])
             per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
     if not per:
         raise ValueError(f"no {counter} rows for kernel {kernel!r} in {path}")
-    if last:
-        if len(per) < last:
-            raise ValueError(f"{len(per)} dispatches of {kernel!r} in {path}, fewer than {last}")
-        per = {d: per[d] for d in sorted(per)[-last:]}
+    if last or first:
+        n = last or first
+        if len(per) < n:
+            raise ValueError(f"{len(per)} dispatches of {kernel!r} in {path}, fewer than {n}")
+        keep = sorted(per)[-last:] if last else sorted(per)[:first]
+        per = {d: per[d] for d in keep}
     return sum(per.values()) / len(per), len(per)
 
 
@@ -153,12 +166,13 @@ def cmd_stats(a):
 def cmd_traffic(a):
     cf, ncf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
     cw, ncw = counter_per_dispatch(a.copy_write, "WRITE_SIZE", COPY_KERNEL)
-    kf, nkf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel, a.last)
-    kw, nkw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel, a.last)
+    kf, nkf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel, a.last, a.grid, a.first)
+    kw, nkw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel, a.last, a.grid, a.first)
     # the copy kernel reads and writes copy_bytes each: bytes per counted KiB
     f_fetch = a.copy_bytes / cf
     f_write = a.copy_bytes / cw
-    rec = {"kernel": a.kernel, "source": os.path.relpath(a.source, os.path.dirname(a.out) + "/.."),
+    rec = {"kernel": a.kernel, "grid_work_items": a.grid or None,
+           "source": os.path.relpath(a.source, os.path.dirname(a.out) + "/.."),
            "source_digest": source_digest(a.source),
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
            "dispatches": [nkf, nkw],
@@ -167,6 +181,35 @@ def cmd_traffic(a):
            "bytes_per_fetch_unit": f_fetch, "bytes_per_write_unit": f_write,
            "hbm_read_bytes_per_launch": kf * f_fetch, "hbm_write_bytes_per_launch": kw * f_write,
            "hbm_bytes_per_launch": kf * f_fetch + kw * f_write,
+           "command": a.command}
+    with open(a.out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+SIMDS, SHADER_ENGINES = 1024, 32   # MI355X: 256 CUs x 4 SIMDs; 8 XCDs x 4 shader engines
+
+
+def cmd_mfma(a):
+    names = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA",
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_LDS",
+             "SQ_LDS_BANK_CONFLICT"]
+    vals, nd = {}, 0
+    for c in names:
+        try:
+            vals[c], nd = counter_per_dispatch(a.pmc, c, a.kernel, a.last, a.grid, a.first)
+        except ValueError:
+            vals[c] = None
+    busy, sqb = vals["SQ_VALU_MFMA_BUSY_CYCLES"], vals["SQ_BUSY_CYCLES"]
+    cyc = sqb / SHADER_ENGINES if sqb else None   # active cycles of the kernel
+    rec = {"kernel": a.kernel, "grid_work_items": a.grid or None,
+           "source": os.path.relpath(a.source, os.path.dirname(a.out) + "/.."),
+           "source_digest": source_digest(a.source), "dispatches": nd,
+           "per_dispatch": vals, "active_cycles": cyc,
+           "mfma_busy_frac": busy / (cyc * SIMDS) if busy is not None and cyc else None,
+           "busy_cycles_per_mfma": busy / vals["SQ_INSTS_MFMA"]
+           if busy and vals["SQ_INSTS_MFMA"] else None,
            "command": a.command}
     with open(a.out, "w") as f:
         json.dump(rec, f, indent=1)
@@ -189,8 +232,15 @@ def main(argv=None):
     t.add_argument("--copy-bytes", dest="copy_bytes", type=float, required=True)
     t.add_argument("--last", type=int, default=0,
                    help="only the last N dispatches of the kernel (default: all)")
+    m = sub.add_parser("mfma")
+    for k in ("kernel", "pmc", "source", "out", "command"):
+        m.add_argument("--" + k, dest=k, required=True)
+    for q in (t, m):
+        q.add_argument("--grid", type=int, default=0, help="only dispatches of this grid size")
+        q.add_argument("--first", type=int, default=0, help="only the first N dispatches")
+    m.add_argument("--last", type=int, default=0, help="only the last N dispatches")
     a = ap.parse_args(argv)
-    (cmd_stats if a.cmd == "stats" else cmd_traffic)(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
