@@ -353,15 +353,17 @@ def projection(hta, dev, steps):
 
 
 def train(hta, w, x, dev, steps, warmup, cpu_heads):
-    """The training pair on the same batch (NEXT to the forward hot path): one
-    step = hta_hybrid_fwd_train + hta_hybrid_bwd (dL/do ~ N(0, 1), fp32), wall
+    """The training pair on the same batch (NEXT to the forward hot path), with a
+    side stream: one step = hta_hybrid_fwd_train + hta_hybrid_bwd (dL/do ~ N(0, 1), fp32), wall
     time; the backward alone and each attention branch's backward alone
     (HIP events), with the attention backward's MFMA roofline: its algorithmic
     work is 2.5x the branch's forward (recompute S, then dP, dV, dK, dQ: five
     products of 2 d P^2 per (query frame, tap frame) pair against two)."""
     import torch
     from hybrid_linear_temporal_hta_amd.inputs import make_output_grad
-    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk)
+    # with a side stream, as the forward metric: the GLA backward runs beside the
+    # SWA backward
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, side=hta.SideStream(dev))
     q, k, v, a, b = x["q"], x["k"], x["v"], x["alpha"], x["beta"]
     o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device=dev)
     st = torch.zeros(w.B, w.H, w.dk, w.dv, device=dev)
