@@ -36,6 +36,15 @@
  *     and workspace must start on a 16-byte boundary; alpha, beta, lse, dalpha
  *     and dbeta on a 4-byte boundary. Otherwise the call returns HTA_ERR_ALIGN.
  *     (Fresh torch or hipMalloc allocations are 256-byte aligned.)
+ *   - Values: every finite input is supported, in either dtype. Some products of
+ *     the bf16 paths run on fp16 operands; each such operand carries a power of
+ *     two chosen from the data (per chunk, per state column group, or per tensor
+ *     in the backward), an exact rescaling, so no range limit applies beyond
+ *     fp32's. A NaN or Inf input makes every output that depends on it
+ *     non-finite (in the GLA branch also the other tokens of its 64-token chunk,
+ *     whose triangular products multiply masked entries by zero) and leaves the
+ *     independent outputs as they would be without it.
+ *   - Results are deterministic: identical calls return identical bits.
  *
  * Readings of the pages that the library implements (where they are silent):
  *   - the SWA window counts the current frame: frames f-W+1..f; attention is
