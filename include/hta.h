@@ -109,7 +109,10 @@ typedef struct {
      * both required with a side stream (HTA_ERR_NULL otherwise). The call orders
      * everything it enqueues on side_stream after the work already on `stream`,
      * and later work on `stream` after all of it. A call's use of the events must
-     * not overlap another call's. The results are the same bits either way. */
+     * not overlap another call's. The results are the same bits either way. The
+     * overlap needs the two streams on different hardware queues: HIP deals its
+     * streams out over a few queues in turn, and two streams that share one run
+     * one after the other. */
     void* side_stream;
     void* fork_event;
     void* join_event;
