@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 METRIC = "hybrid temporal-attn fwd tokens/s at L=32760,H=16,d=128; % MFMA peak"
 PEAK_MFMA_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0              # MI355X HBM3E
+NUM_CUS = 256                       # MI355X compute units
+CLOCK_GHZ = 2.4                     # MI355X peak engine clock (per-CU byte rates are quoted at it)
 ATTN_KERNEL = "win_attn_bf16_kernel<3>"   # both windows in one pass (own frame shared)
 PMC_FILE = os.path.join(ROOT, "profiles", "win_attn_bf16_onepass_hybrid_fwd_B2H16L32760_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "hybrid_linear_temporal_hta_amd", "csrc", "win_attn.hip")
@@ -155,12 +157,31 @@ def measured_peaks(dev, stream):
     copy_ms = timed_events(lambda: peaks.copy(src, dst, stream), 10, 2, stream)
     del src, dst
     torch.cuda.empty_cache()
+    # the on-chip paths of the kernels' tiles: direct global->LDS loads from an
+    # L2-resident 2 MiB window (contiguous 1 KiB, and 32 rows x 32 bytes), and LDS
+    # reads (ds_read_b128, ds_read_b64_tr_b16); two workgroups per CU
+    win = 1 << 21
+    lsrc = torch.ones(win // 4, device=dev)
+    onchip = {}
+    for name, pattern in (("l2_to_lds_contiguous", 0), ("l2_to_lds_32B_rows", 1)):
+        ms = timed_events(lambda: peaks.lds_dma(lsrc, win, 512, 400, pattern, stream), 5, 1, stream)
+        onchip[name] = peaks.lds_dma_bytes(512, 400) / (ms / 1e3)
+    lsink = torch.empty(512 * 256, device=dev)
+    for name, tr in (("lds_read_b128", False), ("lds_read_b64_tr_b16", True)):
+        ms = timed_events(lambda: peaks.lds_read(512, 4000, tr, lsink, stream), 5, 1, stream)
+        onchip[name] = peaks.lds_read_bytes(512, 4000, tr) / (ms / 1e3)
+    del lsrc, lsink
+    onchip_rates = {k: {"TBps": round(v / 1e12, 2),
+                        "B_per_clk_per_CU": round(v / (NUM_CUS * CLOCK_GHZ * 1e9), 1)}
+                    for k, v in onchip.items()}
     return {"mfma_kernel": "mfma_loop_kernel (v_mfma_f32_32x32x16_bf16)",
             "mfma_TFLOPs": round(fl / (mfma_ms / 1e3) / 1e12, 1),
             "mfma_frac_of_spec": round(fl / (mfma_ms / 1e3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4),
             "copy_kernel": "hbm_copy_kernel", "copy_bytes_moved": 2 * COPY_BYTES,
             "hbm_copy_GBps": round(2 * COPY_BYTES / (copy_ms / 1e3) / 1e9, 1),
-            "hbm_frac_of_spec": round(2 * COPY_BYTES / (copy_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4)}
+            "hbm_frac_of_spec": round(2 * COPY_BYTES / (copy_ms / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "onchip": onchip_rates,
+            "onchip_clock_GHz": CLOCK_GHZ}
 
 
 def cpu_baseline(w, x, heads: int):

@@ -1,6 +1,7 @@
-"""ctypes binding of libhta_peaks.so (include/hta_peaks.h): the MFMA issue loop
-and the HBM copy whose rates the benchmark reports beside the published peaks.
-Argument marshalling only; the library must be built (it raises otherwise)."""
+"""ctypes binding of libhta_peaks.so (include/hta_peaks.h): the MFMA issue loop,
+the HBM copy, and the global->LDS load and LDS read loops whose rates the
+benchmark reports beside the published peaks. Argument marshalling only; the
+library must be built (it raises otherwise)."""
 from __future__ import annotations
 
 import ctypes
@@ -8,7 +9,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhta_peaks.so")
-EXPORTED = ("hta_peak_mfma", "hta_peak_mfma_chains", "hta_peak_copy")
+EXPORTED = ("hta_peak_mfma", "hta_peak_mfma_chains", "hta_peak_copy", "hta_peak_lds_dma",
+            "hta_peak_lds_read")
 MFMA_FLOP = 2 * 32 * 32 * 16          # one v_mfma_f32_32x32x16_bf16 per wave
 WAVES_PER_BLOCK = 4
 
@@ -29,6 +31,10 @@ def lib() -> ctypes.CDLL:
         L.hta_peak_mfma_chains.argtypes = []
         L.hta_peak_copy.restype = i
         L.hta_peak_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.hta_peak_lds_dma.restype = i
+        L.hta_peak_lds_dma.argtypes = [vp, ctypes.c_size_t, i, i, i, vp]
+        L.hta_peak_lds_read.restype = i
+        L.hta_peak_lds_read.argtypes = [i, i, i, vp, vp]
         _lib = L
     return _lib
 
@@ -58,3 +64,27 @@ def copy(src, dst, stream=None) -> None:
                              _stream(stream))
     if st != 0:
         raise RuntimeError(f"hta_peak_copy: status {st}")
+
+
+def lds_dma_bytes(blocks: int, iters: int) -> float:
+    return float(blocks) * WAVES_PER_BLOCK * iters * 8 * 1024
+
+
+def lds_dma(src, window_bytes: int, blocks: int, iters: int, pattern: int, stream=None) -> None:
+    if window_bytes > src.numel() * src.element_size():
+        raise ValueError("window larger than src")
+    st = lib().hta_peak_lds_dma(ctypes.c_void_p(src.data_ptr()), int(window_bytes), int(blocks),
+                                int(iters), int(pattern), _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"hta_peak_lds_dma: status {st}")
+
+
+def lds_read_bytes(blocks: int, iters: int, transposed: bool) -> float:
+    return float(blocks) * WAVES_PER_BLOCK * iters * 8 * (512 if transposed else 1024)
+
+
+def lds_read(blocks: int, iters: int, transposed: bool, sink, stream=None) -> None:
+    st = lib().hta_peak_lds_read(int(blocks), int(iters), int(bool(transposed)),
+                                 ctypes.c_void_p(sink.data_ptr()), _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"hta_peak_lds_read: status {st}")

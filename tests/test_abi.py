@@ -66,6 +66,16 @@ def test_peaks_argument_errors():
     assert L.hta_peak_copy(F, G, 16384 + 64, None) == -2
     assert L.hta_peak_copy(ctypes.c_void_p(F.value + 8), G, 16384, None) == -10
     assert L.hta_peak_copy(F, ctypes.c_void_p(F.value + 16384), 32768, None) == -9
+    assert L.hta_peak_lds_dma(None, 1 << 21, 1, 1, 0, None) == -1
+    assert L.hta_peak_lds_dma(F, 1 << 21, 0, 1, 0, None) == -2
+    assert L.hta_peak_lds_dma(F, 1 << 21, 1, 0, 0, None) == -2
+    assert L.hta_peak_lds_dma(F, 1 << 21, 1, 1, 2, None) == -2
+    assert L.hta_peak_lds_dma(F, 4096, 1, 1, 0, None) == -2
+    assert L.hta_peak_lds_dma(F, (1 << 21) + 8192, 1, 1, 0, None) == -2
+    assert L.hta_peak_lds_dma(ctypes.c_void_p(F.value + 8), 1 << 21, 1, 1, 1, None) == -10
+    assert L.hta_peak_lds_read(1, 1, 0, None, None) == -1
+    assert L.hta_peak_lds_read(0, 1, 1, F, None) == -2
+    assert L.hta_peak_lds_read(1, 0, 0, F, None) == -2
 
 
 def test_version_and_status_strings():
