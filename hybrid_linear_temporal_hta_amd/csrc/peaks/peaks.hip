@@ -111,7 +111,12 @@ __global__ __launch_bounds__(256) void lds_dma_kernel(const char* src, unsigned 
 template <bool TR>
 __global__ __launch_bounds__(256) void lds_read_kernel(int iters, float* sink) {
     __shared__ __attribute__((aligned(16))) float buf[16384];
-    for (int i = threadIdx.x; i < 16384; i += 256) buf[i] = (float)(i & 255) * 1e-3f;
+    if (TR) {   // read as bf16: every 16-bit half a finite bf16
+        bf16* hb = reinterpret_cast<bf16*>(buf);
+        for (int i = threadIdx.x; i < 32768; i += 256) hb[i] = (bf16)((float)(i & 255) * 1e-3f);
+    } else {
+        for (int i = threadIdx.x; i < 16384; i += 256) buf[i] = (float)(i & 255) * 1e-3f;
+    }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float acc = 0.f;

@@ -73,7 +73,10 @@ class Params(ctypes.Structure):
 
 class SideStream:
     """A second stream on the current device and the two events hta_params needs
-    to run work on it (held here so that they outlive the calls using them)."""
+    to run work on it (held here so that they outlive the calls using them). The
+    overlap needs the stream on another hardware queue than the caller's: HIP
+    deals streams out over a few queues in turn, and two on one queue run one
+    after the other (same results, no overlap)."""
 
     def __init__(self, device=None):
         self.stream = torch.cuda.Stream(device=device)
