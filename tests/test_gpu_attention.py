@@ -197,3 +197,37 @@ def test_swa_dswa_one_pass(B, H, T, P, d, dtype, window, taps, dil, mode):
         assert_parity_rounded(o, ref, TOL[dtype], "one-pass bf16-out")
     else:
         assert_parity(o, ref, dtype, f"one-pass {mode}")
+
+
+@pytest.mark.parametrize("T,P,window,taps,dil", [
+    (20, 40, 16, 16, 1),       # the largest window and tap count
+    (4100, 1, 1, 2, 4095),     # the farthest tap: (taps - 1) * dilation + 1 = 4096 frames
+    (45, 24, 16, 4, 14),       # a full window beside taps that outreach it
+])
+def test_window_and_taps_at_limits(T, P, window, taps, dil):
+    """The largest supported windows (window, taps <= 16 and a tap span of 4096 frames):
+    SWA and DSWA alone, the one-pass pair, and the bf16 hybrid with a side stream,
+    against the oracle."""
+    print(f"[case] limits T{T} P{P} W{window} taps{taps} dil{dil}", flush=True)
+    w = _workload(1, 2, T, P, 128, torch.bfloat16, seed=700 + T + P, qv_std=1.0, k_std=1.0)
+    x = _gpu(make_inputs(w, frames=T))
+    ref_s = oracle.swa(x["q"], x["k"], x["v"], T, P, window)
+    ref_d = oracle.dswa(x["q"], x["k"], x["v"], T, P, taps, dil)
+    assert_parity(_run_swa(x, P, window), ref_s, w.dtype, "swa")
+    assert_parity(_run_dswa(x, P, taps, dil), ref_d, w.dtype, "dswa")
+    o = _out(x)
+    hta.hta_swa_dswa_fwd_ex(x["q"], x["k"], x["v"], o, P, hta.make_params(window, taps, dil))
+    torch.cuda.synchronize()
+    assert_parity(o, ref_s + ref_d, w.dtype, "one-pass")
+    # the hybrid with unit-norm q and k (the GLA recurrence is bounded for |k| = 1)
+    w = w.replace(q_unit=True, k_unit=True)
+    x = _gpu(make_inputs(w, frames=T))
+    ref_o, ref_state, _ = oracle.hybrid(x["q"], x["k"], x["v"], x["alpha"], x["beta"], T, P,
+                                        window, taps, dil)
+    st = torch.zeros(w.B, w.H, 128, 128, device="cuda")
+    o = _out(x)
+    prm = hta.make_params(window, taps, dil, 64, side=hta.SideStream())
+    hta.hta_hybrid_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, P, prm)
+    torch.cuda.synchronize()
+    assert_parity(o, ref_o, w.dtype, "hybrid")
+    assert_parity(st, ref_state, w.dtype, "hybrid state")
