@@ -99,6 +99,17 @@ def test_stream_dilation_12_printed_form():
     _run_and_check(w, T0=30, N=10, form=hta.HTA_GLA_PRINTED)
 
 
+def test_stream_farthest_tap():
+    """The largest tap span (a 4095-frame dilation: 4096 frames) at P = 1 through a
+    4096-frame ring, with a side stream: the DSWA tap of each step reads the slot
+    written 4095 frames earlier (frame 4096's tap reads frame 1 after frame 4096 has
+    replaced frame 0 in slot 0)."""
+    print("[case] stream farthest tap: dil 4095, ring 4096, P 1", flush=True)
+    w = Workload("case", 1, 2, 4094, 1, 128, 128, torch.bfloat16, window=1, taps=2, dilation=4095,
+                 q_unit=True, k_unit=True, ring=4096, seed=46)
+    _run_and_check(w, T0=4094, N=4, side=True)
+
+
 def test_stream_from_empty_prefix():
     """A stream started with no prefix: early frames see only the taps that exist."""
     print("[case] stream from empty prefix", flush=True)
