@@ -90,6 +90,21 @@ def test_hybrid_bwd_bf16(out_dtype, form, side):
     _check(got, ref, w.dtype, "hybrid")
 
 
+@pytest.mark.parametrize("T,P,window,taps,dil", [(20, 40, 16, 16, 1), (4100, 1, 1, 2, 4095)])
+def test_hybrid_bwd_at_limits(T, P, window, taps, dil):
+    """The training pair at the largest window and tap count, and at the largest tap
+    span (4096 frames, P = 1), with a side stream, against the oracle's gradients."""
+    w = WORKLOADS["hybrid_stream"].replace(B=1, H=2, T=T, P=P, stream_frames=0, window=window,
+                                           taps=taps, dilation=dil, seed=51)
+    print(f"[case] hybrid bwd limits T{T} P{P} W{window} taps{taps} dil{dil}", flush=True)
+    x, dout, s0, dsf = _inputs(w, torch.float32)
+    prm = hta.make_params(window, taps, dil, w.chunk, side=hta.SideStream())
+    got = _run(w, x, dout, s0, dsf, prm, torch.float32)
+    ref = oracle.hybrid_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["alpha"]),
+                            f64(x["beta"]), f64(dout), T, P, window, taps, dil, f64(s0), f64(dsf))
+    _check(got, ref, w.dtype, "hybrid at limits")
+
+
 def test_hybrid_bwd_fp32():
     w = WORKLOADS["tiny_fp32"]
     print(f"[case] hybrid bwd {w.name}", flush=True)
