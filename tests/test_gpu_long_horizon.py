@@ -53,3 +53,45 @@ def test_long_horizon_last_frames_and_state():
     assert_parity(st_gpu, ref_st, w.dtype, "long-horizon final state")
     ref = ref_att.reshape(w.B, w.H, n_last * w.P, w.dv) + ref_g[:, :, (w.T - n_last) * w.P:]
     assert_parity(got, ref, w.dtype, "long-horizon last two frames")
+
+
+@pytest.mark.slow
+def test_element_offsets_beyond_2_31():
+    """B2 H16 T337 P1560 (L = 525720): each sequence tensor holds 2 153 349 120
+    elements, more than 2^31, so the last head's element offsets pass 2^31 (its
+    first element sits at 2.09e9). The hybrid with a side stream; the oracle checks
+    that head's last two frames (SWA/DSWA over a 14-frame slice plus the GLA branch)
+    and its final GLA state, the GLA from the recurrence over all of its tokens."""
+    w = WORKLOADS["long_horizon"].replace(B=2, T=337, seed=5)
+    n_el = w.B * w.H * w.L * w.dk
+    assert n_el > 2 ** 31
+    print(f"[case] offsets beyond 2^31: B{w.B} H{w.H} T{w.T} P{w.P} ({n_el} elements)", flush=True)
+    x = make_inputs(w, device="cuda", frames=w.T)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, side=hta.SideStream())
+    st = torch.zeros(w.B, w.H, w.dk, w.dv, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.dv, dtype=torch.float32, device="cuda")
+    hta.hta_hybrid_fwd(x["q"], x["k"], x["v"], x["alpha"], x["beta"], st, o, w.P, prm)
+    torch.cuda.synchronize()
+    b, h = w.B - 1, w.H - 1
+    reach = max(w.window - 1, (w.taps - 1) * w.dilation)
+    n_last = 2
+    F0 = w.T - n_last - reach
+    Th = w.T - F0
+    got = f64(o[b:b + 1, h:h + 1, (w.T - n_last) * w.P:])
+    st_gpu = f64(st[b:b + 1, h:h + 1])
+    del o
+    head = {n: x[n][b:b + 1, h:h + 1].contiguous() for n in ("q", "k", "v", "alpha", "beta")}
+    del x
+    torch.cuda.empty_cache()
+    sl = slice(F0 * w.P, w.T * w.P)
+    qh, kh, vh = (f64(head[n][:, :, sl]) for n in ("q", "k", "v"))
+    rows = np.arange((Th - n_last) * w.P, Th * w.P)
+    print(f"[case] oracle SWA/DSWA on {rows.size} rows of the last head", flush=True)
+    ref_att = oracle.swa_rows(qh, kh, vh, Th, w.P, w.window, rows) + \
+        oracle.dswa_rows(qh, kh, vh, Th, w.P, w.taps, w.dilation, rows)
+    print("[case] oracle GLA recurrence over the last head's tokens", flush=True)
+    ref_g, ref_st = oracle.gla(f64(head["q"]), f64(head["k"]), f64(head["v"]),
+                               head["alpha"].cpu(), head["beta"].cpu())
+    assert_parity(st_gpu, ref_st, w.dtype, "last head's final state")
+    ref = ref_att.reshape(1, 1, n_last * w.P, w.dv) + ref_g[:, :, (w.T - n_last) * w.P:]
+    assert_parity(got, ref, w.dtype, "last head's last two frames")
