@@ -153,6 +153,62 @@ def test_hybrid_bwd_full_size_sampled():
                                   TOL[w.dtype], f"full-size {name} sampled rows (b,h)=({b_},{h_})")
 
 
+@pytest.mark.slow
+def test_hybrid_bwd_offsets_beyond_2_31():
+    """The training pair at B2 H16 T337 P1560 (L = 525720): each sequence tensor holds
+    2 153 349 120 elements, more than 2^31; the last head's last 31 frames lie past
+    2^31. For that head's last 14 frames: the GLA gradients (the oracle's forward
+    over the frames before gives the state entering them, its backward over them the
+    exact gradients of their tokens) and dq / dk / dv of the last two frames (the
+    attention part from the oracle's row routines over those 14 frames)."""
+    w = WORKLOADS["long_horizon"].replace(B=2, T=337, seed=6)
+    assert w.B * w.H * w.L * w.dk > 2 ** 31
+    print(f"[case] hybrid bwd offsets beyond 2^31: B{w.B} H{w.H} T{w.T} P{w.P}", flush=True)
+    x, dout, s0, dsf = _inputs(w, torch.float32)
+    torch.cuda.empty_cache()   # the draws' fp32 temporaries (the backward needs ~160 GB)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, side=hta.SideStream())
+    q, k, v, a, b = x["q"], x["k"], x["v"], x["alpha"], x["beta"]
+    o = torch.empty(w.B, w.H, w.L, w.dv, device="cuda")
+    saved = torch.empty(hta.hta_hybrid_saved_bytes(hta.make_shape(q, v, w.P, o)),
+                        dtype=torch.uint8, device="cuda")
+    hta.hta_hybrid_fwd_train(q, k, v, a, b, s0.clone(), o, saved, w.P, prm)
+    torch.cuda.synchronize()
+    del o
+    torch.cuda.empty_cache()   # the forward's workspace
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    da, db = torch.empty_like(a), torch.empty_like(b)
+    hta.hta_hybrid_bwd(q, k, v, a, b, saved, dout, dsf.clone(), dq, dk, dv, da, db, w.P, prm)
+    torch.cuda.synchronize()
+    got = dict(dq=dq, dk=dk, dv=dv, dalpha=da, dbeta=db)
+    del saved, q, k, v, a, b, dq, dk, dv, da, db
+    b_, h_ = w.B - 1, w.H - 1
+    nt = 14                                   # frames checked: the last taps reach 12 back
+    t0 = (w.T - nt) * w.P
+    head = {n: f64(x[n][b_:b_ + 1, h_:h_ + 1]) for n in ("q", "k", "v", "alpha", "beta")}
+    do = f64(dout[b_:b_ + 1, h_:h_ + 1])
+    got = {n: t[b_, h_].cpu() for n, t in got.items()}
+    del x, dout
+    torch.cuda.empty_cache()
+    print("[case] oracle GLA forward to the checked frames, backward over them", flush=True)
+    _, st_mid = oracle.gla(*(head[n][:, :, :t0] for n in ("q", "k", "v", "alpha", "beta")),
+                           f64(s0[b_:b_ + 1, h_:h_ + 1]))
+    tail = {n: head[n][:, :, t0:] for n in head}
+    g = oracle.gla_bwd(tail["q"], tail["k"], tail["v"], tail["alpha"], tail["beta"],
+                       do[:, :, t0:], st_mid, f64(dsf[b_:b_ + 1, h_:h_ + 1]))
+    for name in ("dalpha", "dbeta"):
+        assert_parity(got[name][t0:], g[name][0, 0], w.dtype, f"tail {name}")
+    pos = np.arange((nt - 2) * w.P, nt * w.P)   # the last two frames, within the tail
+    q, k, v = tail["q"], tail["k"], tail["v"]
+    att_dq = sum(oracle.window_dq_rows(kind, q, k, v, do[:, :, t0:], nt, w.P, a, dd, pos)
+                 for kind, a, dd in (("swa", w.window, 0), ("dswa", w.taps, w.dilation)))
+    kv = [oracle.window_dkv_rows(kind, q, k, v, do[:, :, t0:], nt, w.P, a, dd, pos)
+          for kind, a, dd in (("swa", w.window, 0), ("dswa", w.taps, w.dilation))]
+    att_dk, att_dv = kv[0][0] + kv[1][0], kv[0][1] + kv[1][1]
+    for name, att in (("dq", att_dq), ("dk", att_dk), ("dv", att_dv)):
+        ref = att + g[name][0, 0, pos]
+        assert_parity_rounded(got[name][t0 + pos], ref, TOL[w.dtype], f"last two frames {name}")
+
+
 @pytest.mark.parametrize("side", [False, True])
 def test_hybrid_bwd_deterministic(side):
     """The training pair is bitwise reproducible: two backward calls on the same
