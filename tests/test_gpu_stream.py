@@ -110,6 +110,56 @@ def test_stream_farthest_tap():
     _run_and_check(w, T0=4094, N=4, side=True)
 
 
+@pytest.mark.slow
+def test_stream_ring_offsets_beyond_2_31():
+    """A ring of 4097 frames at B2 H16 P128 holds 2 148 007 936 elements per tensor,
+    more than 2^31, so the last head's slots sit past 2^31; with a 4095-frame dilation
+    each step's DSWA tap reads a slot 4095 frames back. Side stream. The oracle checks
+    the last head: both steps' outputs from the whole history and its final state;
+    the ring must hold that head's frames exactly."""
+    w = Workload("case", 2, 16, 4096, 128, 128, 128, torch.bfloat16, window=1, taps=2,
+                 dilation=4095, q_unit=True, k_unit=True, ring=4097, seed=47)
+    T0, N = w.T, 2
+    assert w.B * w.H * w.ring * w.P * w.dk > 2 ** 31
+    print(f"[case] stream ring beyond 2^31: B{w.B} H{w.H} P{w.P} ring {w.ring}", flush=True)
+    prm = hta.make_params(w.window, w.taps, w.dilation, w.chunk, side=hta.SideStream())
+    full = make_inputs(w, device="cuda", frames=T0 + N)
+    torch.cuda.empty_cache()
+    s, o_prefix = _start_stream(w, full, T0, prm)
+    del o_prefix
+    torch.cuda.empty_cache()
+    b_, h_ = w.B - 1, w.H - 1
+    outs = []
+    for n in range(N):
+        f = _frames(full, w.P, T0 + n)
+        o = torch.empty(w.B, w.H, w.P, w.dv, device="cuda")
+        hta.hta_stream_step(s, f["q"], f["k"], f["v"], f["alpha"], f["beta"], o)
+        outs.append(o[b_, h_].clone())
+    torch.cuda.synchronize()
+    assert s.n_frames == T0 + N
+    last = T0 + N
+    for fr in (0, 1, last - 2, last - 1):   # slots of the oldest and the newest frames
+        if fr < last - w.ring:
+            continue
+        slot = fr % w.ring
+        sl = slice(fr * w.P, (fr + 1) * w.P)
+        assert torch.equal(s.ring_k[b_, h_, slot], full["k"][b_, h_, sl])
+        assert torch.equal(s.ring_v[b_, h_, slot], full["v"][b_, h_, sl])
+    st_gpu = f64(s.state[b_:b_ + 1, h_:h_ + 1])
+    head = {n: f64(full[n][b_:b_ + 1, h_:h_ + 1]) for n in ("q", "k", "v", "alpha", "beta")}
+    del s, full
+    torch.cuda.empty_cache()
+    ref_g, ref_st = oracle.gla(head["q"], head["k"], head["v"], head["alpha"], head["beta"])
+    assert_parity(st_gpu, ref_st, w.dtype, "last head's state after the steps")
+    for n, o in enumerate(outs):
+        fr = T0 + n
+        ref_att = oracle.stream_frame(head["k"][:, :, :(fr + 1) * w.P], head["v"][:, :, :(fr + 1) * w.P],
+                                      head["q"][:, :, fr * w.P:(fr + 1) * w.P], w.P, w.window,
+                                      w.taps, w.dilation)
+        ref = ref_att + ref_g[:, :, fr * w.P:(fr + 1) * w.P]
+        assert_parity(f64(o)[None, None], ref, w.dtype, f"last head, step {n + 1} (frame {fr})")
+
+
 def test_stream_from_empty_prefix():
     """A stream started with no prefix: early frames see only the taps that exist."""
     print("[case] stream from empty prefix", flush=True)
