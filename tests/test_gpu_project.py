@@ -81,3 +81,24 @@ def test_project_full_size_sampled():
     ref = project(xs, f64(w), H, 128, 128, True, True)
     sub = [t[:, :, toks] for t in got]
     _check(sub, ref, "project full-size sampled")
+
+
+@pytest.mark.slow
+def test_project_offsets_beyond_2_31():
+    """B2 L525720 H16 at model width 2048: x and each of q, k, v hold 2.15e9 elements,
+    more than 2^31; sampled tokens (the sequence's last ones, where batch 1's offsets
+    pass 2^31, and both tile edges) against the oracle."""
+    B, T, P, H, Dm = 2, 337, 1560, 16, 2048
+    L = T * P
+    assert B * L * Dm > 2 ** 31 and B * H * L * 128 > 2 ** 31
+    print(f"[case] project offsets beyond 2^31: B{B} L{L} H{H} Dm{Dm}", flush=True)
+    x, w = _inputs(B, L, Dm, H, seed=13)
+    torch.cuda.empty_cache()
+    got = _run(x, w, B, L, H, P, hta.HTA_NORM_Q | hta.HTA_NORM_K)
+    rng = np.random.default_rng(14)
+    toks = np.unique(np.concatenate([[0, 127, 128, L - 129, L - 128, L - 1],
+                                     rng.integers(L - 40000, L, 120)]))
+    xs = f64(x[:, toks])
+    ref = project(xs, f64(w), H, 128, 128, True, True)
+    sub = [t[:, :, toks] for t in got]
+    _check(sub, ref, "project beyond 2^31 sampled")
